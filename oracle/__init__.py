@@ -1,0 +1,41 @@
+"""CPU float64 oracle for selectively-read decode attention over a paged KV cache.
+
+TEST INFRASTRUCTURE. Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import or call anything in this
+package. The product library (``sparse_kv_recall_amd``) never imports it and
+shares no code with it: no kernels, headers, helpers, tables or constants.
+
+Every function here is the plain definition of what the decode path computes,
+written in float64 from the sources below, without blocking, fusion or
+reordering beyond what the definition itself states:
+
+* "On-Demand Attention: Language Models Know When to Recall" (arxiv-wiki
+  summary page): the local-first view with s sink tokens and a recent window
+  of w tokens that includes the current token, the recall head
+  R(h_{t-1}, E(x_t), h^L_t) -> q_t, the gate q_t > theta, recomputation of the
+  current step with full attention, and commit of the selected pass's
+  current-position KV ("Approach" section; the Local setting in "Main
+  results"; the Local/full-view runtime and FP32 recall head in "Developer
+  perspective").
+* "[Paper review] Language Models Can Control Their Own Attention" (blog
+  review of Declarative Attention), section 3 "Method & Key Results": the
+  mask is applied at KV-block granularity by rewriting the block table so the
+  attention kernel sees only kept blocks; the global / focus / local modes of
+  section 1 "Key Terms" and of the chatpaper abstract page.
+
+Parity status of each function (pinned by the ``-m "not gpu"`` tests):
+
+* keysets.full_keys / local_keys / block_keys ......... pinned
+* attention.attend ..................................... pinned
+* recall.recall_score / recall.gate .................... pinned
+* gather.gather_blocks / gather.da_mode_blocks ......... pinned
+* oda.oda_layer_step / oda.request_mode ................ pinned by definition only
+  (the pages print no worked example of a stack step; the commit and select
+  rules are checked against their restatement, brute force and invariants)
+* cost.* ............................................... attention-only ratio
+  pinned; the pages' whole-model 24.26% figure is parity unpinned (it needs
+  dense-layer sizes the pages do not give).
+"""
+
+from . import attention, cost, gather, keysets, oda, recall  # noqa: F401
+from .bf16 import bf16_bits_to_f64  # noqa: F401

@@ -1,0 +1,412 @@
+"""Pins of the float64 oracle against what the pages and the mathematics fix.
+
+Every check here uses something other than the oracle's own formula: the
+golden fixtures (hand-derived from the pages' definitions), closed forms,
+textbook values, scalar brute force, a second formulation (online softmax
+with an LSE merge), and invariants. Each is chosen so that a plausible slip
+in the oracle (an off-by-one window, duplicated sink keys, a wrong GQA
+index, a missing scale, a transposed operand, a non-strict gate, an unsorted
+block list) fails at least one of them.
+"""
+
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import attention, cost, gather, keysets, oda, recall
+from conftest import read_golden
+
+SCALE = 1.0 / math.sqrt(128.0)
+
+
+def to_bf16_bits(x):
+    """float -> bf16 bits via torch's own round-to-nearest-even cast."""
+    t = torch.as_tensor(np.asarray(x, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def rand_case(n, Hq, Hkv, D=128, seed=0, qscale=1.0):
+    rng = np.random.default_rng(seed)
+    q = (rng.standard_normal((Hq, D)) * qscale).astype(np.float32)
+    k = to_bf16_bits(rng.standard_normal((n, Hkv, D)))
+    v = to_bf16_bits(rng.standard_normal((n, Hkv, D)))
+    return q, k, v
+
+
+def parse_ranges(spec):
+    out = []
+    for part in spec.split("+"):
+        a, b = part.strip("[)").split(",")
+        out.extend(range(int(a), int(b)))
+    return np.asarray(out)
+
+
+# ---------------------------------------------------------------- key sets
+
+
+def test_local_window_golden():
+    for n, size, ranges in read_golden("local_window.txt"):
+        n, size = int(n), int(size)
+        got = keysets.local_keys(n, 4, 2048)
+        assert got.size == size, n
+        assert np.array_equal(got, parse_ranges(ranges)), n
+
+
+def test_local_equals_full_iff_n_le_s_plus_w():
+    # P1: the sets coincide exactly up to n = s + w = 2052 and differ from 2053 on
+    for n in list(range(1, 40)) + [2047, 2048, 2049, 2051, 2052]:
+        assert np.array_equal(keysets.local_keys(n), keysets.full_keys(n)), n
+    for n in [2053, 2054, 4096, 131073]:
+        assert not np.array_equal(keysets.local_keys(n), keysets.full_keys(n)), n
+
+
+@pytest.mark.parametrize("n", [1, 4, 5, 2048, 2052])
+def test_local_attention_bit_identical_to_full(n):
+    q, k, v = rand_case(n, 8, 2, seed=n)
+    o_l = attention.attend(q, k, v, keysets.local_keys(n), SCALE)
+    o_f = attention.attend(q, k, v, keysets.full_keys(n), SCALE)
+    assert np.array_equal(o_l, o_f)
+
+
+def test_local_attention_differs_past_window():
+    n = 2053
+    q, k, v = rand_case(n, 8, 2, seed=7)
+    o_l = attention.attend(q, k, v, keysets.local_keys(n), SCALE)
+    o_f = attention.attend(q, k, v, keysets.full_keys(n), SCALE)
+    assert np.abs(o_l - o_f).max() > 1e-6
+
+
+def test_all_blocks_equal_full():
+    # P2: DA's global mode (every block kept) is full attention
+    for n in [1, 15, 16, 17, 70, 1000]:
+        q, k, v = rand_case(n, 8, 2, seed=n + 100)
+        nb = (n + 15) // 16
+        ks = keysets.block_keys(n, range(nb))
+        assert np.array_equal(ks, keysets.full_keys(n))
+        o_b = attention.attend(q, k, v, ks, SCALE)
+        o_f = attention.attend(q, k, v, keysets.full_keys(n), SCALE)
+        assert np.array_equal(o_b, o_f)
+
+
+# ---------------------------------------------------------------- softmax invariants
+
+
+def test_weights_sum_to_one():
+    # P3: a value column of ones returns exactly the sum of the weights
+    n = 3000
+    q, k, v = rand_case(n, 8, 2, seed=3, qscale=4.0)
+    v = v.copy()
+    v[:, :, 5] = to_bf16_bits(1.0)
+    for keys in (keysets.full_keys(n), keysets.local_keys(n)):
+        o = attention.attend(q, k, v, keys, SCALE)
+        assert np.abs(o[:, 5] - 1.0).max() <= 1e-14
+
+
+def test_zero_query_gives_mean_of_values():
+    # P4: q = 0 -> uniform weights -> mean of V over S, computed independently
+    n = 2500
+    _, k, v = rand_case(n, 8, 2, seed=4)
+    q = np.zeros((8, 128), dtype=np.float32)
+    vf = torch.from_numpy(v.view(np.int16)).view(torch.bfloat16).double().numpy()
+    for keys in (keysets.full_keys(n), keysets.local_keys(n), keysets.block_keys(n, [0, 3, 100, 156])):
+        o = attention.attend(q, k, v, keys, SCALE)
+        ref = vf[keys].mean(axis=0)  # [Hkv][D]
+        for h in range(8):
+            assert np.allclose(o[h], ref[h // 4], rtol=0, atol=1e-14)
+
+
+def test_single_key_returns_its_value():
+    # P5: n = 1 -> o = v_0 exactly, whatever q is
+    q, k, v = rand_case(1, 8, 2, seed=5, qscale=10.0)
+    o = attention.attend(q, k, v, keysets.full_keys(1), SCALE)
+    vf = oracle.bf16_bits_to_f64(v[0])
+    for h in range(8):
+        assert np.array_equal(o[h], vf[h // 4])
+
+
+def test_membership_probe():
+    # P6: q = 0 and V encodes the position -> the output is the mean position of S,
+    # which exposes any missing or extra key
+    n = 4097
+    k = np.zeros((n, 2, 128), dtype=np.uint16)
+    v = np.zeros((n, 2, 128), dtype=np.uint16)
+    pos = np.arange(n)
+    v[:, :, 0] = to_bf16_bits((pos % 256) / 256.0)[:, None]
+    v[:, :, 1] = to_bf16_bits((pos // 256) / 256.0)[:, None]
+    q = np.zeros((8, 128), dtype=np.float32)
+    for keys, members in (
+        (keysets.local_keys(n), np.r_[0:4, n - 2048:n]),
+        (keysets.full_keys(n), np.arange(n)),
+        (keysets.block_keys(n, [0, 5, 256]), np.r_[0:16, 80:96, 4096:4097]),
+    ):
+        o = attention.attend(q, k, v, keys, SCALE)
+        assert abs(o[0, 0] - np.mean(members % 256) / 256.0) < 1e-12
+        assert abs(o[0, 1] - np.mean(members // 256) / 256.0) < 1e-12
+
+
+def test_gqa_grouping_is_contiguous():
+    # query head h reads KV head floor(h * Hkv / Hq): make V of KV head g the constant g + 1
+    for Hq, Hkv in ((8, 2), (16, 8), (32, 8), (4, 4)):
+        n = 37
+        q, k, _ = rand_case(n, Hq, Hkv, seed=Hq)
+        v = np.zeros((n, Hkv, 128), dtype=np.uint16)
+        for g in range(Hkv):
+            v[:, g, :] = to_bf16_bits(float(g + 1))
+        o = attention.attend(q, k, v, keysets.full_keys(n), SCALE)
+        for h in range(Hq):
+            assert np.allclose(o[h], (h * Hkv) // Hq + 1, rtol=0, atol=1e-13)
+
+
+def brute_force(q, k, v, keys, scale):
+    """Scalar loops with math.exp; no numpy arithmetic."""
+    Hq, D = q.shape
+    Hkv = k.shape[1]
+    kf = oracle.bf16_bits_to_f64(k).tolist()
+    vf = oracle.bf16_bits_to_f64(v).tolist()
+    out = []
+    for h in range(Hq):
+        g = h * Hkv // Hq
+        z = []
+        for j in keys:
+            s = 0.0
+            for d in range(D):
+                s += float(q[h, d]) * kf[j][g][d]
+            z.append(s * scale)
+        m = max(z)
+        e = [math.exp(x - m) for x in z]
+        tot = sum(e)
+        row = []
+        for d in range(D):
+            acc = 0.0
+            for w, j in zip(e, keys):
+                acc += w * vf[j][g][d]
+            row.append(acc / tot)
+        out.append(row)
+    return np.asarray(out)
+
+
+@pytest.mark.parametrize("n,Hq,Hkv,qs", [(1, 2, 1, 1.0), (7, 4, 2, 1.0), (33, 4, 1, 3.0), (64, 4, 4, 8.0)])
+def test_brute_force_small(n, Hq, Hkv, qs):
+    # P7
+    q, k, v = rand_case(n, Hq, Hkv, D=16, seed=n, qscale=qs)
+    for keys in (keysets.full_keys(n), keysets.local_keys(n, sinks=2, window=5)):
+        ref = brute_force(q, k, v, list(keys), 0.25)
+        got = attention.attend(q, k, v, keys, 0.25)
+        assert np.abs(got - ref).max() <= 1e-12
+
+
+def online_split_merge(q, k, v, keys, scale, splits):
+    """Second formulation: per-split online softmax state (m, l, acc) folded one
+    key at a time, then a log-sum-exp merge of the splits."""
+    qf = np.asarray(q, dtype=np.float64)
+    Hq, D = qf.shape
+    Hkv = k.shape[1]
+    kf = oracle.bf16_bits_to_f64(k)
+    vf = oracle.bf16_bits_to_f64(v)
+    parts = []
+    for part in np.array_split(np.asarray(keys), splits):
+        if part.size == 0:
+            continue
+        m = np.full(Hq, -np.inf)
+        l = np.zeros(Hq)
+        acc = np.zeros((Hq, D))
+        for j in part:
+            for h in range(Hq):
+                g = h * Hkv // Hq
+                z = scale * float(qf[h] @ kf[j, g])
+                mn = max(m[h], z)
+                a = math.exp(m[h] - mn) if m[h] != -np.inf else 0.0
+                b = math.exp(z - mn)
+                acc[h] = acc[h] * a + b * vf[j, g]
+                l[h] = l[h] * a + b
+                m[h] = mn
+        parts.append((m, l, acc))
+    M = np.max([p[0] for p in parts], axis=0)
+    L = sum(p[1] * np.exp(p[0] - M) for p in parts)
+    O = sum(p[2] * np.exp(p[0] - M)[:, None] for p in parts)
+    return O / L[:, None]
+
+
+@pytest.mark.parametrize("splits", [1, 3, 7])
+def test_online_split_merge_matches_two_pass(splits):
+    # P8
+    n = 300
+    q, k, v = rand_case(n, 4, 2, D=32, seed=splits, qscale=6.0)
+    for keys in (keysets.full_keys(n), keysets.local_keys(n, sinks=4, window=100)):
+        ref = online_split_merge(q, k, v, keys, 0.3, splits)
+        got = attention.attend(q, k, v, keys, 0.3)
+        assert np.abs(got - ref).max() <= 1e-12
+
+
+def test_scale_enters_the_logits():
+    # a peaky query selects the planted key: with the scale applied, weights follow exp(scale * <q,k>)
+    n = 10
+    D = 128
+    q = np.zeros((1, D), dtype=np.float32)
+    q[0, 0] = 8.0
+    k = np.zeros((n, 1, D), dtype=np.uint16)
+    v = np.zeros((n, 1, D), dtype=np.uint16)
+    k[3, 0, 0] = to_bf16_bits(2.0)
+    v[3, 0, 1] = to_bf16_bits(1.0)
+    o = attention.attend(q, k, v, keysets.full_keys(n), SCALE)
+    z = 16.0 * SCALE
+    assert abs(o[0, 1] - math.exp(z) / (math.exp(z) + 9.0)) < 1e-14
+
+
+# ---------------------------------------------------------------- recall head
+
+
+def test_gelu_textbook_values():
+    for a, phi in read_golden("gelu_phi.txt"):
+        a, phi = float(a), float(phi)
+        assert abs(recall.gelu(np.array([a]))[0] - a * phi) <= 1e-15 * max(1.0, abs(a))
+
+
+def test_gelu_against_math_erf_and_symmetry():
+    a = np.linspace(-6, 6, 1001)
+    ref = np.array([x * 0.5 * (1.0 + math.erf(x / math.sqrt(2.0))) for x in a])
+    assert np.abs(recall.gelu(a) - ref).max() <= 1e-15
+    # x Phi(x) - (-x) Phi(-x) = x
+    assert np.abs(recall.gelu(a) - recall.gelu(-a) - a).max() <= 1e-14
+
+
+def test_recall_score_against_loops():
+    # P10: the MLP against explicit loops, on a small head
+    rng = np.random.default_rng(11)
+    din, hid = 12, 5
+    W1 = rng.standard_normal((hid, din)).astype(np.float32)
+    b1 = rng.standard_normal(hid).astype(np.float32)
+    w2 = rng.standard_normal(hid).astype(np.float32)
+    b2 = np.float32(0.3)
+    parts = [rng.standard_normal(4).astype(np.float32) for _ in range(3)]
+    x = recall.concat_inputs(*parts)
+    assert np.array_equal(x[:4], parts[0]) and np.array_equal(x[8:], parts[2])
+    q = float(b2)
+    for i in range(hid):
+        a = float(b1[i]) + sum(float(W1[i, j]) * float(x[j]) for j in range(din))
+        q += float(w2[i]) * a * 0.5 * (1.0 + math.erf(a / math.sqrt(2.0)))
+    assert abs(recall.recall_score(x, W1, b1, w2, [b2]) - q) <= 1e-12
+
+
+def test_recall_closed_forms():
+    # zero first layer -> GELU(b1); W1 = I, b1 = 0, w2 = e_i picks GELU(x_i)
+    din = 6
+    x = np.array([1.0, -1.0, 2.0, 0.5, -2.0, 3.0])
+    b1 = np.array([1.0, 2.0])
+    assert abs(recall.recall_score(x, np.zeros((2, din)), b1, [1.0, 1.0], 0.0)
+               - (0.8413447460685429 + 2 * 0.9772498680518208)) < 1e-15
+    for i, (a, phi) in enumerate([(1.0, 0.8413447460685429), (-1.0, 0.15865525393145707),
+                                   (2.0, 0.9772498680518208)]):
+        w2 = np.zeros(din)
+        w2[i] = 1.0
+        assert abs(recall.recall_score(x, np.eye(din), np.zeros(din), w2, -0.25) - (a * phi - 0.25)) < 1e-15
+
+
+def test_gate_is_strict():
+    assert recall.gate(1e-300, 0.0) is True
+    assert recall.gate(0.0, 0.0) is False
+    assert recall.gate(-0.0, 0.0) is False
+    assert recall.gate(-1e-9, 0.0) is False
+    assert recall.gate(0.5, 0.5) is False
+
+
+# ---------------------------------------------------------------- DA gather
+
+
+def test_gather_golden():
+    rows = {r[0]: r[1:] for r in read_golden("da_gather.txt")}
+    n = int(rows["n"][0])
+    bt = [int(x) for x in rows["block_table"]]
+    kept = [int(x) for x in rows["kept"]]
+    phys, cnt = gather.gather_blocks(bt, kept, n)
+    exp = [tuple(int(y) for y in x.split(":")) for x in rows["gathered"]]
+    assert list(zip(phys.tolist(), cnt.tolist())) == exp
+    pos = []
+    for r in rows["positions"]:
+        a, b = r.split("-")
+        pos.extend(range(int(a), int(b) + 1))
+    assert np.array_equal(keysets.block_keys(n, kept), np.asarray(pos))
+
+
+def test_da_modes_golden():
+    rows = {r[0]: r[1:] for r in read_golden("da_modes.txt")}
+    n = int(rows["n"][0])
+    kw = dict(focus_begin=1, focus_end=3, output_begin=5, local_tokens=20)
+    for name, mode in (("global", gather.GLOBAL), ("focus", gather.FOCUS), ("local", gather.LOCAL)):
+        assert gather.da_mode_blocks(mode, n, **kw) == [int(x) for x in rows[name]]
+
+
+def test_gather_against_sets_and_masks():
+    # P11: set arithmetic vs the bit-mask path; permutation inverse; ordering
+    rng = np.random.default_rng(5)
+    for trial in range(20):
+        n = int(rng.integers(1, 5000))
+        nb = (n + 15) // 16
+        perm = rng.permutation(nb + 7)[:nb]
+        kept = set(rng.choice(nb, size=int(rng.integers(1, nb + 1)), replace=False).tolist())
+        words = np.zeros((nb + 31) // 32 + 1, dtype=np.uint32)
+        for b in kept:
+            words[b // 32] |= np.uint32(1 << (b % 32))
+        assert gather.mask_to_blocks(words, n) == sorted(kept)
+        phys, cnt = gather.gather_blocks(perm, kept, n)
+        inv = {int(p): b for b, p in enumerate(perm)}
+        logical = [inv[int(p)] for p in phys]
+        assert logical == sorted(kept)
+        assert int(cnt.sum()) == len(set(keysets.block_keys(n, kept).tolist()))
+        last = nb - 1
+        for b, c in zip(logical, cnt):
+            assert c == (n - 16 * last if b == last else 16)
+
+
+# ---------------------------------------------------------------- ODA step and cost
+
+
+def test_commit_holds_selected_candidate():
+    # P12: the slot n-1 holds the local candidate unless the step recalled
+    n = 50
+    q, k, v = rand_case(n, 4, 2, seed=9)
+    kl, vl = to_bf16_bits(np.full((2, 128), 0.5)), to_bf16_bits(np.full((2, 128), -0.5))
+    kf, vf = to_bf16_bits(np.full((2, 128), 1.5)), to_bf16_bits(np.full((2, 128), 2.5))
+    for g in (False, True):
+        hk, hv = k.copy(), v.copy()
+        o_l = oda.local_pass(q, kl, vl, hk, hv, n, SCALE)
+        assert np.array_equal(hk[n - 1], kl)
+        o_f = oda.full_pass(q, kf, vf, hk, hv, n, SCALE) if g else None
+        out = oda.select(g, o_l, o_f)
+        assert np.array_equal(hk[n - 1], kf if g else kl)
+        assert np.array_equal(hv[n - 1], vf if g else vl)
+        assert np.array_equal(hk[:n - 1], k[:n - 1])
+        assert out is (o_f if g else o_l)
+
+
+def test_request_mode():
+    assert oda.request_mode(0.1, 0.0, oda.MODE_LOCAL) == oda.MODE_FULL
+    assert oda.request_mode(0.0, 0.0, oda.MODE_BLOCKS) == oda.MODE_BLOCKS
+    assert oda.request_mode(-2.0, 0.0, oda.MODE_LOCAL) == oda.MODE_LOCAL
+
+
+def test_cost_model_golden():
+    rows = read_golden("cost_model.txt")
+    d = {r[0]: r[1:] for r in rows}
+    ns = [131073 + t for t in range(1024)]
+    flags = [t % 8 == 7 for t in range(1024)]
+    assert sum(cost.local_size(n) for n in ns) == int(d["sum_local"][0])
+    assert sum(n for n, f in zip(ns, flags) if f) == int(d["sum_recall"][0])
+    assert sum(ns) == int(d["sum_full"][0])
+    assert cost.oda_over_full(ns, flags) == Fraction(int(d["ratio_num"][0]), int(d["ratio_den"][0]))
+    for r in rows:
+        if r[0] == "step_ratio":
+            assert cost.local_over_full(int(r[1])) == Fraction(r[2])
+    # closed form min(n, s+w)/n
+    for n in [1, 100, 2052, 2053, 9999]:
+        assert cost.local_over_full(n) == Fraction(min(n, 2052), n)
+
+
+def test_cost_counters():
+    assert cost.kv_bytes(131072, 8, 128) == 131072 * 4096
+    assert cost.kv_bytes(2052, 2, 128) == 2052 * 1024
+    assert cost.attention_flops(10, 32, 128) == 4 * 32 * 128 * 10
