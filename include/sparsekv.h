@@ -1,0 +1,235 @@
+/*
+ * sparsekv.h -- C ABI of libsparsekv: single-token decode attention over a
+ * paged bf16 KV cache that reads only a selected subset of it, for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * Sources of the operations (web pages, cited by title and section):
+ *  [ODA]  "On-Demand Attention: Language Models Know When to Recall"
+ *         (arxiv-wiki summary). "Approach": local-first decoding with s = 4
+ *         initial tokens and a recent window w = 2048, a recall head that
+ *         scores the step from (h_{t-1}, E(x_t), h^L_t), a full recompute when
+ *         q_t > theta, and commit of the selected pass's current-position KV
+ *         into the preserved history. "Main results": the window includes the
+ *         current token. "Developer perspective": a Local view and a paged
+ *         full view of one preserved KV cache; the FP32 recall head and the
+ *         conditional Full pass stay in one GPU execution flow.
+ *  [DA]   "[Paper review] Language Models Can Control Their Own Attention"
+ *         (blog review of Declarative Attention), section 3 "Method & Key
+ *         Results": the mask is applied at KV-block granularity and the block
+ *         table is rewritten so the attention kernel sees only kept blocks;
+ *         section 1 "Key Terms": the global / focus / local modes.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every pointer argument is DEVICE memory owned by the caller (for example
+ *    torch tensors), unless a comment says otherwise. The library allocates
+ *    nothing, copies nothing to the host and keeps no state between calls.
+ *  - Every call is asynchronous on the caller's stream `stream` and never
+ *    synchronizes with the host (the only exception is sk_workspace_error,
+ *    which says so).
+ *  - Return value: SK_OK (0) when the work was enqueued; a negative SK_E_*
+ *    code when an argument is invalid (nothing is enqueued then); or
+ *    -(1000 + hipError_t) when a kernel launch failed.
+ *  - Errors that only the device can see (a block id outside the pool, a
+ *    sequence length outside [1, max_blocks*16], an empty key set) set bits
+ *    of the error word in the workspace header (SK_DEVERR_*). A request with
+ *    an invalid length or an empty key set gets an all-zero output row; a
+ *    request that hits an out-of-range block id has an unspecified output.
+ *  - A workspace (see sk_workspace_bytes) must be cleared once with
+ *    sk_workspace_init before first use; the kernels leave it ready for the
+ *    next call. Calls that share one workspace must be ordered (for example
+ *    issued on one stream); concurrent calls on one workspace race.
+ *  - All entry points are reentrant and may be captured in a HIP graph: none
+ *    of them records a memset or a host callback.
+ *
+ * Paged KV layout (sk_paged_kv)
+ * -----------------------------
+ *  The cache is a pool of physical blocks of 16 token positions. For every
+ *  (physical block p, KV head g) there is one 4096-byte K tile and one
+ *  4096-byte V tile, at byte offset (p * num_kv_heads + g) * 4096 of
+ *  k_pool / v_pool. Inside a tile the 16 x 128 bf16 values are stored in the
+ *  order the gfx950 matrix cores consume them:
+ *    K tile: element (token t, dim d) at byte (d/8)*256 + t*16 + (d%8)*2
+ *    V tile: element (token t, dim d) at byte (d/32)*1024 + (t/4)*256
+ *            + (d%16)*16 + ((d%32)/16)*8 + (t%4)*2
+ *  Callers do not need to know this order: sk_kv_write / sk_kv_read move
+ *  tokens between row-major [count][num_kv_heads][128] bf16 arrays and the
+ *  pool, and the decode calls commit the current token themselves.
+ *  block_tables[b * max_blocks + i] is the physical block holding logical
+ *  positions 16i .. 16i+15 of request b. seq_lens[b] = n, the number of
+ *  visible positions INCLUDING the current token, which lives at position
+ *  n-1 ([ODA] "Main results": the window counts the current token).
+ */
+#ifndef SPARSEKV_H
+#define SPARSEKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ---- */
+#define SK_OK 0
+#define SK_E_NULL (-1)        /* a required pointer is NULL */
+#define SK_E_SHAPE (-2)       /* unsupported shape: head_dim != 128, block_size != 16, Hq/Hkv > 16, ... */
+#define SK_E_HEADS (-3)       /* num_q_heads is not a multiple of num_kv_heads */
+#define SK_E_RANGE (-4)       /* a size or index argument is out of range */
+#define SK_E_WORKSPACE (-5)   /* workspace too small for this call */
+#define SK_E_LAUNCH_BASE (-1000) /* -(1000 + hipError_t): a launch failed */
+
+/* ---- device error bits (workspace header word) ---- */
+#define SK_DEVERR_BLOCK_ID 1  /* a block id outside [0, num_phys_blocks) */
+#define SK_DEVERR_SEQ_LEN 2   /* seq_lens[b] outside [1, max_blocks*16] */
+#define SK_DEVERR_EMPTY 4     /* a request's key set is empty */
+
+/* ---- per-request view selectors (ragged batches) ---- */
+#define SK_MODE_LOCAL 0
+#define SK_MODE_FULL 1
+#define SK_MODE_BLOCKS 2
+
+/* ---- Declarative-Attention declared modes ([DA] section 1) ---- */
+#define SK_DA_GLOBAL 0
+#define SK_DA_FOCUS 1
+#define SK_DA_LOCAL 2
+
+typedef struct sk_paged_kv {
+  void* k_pool;                 /* bf16 tiles, [num_phys_blocks][num_kv_heads][4096 B] */
+  void* v_pool;                 /* bf16 tiles, same shape */
+  const int32_t* block_tables;  /* [batch][max_blocks] logical block -> physical block */
+  const int32_t* seq_lens;      /* [batch] visible positions n, current token included */
+  int32_t batch;
+  int32_t num_q_heads;          /* Hq; query head h reads KV head h / (Hq/Hkv) */
+  int32_t num_kv_heads;         /* Hkv; Hq/Hkv must be in 1..16 */
+  int32_t head_dim;             /* must be 128 */
+  int32_t block_size;           /* must be 16 */
+  int32_t max_blocks;           /* columns of block_tables */
+  int64_t num_phys_blocks;      /* blocks in each pool */
+} sk_paged_kv;
+
+/* Bytes of workspace needed by every decode / recall call on up to `batch`
+ * requests with up to `num_q_heads` query heads: a header (error word,
+ * tickets) plus split partials. Depends only on its arguments. */
+size_t sk_workspace_bytes(int32_t batch, int32_t num_q_heads);
+
+/* Clears a workspace (error word, tickets) with a fill kernel on `stream`. */
+int sk_workspace_init(void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Reads the workspace error word: enqueues a copy on `stream`, WAITS for the
+ * stream, and stores the SK_DEVERR_* bits in *err_out (host pointer).
+ * This is the one call that synchronizes with the host. */
+int sk_workspace_error(const void* ws, int32_t* err_out, hipStream_t stream);
+
+/* Human-readable text of a status code (static storage, never NULL). */
+const char* sk_status_str(int status);
+
+/* Writes `count` tokens of request `request` at logical positions
+ * pos0 .. pos0+count-1 into the pool. k, v: bf16 [count][num_kv_heads][128],
+ * row-major. Used to fill a history (prefill) or to restore a cache.
+ * Host-checked: 0 <= request < batch, 0 <= pos0, pos0 + count <= max_blocks*16;
+ * count == 0 enqueues nothing (k and v may then be NULL).
+ * Block ids outside the pool are skipped and reported in the error word of
+ * `ws` when ws is not NULL. seq_lens is not read. */
+int sk_kv_write(sk_paged_kv kv, int32_t request, int32_t pos0, int32_t count,
+                const void* k, const void* v, void* ws, hipStream_t stream);
+
+/* Inverse of sk_kv_write: copies positions pos0 .. pos0+count-1 of request
+ * `request` out of the pool into row-major k_out, v_out
+ * ([count][num_kv_heads][128] bf16). Positions in out-of-range blocks read
+ * as zero and set the error bit when ws is not NULL. */
+int sk_kv_read(sk_paged_kv kv, int32_t request, int32_t pos0, int32_t count,
+               void* k_out, void* v_out, void* ws, hipStream_t stream);
+
+/* Commit ([ODA] "Approach"): writes the current token of every request
+ * (k_new, v_new: bf16 [batch][num_kv_heads][128]) into position
+ * seq_lens[b]-1. When `sel` is not NULL, only requests with
+ * sel[b] == sel_value are written. The decode calls below can do the same
+ * commit themselves (their k_new / v_new arguments); this entry point is the
+ * stand-alone form. */
+int sk_kv_append(sk_paged_kv kv, const void* k_new, const void* v_new,
+                 const int32_t* sel, int32_t sel_value, void* ws, hipStream_t stream);
+
+/* Local-first view ([ODA] "Approach", "Main results"): for every request b
+ * with n = seq_lens[b], attends the key positions
+ *   [0, min(sinks, n))  union  [max(min(sinks, n), n - window), n)
+ * with softmax scale `scale` (typically 1/sqrt(128)).
+ *  q      : fp32 [batch][num_q_heads][128]
+ *  out    : fp32 [batch][num_q_heads][128]; rows of requests that do not run
+ *           are left untouched, so a later call may fill them
+ *  k_new, v_new : NULL, or bf16 [batch][num_kv_heads][128] -- the current
+ *           token's key/value, committed to position n-1 before it is
+ *           attended (fused commit)
+ *  sel    : NULL (every request runs) or int32 [batch]; request b runs iff
+ *           sel[b] == sel_value
+ *  ws     : workspace of at least sk_workspace_bytes(batch, num_q_heads)
+ * Host-checked: sinks >= 0, window >= 1. */
+int oda_decode_local(const float* q, sk_paged_kv kv, const void* k_new, const void* v_new,
+                     int32_t sinks, int32_t window, float scale,
+                     const int32_t* sel, int32_t sel_value,
+                     float* out, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Full view ([ODA] "Approach": recompute the step over the whole preserved
+ * history): attends positions [0, n). Arguments as oda_decode_local. For the
+ * on-device gate, pass sel = the gate array written by oda_recall_score and
+ * sel_value = 1: requests whose gate is 0 do no work, write nothing and
+ * commit nothing, so a launch on a non-recall step costs only its dispatch.
+ * Committing k_new here overwrites the Local pass's candidate at n-1, so the
+ * slot ends up holding the selected pass's KV. */
+int oda_decode_full(const float* q, sk_paged_kv kv, const void* k_new, const void* v_new,
+                    float scale, const int32_t* sel, int32_t sel_value,
+                    float* out, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Recall head and gate ([ODA] "Approach" and "Developer perspective"), FP32:
+ *   a = W1 x_b + b1;  u = GELU(a) (exact erf form);  q_b = <w2, u> + b2;
+ *   gate_b = (q_b > theta) ? 1 : 0          (strict comparison)
+ *  x  : fp32 [batch][in_dim], the concatenation [h_{t-1}, E(x_t), h^L_t]
+ *  W1 : fp32 [hidden][in_dim] row-major;  b1, w2 : fp32 [hidden];  b2 : fp32 [1]
+ *  q_out : fp32 [batch];  gate_out : int32 [batch]
+ * Host-checked: 1 <= batch <= 64, in_dim % 4 == 0, 1 <= in_dim <= 65536,
+ * 1 <= hidden. The reduction order is fixed, so results are deterministic. */
+int oda_recall_score(const float* x, const float* W1, const float* b1, const float* w2,
+                     const float* b2, int32_t batch, int32_t in_dim, int32_t hidden,
+                     float theta, float* q_out, int32_t* gate_out,
+                     void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Gate from given scores (no recall-head GEMV): for every request,
+ *   out[b] = (scores[b] > theta) ? 1 : (fallback ? fallback[b] : 0).
+ * With fallback = NULL this is the recall gate; with a per-request fallback
+ * view (SK_MODE_LOCAL or SK_MODE_BLOCKS) it is the per-request view of a
+ * ragged batch (SK_MODE_FULL == 1 when the score passes). */
+int oda_gate_scores(const float* scores, int32_t batch, float theta,
+                    const int32_t* fallback, int32_t* out, hipStream_t stream);
+
+/* Declared mode -> logical keep mask ([DA] sections 1 and 3), one bit per
+ * logical block (bit i of word i/32, little-endian), words per request =
+ * (max_blocks + 31) / 32. decl: int32 [batch][4] =
+ * {mode, focus_begin_block, focus_end_block, output_begin_block}.
+ *  SK_DA_GLOBAL: every block holding a visible position (blocks < ceil(n/16));
+ *  SK_DA_FOCUS : blocks in [focus_begin, focus_end) plus blocks >= output_begin,
+ *                both cut at ceil(n/16);
+ *  SK_DA_LOCAL : blocks overlapping the last `local_tokens` positions.
+ * Bits of blocks >= ceil(n/16) are written as 0. */
+int da_keep_mask(const int32_t* decl, sk_paged_kv kv, int32_t local_tokens,
+                 uint32_t* keep_mask, hipStream_t stream);
+
+/* Block-table rewrite plus attention over the kept blocks ([DA] section 3).
+ * For every selected request b, the kept logical blocks (bits of keep_mask
+ * row b below ceil(n/16)) are compacted in ascending logical order into
+ *   gathered[b][i]     = block_tables[b][block_i]   (physical id)
+ *   gathered_cnt[b][i] = min(16, n - 16*block_i)    (valid positions)
+ *   num_kept[b]        = number of entries
+ * (rows of [batch][max_blocks] int32), and the request attends exactly the
+ * positions of those blocks. k_new / v_new, when given, are committed to
+ * position n-1 in every case and attended when their block is kept.
+ * Other arguments as oda_decode_local. */
+int da_decode_blocks(const float* q, sk_paged_kv kv, const void* k_new, const void* v_new,
+                     const uint32_t* keep_mask, int32_t* gathered, int32_t* gathered_cnt,
+                     int32_t* num_kept, float scale, const int32_t* sel, int32_t sel_value,
+                     float* out, void* ws, size_t ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SPARSEKV_H */

@@ -1,0 +1,181 @@
+// Recall head, gate and per-request view selection.
+//
+// On-Demand Attention summary page, "Approach": a recall head maps the three inputs
+// available before any global read (previous selected hidden state, current token
+// embedding, current Local final hidden state) to one scalar q_t, and the step is
+// recomputed with Full attention when q_t > theta (theta = 0 by default).
+// "Developer perspective": the head is evaluated in FP32 inside the same GPU
+// execution flow as the Local pass and the conditional Full pass, so the decision
+// never goes back to the host.
+//
+// The head here is a two-layer MLP, q = <w2, GELU(W1 x + b1)> + b2 (exact-erf GELU).
+// It is a GEMV: each wave keeps one row of W1 (in_dim fp32) in registers and dots it
+// with every request's x; no matrix cores are used. Per-workgroup partial sums are
+// added in a fixed order by the last workgroup (atomic ticket), so q is deterministic.
+#include <math.h>
+
+#include "sk_internal.h"
+
+namespace sk {
+namespace {
+
+constexpr int kRecallMaxBatch = 64;
+constexpr int kRecallMaxIn = 65536;
+constexpr int kRecallWaves = 4;  // one W1 row per wave
+
+__device__ inline float gelu_erf(float a) { return 0.5f * a * (1.0f + erff(a * 0.70710678118654752f)); }
+
+// CHUNKS > 0: the W1 row (CHUNKS float4 per lane) stays in registers across requests.
+// CHUNKS == 0: long rows are streamed from memory once per request.
+template <int CHUNKS>
+__global__ __launch_bounds__(256) void recall_kernel(const float* __restrict__ x, const float* __restrict__ W1,
+                                                     const float* __restrict__ b1, const float* __restrict__ w2,
+                                                     const float* __restrict__ b2, int B, int in_dim, int hidden,
+                                                     float theta, float* __restrict__ q_out,
+                                                     int32_t* __restrict__ gate_out, float* partials,
+                                                     uint32_t* ticket) {
+  __shared__ float s_c[kRecallWaves][kRecallMaxBatch];
+  __shared__ int s_last;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int row = blockIdx.x * kRecallWaves + wave;
+  const int n4 = in_dim / 4;
+  const f32x4* wrow = reinterpret_cast<const f32x4*>(W1 + size_t(row < hidden ? row : 0) * in_dim);
+  constexpr int R = CHUNKS > 0 ? CHUNKS : 1;
+  f32x4 w[R];
+  if (CHUNKS > 0) {
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      int c = lane + 64 * i;
+      w[i] = (row < hidden && c < n4) ? wrow[c] : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+  for (int b = 0; b < B; ++b) {
+    float dot = 0.f;
+    const f32x4* xb = reinterpret_cast<const f32x4*>(x + size_t(b) * in_dim);
+    if (CHUNKS > 0) {
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        int c = lane + 64 * i;
+        if (c < n4) {
+          f32x4 v = xb[c];
+          dot += w[i].x * v.x + w[i].y * v.y + w[i].z * v.z + w[i].w * v.w;
+        }
+      }
+    } else if (row < hidden) {
+      for (int c = lane; c < n4; c += 64) {
+        f32x4 v = xb[c], u = wrow[c];
+        dot += u.x * v.x + u.y * v.y + u.z * v.z + u.w * v.w;
+      }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) dot += __shfl_xor(dot, off);
+    if (lane == 0) s_c[wave][b] = (row < hidden) ? w2[row] * gelu_erf(dot + b1[row]) : 0.f;
+  }
+  __syncthreads();
+  for (int b = tid; b < B; b += blockDim.x) {
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < kRecallWaves; ++i) s += s_c[i][b];
+    partials[size_t(blockIdx.x) * B + b] = s;
+  }
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) s_last = (atomicAdd(ticket, 1u) == gridDim.x - 1);
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+  for (int b = tid; b < B; b += blockDim.x) {
+    float s = 0.f;
+    for (unsigned i = 0; i < gridDim.x; ++i) s += partials[size_t(i) * B + b];
+    float q = s + b2[0];
+    q_out[b] = q;
+    gate_out[b] = (q > theta) ? 1 : 0;
+  }
+  if (tid == 0) *ticket = 0u;
+}
+
+__global__ void gate_scores_kernel(const float* __restrict__ scores, int B, float theta,
+                                   const int32_t* __restrict__ fallback, int32_t* __restrict__ out) {
+  int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b < B) out[b] = (scores[b] > theta) ? 1 : (fallback ? fallback[b] : 0);
+}
+
+__global__ void keep_mask_kernel(const int32_t* __restrict__ decl, sk_paged_kv kv, int local_tokens,
+                                 uint32_t* __restrict__ mask) {
+  const int words_row = (kv.max_blocks + 31) / 32;
+  int64_t gid = blockIdx.x * int64_t(blockDim.x) + threadIdx.x;
+  if (gid >= int64_t(kv.batch) * words_row) return;
+  const int b = int(gid / words_row), w = int(gid % words_row);
+  const int n = kv.seq_lens[b];
+  const int nb = (n >= 1 && n <= kv.max_blocks * kBlock) ? (n + kBlock - 1) / kBlock : 0;
+  const int mode = decl[4 * b], fb = decl[4 * b + 1], fe = decl[4 * b + 2], ob = decl[4 * b + 3];
+  const int first_local = (n > local_tokens ? n - local_tokens : 0) / kBlock;
+  uint32_t bits = 0u;
+  for (int i = 0; i < 32; ++i) {
+    int blk = 32 * w + i;
+    bool keep = false;
+    if (blk < nb) {
+      if (mode == SK_DA_GLOBAL) keep = true;
+      else if (mode == SK_DA_FOCUS) keep = (blk >= fb && blk < fe) || blk >= ob;
+      else if (mode == SK_DA_LOCAL) keep = blk >= first_local;
+    }
+    bits |= uint32_t(keep) << i;
+  }
+  mask[gid] = bits;
+}
+
+template <int CHUNKS>
+int launch_recall(const float* x, const float* W1, const float* b1, const float* w2, const float* b2, int B,
+                  int in_dim, int hidden, float theta, float* q_out, int32_t* gate_out, void* ws,
+                  hipStream_t stream) {
+  int nwg = (hidden + kRecallWaves - 1) / kRecallWaves;
+  float* partials = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(ws) + kPartialsOffset);
+  uint32_t* ticket = reinterpret_cast<uint32_t*>(ws) + 1;
+  hipLaunchKernelGGL(recall_kernel<CHUNKS>, dim3(nwg), dim3(64 * kRecallWaves), 0, stream, x, W1, b1, w2, b2, B,
+                     in_dim, hidden, theta, q_out, gate_out, partials, ticket);
+  return launch_status(hipGetLastError());
+}
+
+}  // namespace
+}  // namespace sk
+
+using namespace sk;
+
+extern "C" {
+
+int oda_recall_score(const float* x, const float* W1, const float* b1, const float* w2, const float* b2,
+                     int32_t batch, int32_t in_dim, int32_t hidden, float theta, float* q_out, int32_t* gate_out,
+                     void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!x || !W1 || !b1 || !w2 || !b2 || !q_out || !gate_out || !ws) return SK_E_NULL;
+  if (batch < 1 || batch > kRecallMaxBatch || in_dim < 4 || in_dim > kRecallMaxIn || (in_dim % 4) || hidden < 1)
+    return SK_E_RANGE;
+  size_t need = kPartialsOffset + size_t((hidden + kRecallWaves - 1) / kRecallWaves) * batch * 4;
+  if (ws_bytes < need) return SK_E_WORKSPACE;
+  int chunks = (in_dim / 4 + 63) / 64;  // float4 per lane
+  if (chunks <= 8) return launch_recall<8>(x, W1, b1, w2, b2, batch, in_dim, hidden, theta, q_out, gate_out, ws, stream);
+  if (chunks <= 24) return launch_recall<24>(x, W1, b1, w2, b2, batch, in_dim, hidden, theta, q_out, gate_out, ws, stream);
+  return launch_recall<0>(x, W1, b1, w2, b2, batch, in_dim, hidden, theta, q_out, gate_out, ws, stream);
+}
+
+int oda_gate_scores(const float* scores, int32_t batch, float theta, const int32_t* fallback, int32_t* out,
+                    hipStream_t stream) {
+  if (!scores || !out) return SK_E_NULL;
+  if (batch < 1) return SK_E_RANGE;
+  hipLaunchKernelGGL(gate_scores_kernel, dim3((batch + 255) / 256), dim3(256), 0, stream, scores, batch, theta,
+                     fallback, out);
+  return launch_status(hipGetLastError());
+}
+
+int da_keep_mask(const int32_t* decl, sk_paged_kv kv, int32_t local_tokens, uint32_t* keep_mask,
+                 hipStream_t stream) {
+  int st = check_kv(kv);
+  if (st) return st;
+  if (!decl || !keep_mask) return SK_E_NULL;
+  if (local_tokens < 0) return SK_E_RANGE;
+  int64_t threads = int64_t(kv.batch) * ((kv.max_blocks + 31) / 32);
+  hipLaunchKernelGGL(keep_mask_kernel, dim3(unsigned((threads + 255) / 256)), dim3(256), 0, stream, decl, kv,
+                     local_tokens, keep_mask);
+  return launch_status(hipGetLastError());
+}
+
+}  // extern "C"

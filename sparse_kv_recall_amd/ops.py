@@ -1,0 +1,216 @@
+"""Torch-facing binding of libsparsekv: same names as the C ABI, argument marshalling only.
+
+Tensors must live on the GPU; every step of the computation runs in the HIP
+library on torch's current stream. Nothing here computes a result.
+"""
+
+import math
+
+import torch
+
+from . import _lib
+
+BLOCK = 16
+HEAD_DIM = 128
+TILE_ELEMS = BLOCK * HEAD_DIM
+
+MODE_LOCAL, MODE_FULL, MODE_BLOCKS = 0, 1, 2
+DA_GLOBAL, DA_FOCUS, DA_LOCAL = 0, 1, 2
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device=None):
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _check(t, dtype, name, numel=None):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor" % name)
+    if t.dtype != dtype:
+        raise ValueError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if numel is not None and t.numel() < numel:
+        raise ValueError("%s has %d elements, needs %d" % (name, t.numel(), numel))
+
+
+class PagedKVCache:
+    """Device memory of one paged bf16 KV cache (one attention layer).
+
+    k_pool / v_pool: bf16 [num_phys_blocks][num_kv_heads][16*128] tiles in the
+    library's tile order; block_tables: int32 [batch][max_blocks];
+    seq_lens: int32 [batch] (visible positions, current token included).
+    """
+
+    def __init__(self, num_phys_blocks, batch, num_q_heads, num_kv_heads, max_blocks, device="cuda",
+                 block_tables=None, seq_lens=None, k_pool=None, v_pool=None):
+        self.num_phys_blocks = int(num_phys_blocks)
+        self.batch = int(batch)
+        self.num_q_heads = int(num_q_heads)
+        self.num_kv_heads = int(num_kv_heads)
+        self.max_blocks = int(max_blocks)
+        shape = (self.num_phys_blocks, self.num_kv_heads, TILE_ELEMS)
+        self.k_pool = k_pool if k_pool is not None else torch.empty(shape, dtype=torch.bfloat16, device=device)
+        self.v_pool = v_pool if v_pool is not None else torch.empty(shape, dtype=torch.bfloat16, device=device)
+        self.block_tables = (block_tables if block_tables is not None else
+                             torch.zeros((self.batch, self.max_blocks), dtype=torch.int32, device=device))
+        self.seq_lens = (seq_lens if seq_lens is not None else
+                         torch.zeros(self.batch, dtype=torch.int32, device=device))
+        _check(self.k_pool, torch.bfloat16, "k_pool", self.num_phys_blocks * self.num_kv_heads * TILE_ELEMS)
+        _check(self.v_pool, torch.bfloat16, "v_pool", self.num_phys_blocks * self.num_kv_heads * TILE_ELEMS)
+        _check(self.block_tables, torch.int32, "block_tables", self.batch * self.max_blocks)
+        _check(self.seq_lens, torch.int32, "seq_lens", self.batch)
+
+    def abi(self):
+        return _lib.PagedKVStruct(self.k_pool.data_ptr(), self.v_pool.data_ptr(), self.block_tables.data_ptr(),
+                                  self.seq_lens.data_ptr(), self.batch, self.num_q_heads, self.num_kv_heads,
+                                  HEAD_DIM, BLOCK, self.max_blocks, self.num_phys_blocks)
+
+    def nbytes(self):
+        return self.k_pool.numel() * 2 * 2
+
+
+def workspace_bytes(batch, num_q_heads):
+    return int(_lib.load().sk_workspace_bytes(int(batch), int(num_q_heads)))
+
+
+def workspace(batch, num_q_heads, device="cuda"):
+    """Allocate and clear a workspace for calls on up to `batch` requests."""
+    n = workspace_bytes(batch, num_q_heads)
+    ws = torch.empty(n, dtype=torch.uint8, device=device)
+    _lib.call("sk_workspace_init", ws.data_ptr(), n, _stream(ws.device))
+    return ws
+
+
+def workspace_error(ws):
+    """SK_DEVERR_* bits of the workspace (synchronizes the current stream)."""
+    import ctypes
+    v = ctypes.c_int32(0)
+    _lib.call("sk_workspace_error", ws.data_ptr(), ctypes.addressof(v), _stream(ws.device))
+    return int(v.value)
+
+
+def kv_write(kv, request, pos0, k, v, ws=None):
+    count = k.shape[0]
+    _check(k, torch.bfloat16, "k", count * kv.num_kv_heads * HEAD_DIM)
+    _check(v, torch.bfloat16, "v", count * kv.num_kv_heads * HEAD_DIM)
+    _lib.call("sk_kv_write", kv.abi(), int(request), int(pos0), int(count), k.data_ptr(), v.data_ptr(), _ptr(ws),
+              _stream(k.device))
+
+
+def kv_read(kv, request, pos0, count, ws=None):
+    k = torch.empty((count, kv.num_kv_heads, HEAD_DIM), dtype=torch.bfloat16, device=kv.k_pool.device)
+    v = torch.empty_like(k)
+    _lib.call("sk_kv_read", kv.abi(), int(request), int(pos0), int(count), k.data_ptr(), v.data_ptr(), _ptr(ws),
+              _stream(k.device))
+    return k, v
+
+
+def kv_append(kv, k_new, v_new, sel=None, sel_value=1, ws=None):
+    n = kv.batch * kv.num_kv_heads * HEAD_DIM
+    _check(k_new, torch.bfloat16, "k_new", n)
+    _check(v_new, torch.bfloat16, "v_new", n)
+    _check(sel, torch.int32, "sel", kv.batch)
+    _lib.call("sk_kv_append", kv.abi(), k_new.data_ptr(), v_new.data_ptr(), _ptr(sel), int(sel_value), _ptr(ws),
+              _stream(k_new.device))
+
+
+def _decode_common(q, kv, k_new, v_new, sel, out, ws):
+    _check(q, torch.float32, "q", kv.batch * kv.num_q_heads * HEAD_DIM)
+    n = kv.batch * kv.num_kv_heads * HEAD_DIM
+    _check(k_new, torch.bfloat16, "k_new", n)
+    _check(v_new, torch.bfloat16, "v_new", n)
+    _check(sel, torch.int32, "sel", kv.batch)
+    if out is None:
+        out = torch.zeros((kv.batch, kv.num_q_heads, HEAD_DIM), dtype=torch.float32, device=q.device)
+    _check(out, torch.float32, "out", kv.batch * kv.num_q_heads * HEAD_DIM)
+    if ws is None:
+        ws = workspace(kv.batch, kv.num_q_heads, q.device)
+    _check(ws, torch.uint8, "ws")
+    return out, ws
+
+
+def oda_decode_local(q, kv, k_new=None, v_new=None, sinks=4, window=2048, scale=None, sel=None,
+                     sel_value=MODE_LOCAL, out=None, ws=None):
+    out, ws = _decode_common(q, kv, k_new, v_new, sel, out, ws)
+    scale = 1.0 / math.sqrt(HEAD_DIM) if scale is None else float(scale)
+    _lib.call("oda_decode_local", q.data_ptr(), kv.abi(), _ptr(k_new), _ptr(v_new), int(sinks), int(window), scale,
+              _ptr(sel), int(sel_value), out.data_ptr(), ws.data_ptr(), ws.numel(), _stream(q.device))
+    return out
+
+
+def oda_decode_full(q, kv, k_new=None, v_new=None, scale=None, sel=None, sel_value=1, out=None, ws=None):
+    out, ws = _decode_common(q, kv, k_new, v_new, sel, out, ws)
+    scale = 1.0 / math.sqrt(HEAD_DIM) if scale is None else float(scale)
+    _lib.call("oda_decode_full", q.data_ptr(), kv.abi(), _ptr(k_new), _ptr(v_new), scale, _ptr(sel),
+              int(sel_value), out.data_ptr(), ws.data_ptr(), ws.numel(), _stream(q.device))
+    return out
+
+
+def oda_recall_score(x, W1, b1, w2, b2, theta=0.0, q_out=None, gate_out=None, ws=None):
+    batch, in_dim = x.shape
+    hidden = W1.shape[0]
+    for t, name, n in ((x, "x", batch * in_dim), (W1, "W1", hidden * in_dim), (b1, "b1", hidden),
+                       (w2, "w2", hidden), (b2, "b2", 1)):
+        _check(t, torch.float32, name, n)
+    if q_out is None:
+        q_out = torch.empty(batch, dtype=torch.float32, device=x.device)
+    if gate_out is None:
+        gate_out = torch.empty(batch, dtype=torch.int32, device=x.device)
+    _check(q_out, torch.float32, "q_out", batch)
+    _check(gate_out, torch.int32, "gate_out", batch)
+    if ws is None:
+        ws = workspace(batch, 1, x.device)
+    _lib.call("oda_recall_score", x.data_ptr(), W1.data_ptr(), b1.data_ptr(), w2.data_ptr(), b2.data_ptr(),
+              int(batch), int(in_dim), int(hidden), float(theta), q_out.data_ptr(), gate_out.data_ptr(),
+              ws.data_ptr(), ws.numel(), _stream(x.device))
+    return q_out, gate_out
+
+
+def oda_gate_scores(scores, theta=0.0, fallback=None, out=None):
+    batch = scores.numel()
+    _check(scores, torch.float32, "scores", batch)
+    _check(fallback, torch.int32, "fallback", batch)
+    if out is None:
+        out = torch.empty(batch, dtype=torch.int32, device=scores.device)
+    _check(out, torch.int32, "out", batch)
+    _lib.call("oda_gate_scores", scores.data_ptr(), int(batch), float(theta), _ptr(fallback), out.data_ptr(),
+              _stream(scores.device))
+    return out
+
+
+def da_keep_mask(decl, kv, local_tokens=1024, mask=None):
+    words = (kv.max_blocks + 31) // 32
+    _check(decl, torch.int32, "decl", kv.batch * 4)
+    if mask is None:
+        mask = torch.empty((kv.batch, words), dtype=torch.int32, device=decl.device)
+    _check(mask, torch.int32, "mask", kv.batch * words)
+    _lib.call("da_keep_mask", decl.data_ptr(), kv.abi(), int(local_tokens), mask.data_ptr(), _stream(decl.device))
+    return mask
+
+
+def da_decode_blocks(q, kv, keep_mask, k_new=None, v_new=None, scale=None, sel=None, sel_value=MODE_BLOCKS,
+                     out=None, gathered=None, gathered_cnt=None, num_kept=None, ws=None):
+    out, ws = _decode_common(q, kv, k_new, v_new, sel, out, ws)
+    words = (kv.max_blocks + 31) // 32
+    _check(keep_mask, torch.int32, "keep_mask", kv.batch * words)
+    dev = q.device
+    if gathered is None:
+        gathered = torch.zeros((kv.batch, kv.max_blocks), dtype=torch.int32, device=dev)
+    if gathered_cnt is None:
+        gathered_cnt = torch.zeros((kv.batch, kv.max_blocks), dtype=torch.int32, device=dev)
+    if num_kept is None:
+        num_kept = torch.zeros(kv.batch, dtype=torch.int32, device=dev)
+    _check(gathered, torch.int32, "gathered", kv.batch * kv.max_blocks)
+    _check(gathered_cnt, torch.int32, "gathered_cnt", kv.batch * kv.max_blocks)
+    _check(num_kept, torch.int32, "num_kept", kv.batch)
+    scale = 1.0 / math.sqrt(HEAD_DIM) if scale is None else float(scale)
+    _lib.call("da_decode_blocks", q.data_ptr(), kv.abi(), _ptr(k_new), _ptr(v_new), keep_mask.data_ptr(),
+              gathered.data_ptr(), gathered_cnt.data_ptr(), num_kept.data_ptr(), scale, _ptr(sel), int(sel_value),
+              out.data_ptr(), ws.data_ptr(), ws.numel(), _stream(dev))
+    return out, gathered, gathered_cnt, num_kept

@@ -1,0 +1,94 @@
+"""CPU checks of the C ABI: the library loads, exports every declared symbol, and
+rejects invalid arguments with the documented codes before touching a GPU."""
+
+import ctypes
+
+import pytest
+
+from sparse_kv_recall_amd import _lib
+
+SK_E_NULL, SK_E_SHAPE, SK_E_HEADS, SK_E_RANGE, SK_E_WORKSPACE = -1, -2, -3, -4, -5
+FAKE = 0x1000  # never dereferenced: every call below fails validation first
+
+
+def lib():
+    try:
+        return _lib.load()
+    except _lib.LibraryMissing as e:
+        pytest.fail(str(e))
+
+
+def test_exports_every_header_function():
+    names = _lib.header_functions()
+    assert len(names) >= 13
+    L = lib()
+    missing = [n for n in names if not hasattr(L, n)]
+    assert not missing, missing
+    assert set(_lib._SIGNATURES) == set(names)
+
+
+def kv(**over):
+    d = dict(k_pool=FAKE, v_pool=FAKE, block_tables=FAKE, seq_lens=FAKE, batch=1, num_q_heads=32,
+             num_kv_heads=8, head_dim=128, block_size=16, max_blocks=100, num_phys_blocks=100)
+    d.update(over)
+    return _lib.PagedKVStruct(**d)
+
+
+def decode_full(k, ws_bytes=1 << 30, q=FAKE, out=FAKE, ws=FAKE):
+    return lib().oda_decode_full(q, k, None, None, 0.1, None, 1, out, ws, ws_bytes, None)
+
+
+def test_decode_argument_validation():
+    assert decode_full(kv(k_pool=None)) == SK_E_NULL
+    assert decode_full(kv(), q=None) == SK_E_NULL
+    assert decode_full(kv(head_dim=64)) == SK_E_SHAPE
+    assert decode_full(kv(block_size=32)) == SK_E_SHAPE
+    assert decode_full(kv(num_q_heads=12)) == SK_E_HEADS
+    assert decode_full(kv(num_q_heads=64, num_kv_heads=2)) == SK_E_SHAPE  # group 32 > 16
+    assert decode_full(kv(batch=0)) == SK_E_RANGE
+    assert decode_full(kv(max_blocks=0)) == SK_E_RANGE
+    assert decode_full(kv(), ws_bytes=16) == SK_E_WORKSPACE
+    L = lib()
+    assert L.oda_decode_local(FAKE, kv(), None, None, -1, 2048, 0.1, None, 0, FAKE, FAKE, 1 << 30, None) == SK_E_RANGE
+    assert L.oda_decode_local(FAKE, kv(), None, None, 4, 0, 0.1, None, 0, FAKE, FAKE, 1 << 30, None) == SK_E_RANGE
+    # k_new without v_new
+    assert L.oda_decode_local(FAKE, kv(), FAKE, None, 4, 2048, 0.1, None, 0, FAKE, FAKE, 1 << 30, None) == SK_E_NULL
+
+
+def test_other_entry_points_validation():
+    L = lib()
+    assert L.oda_recall_score(None, FAKE, FAKE, FAKE, FAKE, 1, 8, 4, 0.0, FAKE, FAKE, FAKE, 1 << 20, None) == SK_E_NULL
+    assert L.oda_recall_score(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 8, 4, 0.0, FAKE, FAKE, FAKE, 1 << 20, None) == SK_E_RANGE
+    assert L.oda_recall_score(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 6, 4, 0.0, FAKE, FAKE, FAKE, 1 << 20, None) == SK_E_RANGE
+    assert L.oda_recall_score(FAKE, FAKE, FAKE, FAKE, FAKE, 65, 8, 4, 0.0, FAKE, FAKE, FAKE, 1 << 20, None) == SK_E_RANGE
+    assert L.oda_recall_score(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, 4, 0.0, FAKE, FAKE, FAKE, 8, None) == SK_E_WORKSPACE
+    assert L.oda_gate_scores(None, 1, 0.0, None, FAKE, None) == SK_E_NULL
+    assert L.oda_gate_scores(FAKE, 0, 0.0, None, FAKE, None) == SK_E_RANGE
+    assert L.da_keep_mask(None, kv(), 1024, FAKE, None) == SK_E_NULL
+    assert L.da_keep_mask(FAKE, kv(), -1, FAKE, None) == SK_E_RANGE
+    assert L.da_decode_blocks(FAKE, kv(), None, None, None, FAKE, FAKE, FAKE, 0.1, None, 2, FAKE, FAKE,
+                              1 << 30, None) == SK_E_NULL
+    assert L.sk_kv_write(kv(), 1, 0, 1, FAKE, FAKE, None, None) == SK_E_RANGE       # request >= batch
+    assert L.sk_kv_write(kv(), 0, 1599, 2, FAKE, FAKE, None, None) == SK_E_RANGE    # past max_blocks*16
+    assert L.sk_kv_write(kv(), 0, 0, 1, None, FAKE, None, None) == SK_E_NULL
+    assert L.sk_kv_write(kv(), 0, 0, 0, None, None, None, None) == 0  # empty write: nothing enqueued
+    assert L.sk_kv_read(kv(), 0, -1, 1, FAKE, FAKE, None, None) == SK_E_RANGE
+    assert L.sk_kv_append(kv(), None, FAKE, None, 0, None, None) == SK_E_NULL
+    assert L.sk_workspace_init(None, 1 << 20, None) == SK_E_NULL
+    assert L.sk_workspace_init(FAKE, 8, None) == SK_E_WORKSPACE
+    assert L.sk_workspace_error(None, FAKE, None) == SK_E_NULL
+
+
+def test_workspace_size_monotone_and_status_strings():
+    L = lib()
+    prev = 0
+    for b in (1, 2, 8, 32, 1024):
+        for h in (1, 8, 32):
+            s = L.sk_workspace_bytes(b, h)
+            assert s > 0
+            if h == 32:
+                assert s >= prev
+                prev = s
+    assert L.sk_workspace_bytes(32, 32) >= L.sk_workspace_bytes(1, 32)
+    for code in (0, -1, -2, -3, -4, -5, -1001, 7):
+        assert isinstance(L.sk_status_str(code), bytes) and L.sk_status_str(code)

@@ -1,0 +1,323 @@
+"""GPU parity of the decode entry points against the fp64 oracle on small shapes.
+
+Shapes span several 16-position tiles, several splits and ragged tails; unwritten
+slots and unkept blocks of the pool hold bf16 NaN, so any over-read shows up.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import attention, gather, keysets
+from synth import rng
+from tests.helpers import (SCALE, HostCache, bf16_tensor_to_bits, bits_to_bf16_tensor, check_close, rand_bits,
+                           rand_f32, requires_gpu)
+
+pytestmark = [pytest.mark.gpu, requires_gpu]
+
+NS_EDGE = [1, 3, 4, 5, 15, 16, 17, 31, 32, 33, 47, 100, 2051, 2052, 2053, 2069, 4097]
+
+
+def _q(Hq, B, seed, sigma=1.0):
+    return rand_f32(rng.mix_key(901, seed), (B, Hq, 128), sigma)
+
+
+def _run_full(hc, q, **kw):
+    from sparse_kv_recall_amd import ops
+    out = ops.oda_decode_full(torch.as_tensor(q, device="cuda"), hc.kv, **kw)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(8, 2), (16, 8), (32, 8), (4, 4), (32, 2)])
+def test_full_edge_lengths(Hq, Hkv):
+    ns = NS_EDGE if Hq <= 16 else NS_EDGE[::2]
+    hc = HostCache(Hq, Hkv, ns, seed=Hq + Hkv)
+    q = _q(Hq, len(ns), seed=3)
+    got = _run_full(hc, q)
+    for b, n in enumerate(ns):
+        ref = attention.attend(q[b], hc.k[b], hc.v[b], keysets.full_keys(n), SCALE)
+        check_close(got[b], ref, what="full n=%d" % n)
+        if n <= 5000:
+            check_close(got[b], ref, abs_tol=1e-5, row_rel_tol=1e-4, what="full tight n=%d" % n)
+
+
+@pytest.mark.parametrize("sinks,window", [(4, 2048), (3, 20), (0, 17), (20, 5), (4, 1)])
+def test_local_edge_lengths(sinks, window):
+    Hq, Hkv = 8, 2
+    ns = NS_EDGE
+    hc = HostCache(Hq, Hkv, ns, seed=sinks * 31 + window)
+    q = _q(Hq, len(ns), seed=4)
+    from sparse_kv_recall_amd import ops
+    out = ops.oda_decode_local(torch.as_tensor(q, device="cuda"), hc.kv, sinks=sinks, window=window)
+    got = out.cpu().numpy()
+    for b, n in enumerate(ns):
+        ref = attention.attend(q[b], hc.k[b], hc.v[b], keysets.local_keys(n, sinks, window), SCALE)
+        check_close(got[b], ref, abs_tol=1e-5, row_rel_tol=1e-4, what="local n=%d s=%d w=%d" % (n, sinks, window))
+
+
+def test_local_equals_full_up_to_s_plus_w():
+    Hq, Hkv = 8, 2
+    ns = [1, 4, 5, 2048, 2052]
+    hc = HostCache(Hq, Hkv, ns, seed=77)
+    q = _q(Hq, len(ns), seed=5)
+    from sparse_kv_recall_amd import ops
+    qt = torch.as_tensor(q, device="cuda")
+    a = ops.oda_decode_local(qt, hc.kv).cpu().numpy()
+    f = ops.oda_decode_full(qt, hc.kv).cpu().numpy()
+    for b, n in enumerate(ns):
+        ref = attention.attend(q[b], hc.k[b], hc.v[b], keysets.full_keys(n), SCALE)
+        check_close(a[b], ref, abs_tol=1e-5, row_rel_tol=1e-4)
+        check_close(f[b], ref, abs_tol=1e-5, row_rel_tol=1e-4)
+
+
+def test_peaky_queries_rescale_path():
+    # q scaled x8 plus planted matching keys far apart: the running max changes across splits
+    Hq, Hkv = 32, 8
+    ns = [5000, 70000]
+    hc = HostCache(Hq, Hkv, ns, seed=8, poison=False)
+    q = _q(Hq, len(ns), seed=6, sigma=8.0)
+    from sparse_kv_recall_amd import ops
+    for b, n in enumerate(ns):
+        for pos in (3, n // 3, n - 2):
+            g = 1
+            kb = hc.k[b][pos].copy()
+            qk = np.clip(q[b, g * 4] / 8.0, -3, 3)
+            kb[g] = oracle_bits(qk)
+            hc.k[b][pos] = kb
+            ops.kv_write(hc.kv, b, pos, bits_to_bf16_tensor(kb[None]), bits_to_bf16_tensor(hc.v[b][pos][None]))
+    got = _run_full(hc, q)
+    for b, n in enumerate(ns):
+        ref = attention.attend(q[b], hc.k[b], hc.v[b], keysets.full_keys(n), SCALE)
+        check_close(got[b], ref, what="peaky n=%d" % n)
+        check_close(got[b], ref, abs_tol=1e-4, row_rel_tol=1e-4, what="peaky tight n=%d" % n)
+
+
+def oracle_bits(x):
+    from synth.rng import f32_to_bf16_bits
+    return f32_to_bf16_bits(np.asarray(x, np.float32))
+
+
+def test_fused_commit_full_and_local():
+    from sparse_kv_recall_amd import ops
+    Hq, Hkv = 16, 8
+    ns = [1, 16, 17, 300, 2100]
+    hc = HostCache(Hq, Hkv, ns, seed=12)
+    B = len(ns)
+    q = _q(Hq, B, seed=9)
+    kn = rand_bits(rng.mix_key(902, 1), B, Hkv)
+    vn = rand_bits(rng.mix_key(902, 2), B, Hkv)
+    knt, vnt = bits_to_bf16_tensor(kn), bits_to_bf16_tensor(vn)
+    qt = torch.as_tensor(q, device="cuda")
+    for mode in ("local", "full"):
+        if mode == "local":
+            out = ops.oda_decode_local(qt, hc.kv, knt, vnt)
+        else:
+            out = ops.oda_decode_full(qt, hc.kv, knt, vnt)
+        got = out.cpu().numpy()
+        for b, n in enumerate(ns):
+            k = hc.k[b].copy()
+            v = hc.v[b].copy()
+            oracle.oda.commit(k, v, n, kn[b], vn[b])
+            keys = keysets.local_keys(n) if mode == "local" else keysets.full_keys(n)
+            ref = attention.attend(q[b], k, v, keys, SCALE)
+            check_close(got[b], ref, abs_tol=1e-5, row_rel_tol=1e-4, what="%s commit n=%d" % (mode, n))
+            kr, vr = ops.kv_read(hc.kv, b, n - 1, 1)
+            assert np.array_equal(bf16_tensor_to_bits(kr)[0], kn[b])
+            assert np.array_equal(bf16_tensor_to_bits(vr)[0], vn[b])
+            # the rest of the history is untouched
+            kr, vr = ops.kv_read(hc.kv, b, 0, n - 1)
+            assert np.array_equal(bf16_tensor_to_bits(kr), hc.k[b][:n - 1])
+            assert np.array_equal(bf16_tensor_to_bits(vr), hc.v[b][:n - 1])
+
+
+def test_selector_and_gate_skip_requests():
+    from sparse_kv_recall_amd import ops
+    Hq, Hkv = 8, 2
+    ns = [40, 500, 3000, 9]
+    hc = HostCache(Hq, Hkv, ns, seed=13)
+    B = len(ns)
+    q = _q(Hq, B, seed=10)
+    qt = torch.as_tensor(q, device="cuda")
+    gate = torch.tensor([1, 0, 1, 0], dtype=torch.int32, device="cuda")
+    kn = rand_bits(rng.mix_key(903, 1), B, Hkv)
+    vn = rand_bits(rng.mix_key(903, 2), B, Hkv)
+    out = torch.full((B, Hq, 128), 7.0, device="cuda")
+    ops.oda_decode_full(qt, hc.kv, bits_to_bf16_tensor(kn), bits_to_bf16_tensor(vn), sel=gate, sel_value=1, out=out)
+    got = out.cpu().numpy()
+    for b, n in enumerate(ns):
+        if b in (1, 3):
+            assert (got[b] == 7.0).all()
+            kr, _ = ops.kv_read(hc.kv, b, n - 1, 1)
+            assert np.array_equal(bf16_tensor_to_bits(kr)[0], hc.k[b][n - 1])  # nothing committed
+        else:
+            k = hc.k[b].copy()
+            v = hc.v[b].copy()
+            oracle.oda.commit(k, v, n, kn[b], vn[b])
+            ref = attention.attend(q[b], k, v, keysets.full_keys(n), SCALE)
+            check_close(got[b], ref, abs_tol=1e-5, row_rel_tol=1e-4)
+
+
+def _mask_words(kept_lists, max_blocks):
+    words = (max_blocks + 31) // 32
+    m = np.zeros((len(kept_lists), words), np.uint32)
+    for b, kept in enumerate(kept_lists):
+        for blk in kept:
+            m[b, blk // 32] |= np.uint32(1 << (blk % 32))
+    return m
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_blocks_gather_and_attention(seed):
+    from sparse_kv_recall_amd import ops
+    Hq, Hkv = 32, 8
+    g = np.random.default_rng(seed)
+    ns = [int(x) for x in g.integers(1, 6000, size=5)] + [16, 17, 1]
+    hc = HostCache(Hq, Hkv, ns, seed=20 + seed)
+    B = len(ns)
+    kept = []
+    for n in ns:
+        nb = (n + 15) // 16
+        k = set(g.choice(nb, size=int(g.integers(1, nb + 1)), replace=False).tolist())
+        k.add(nb - 1)
+        kept.append(sorted(k))
+    # stale bits beyond ceil(n/16) must be ignored
+    mask = _mask_words([kp + [hc.max_blocks - 1] for kp in kept], hc.max_blocks)
+    q = _q(Hq, B, seed=11)
+    out, gat, cnt, num = ops.da_decode_blocks(torch.as_tensor(q, device="cuda"), hc.kv,
+                                              torch.as_tensor(mask.view(np.int32), device="cuda"))
+    got, gat, cnt, num = out.cpu().numpy(), gat.cpu().numpy(), cnt.cpu().numpy(), num.cpu().numpy()
+    for b, n in enumerate(ns):
+        phys, c = gather.gather_blocks(hc.bt[b], kept[b], n)
+        assert num[b] == len(phys)
+        assert np.array_equal(gat[b, :num[b]], phys)
+        assert np.array_equal(cnt[b, :num[b]], c)
+        ref = attention.attend(q[b], hc.k[b], hc.v[b], keysets.block_keys(n, kept[b]), SCALE)
+        check_close(got[b], ref, abs_tol=1e-5, row_rel_tol=1e-4, what="blocks n=%d" % n)
+
+
+def test_blocks_all_kept_equals_full_and_commit_when_unkept():
+    from sparse_kv_recall_amd import ops
+    Hq, Hkv = 32, 8
+    ns = [1000, 33, 4097]
+    hc = HostCache(Hq, Hkv, ns, seed=31)
+    B = len(ns)
+    q = _q(Hq, B, seed=12)
+    qt = torch.as_tensor(q, device="cuda")
+    allm = _mask_words([list(range((n + 15) // 16)) for n in ns], hc.max_blocks)
+    o_b, _, _, _ = ops.da_decode_blocks(qt, hc.kv, torch.as_tensor(allm.view(np.int32), device="cuda"))
+    o_f = ops.oda_decode_full(qt, hc.kv)
+    for b, n in enumerate(ns):
+        ref = attention.attend(q[b], hc.k[b], hc.v[b], keysets.full_keys(n), SCALE)
+        check_close(o_b.cpu().numpy()[b], ref, abs_tol=1e-5, row_rel_tol=1e-4)
+        check_close(o_f.cpu().numpy()[b], ref, abs_tol=1e-5, row_rel_tol=1e-4)
+    # keep-list without the current token's block: the token is committed, not attended
+    kn = rand_bits(rng.mix_key(904, 1), B, Hkv)
+    vn = rand_bits(rng.mix_key(904, 2), B, Hkv)
+    kept = [[0, 1], [0], [3, 100]]
+    m = _mask_words(kept, hc.max_blocks)
+    out, _, _, _ = ops.da_decode_blocks(qt, hc.kv, torch.as_tensor(m.view(np.int32), device="cuda"),
+                                        bits_to_bf16_tensor(kn), bits_to_bf16_tensor(vn))
+    for b, n in enumerate(ns):
+        k = hc.k[b].copy()
+        v = hc.v[b].copy()
+        oracle.oda.commit(k, v, n, kn[b], vn[b])
+        ref = attention.attend(q[b], k, v, keysets.block_keys(n, kept[b]), SCALE)
+        check_close(out.cpu().numpy()[b], ref, abs_tol=1e-5, row_rel_tol=1e-4)
+        kr, vr = ops.kv_read(hc.kv, b, n - 1, 1)
+        assert np.array_equal(bf16_tensor_to_bits(kr)[0], kn[b])
+        assert np.array_equal(bf16_tensor_to_bits(vr)[0], vn[b])
+
+
+def test_keep_mask_modes():
+    from sparse_kv_recall_amd import ops
+    Hq, Hkv = 8, 2
+    ns = [100, 33000, 5, 1]
+    hc = HostCache(Hq, Hkv, ns, seed=40, max_blocks=2100)
+    decl = np.array([[gather.FOCUS, 1, 3, 5], [gather.GLOBAL, 0, 0, 0], [gather.LOCAL, 0, 0, 0],
+                     [gather.FOCUS, 0, 10, 0]], np.int32)
+    m = ops.da_keep_mask(torch.as_tensor(decl, device="cuda"), hc.kv, local_tokens=20).cpu().numpy().view(np.uint32)
+    for b, n in enumerate(ns):
+        exp = gather.da_mode_blocks(int(decl[b, 0]), n, int(decl[b, 1]), int(decl[b, 2]), int(decl[b, 3]),
+                                    local_tokens=20)
+        words = np.zeros(m.shape[1], np.uint32)
+        for blk in exp:
+            words[blk // 32] |= np.uint32(1 << (blk % 32))
+        assert np.array_equal(m[b], words), b
+
+
+def test_recall_head_small():
+    from sparse_kv_recall_amd import ops
+    g = np.random.default_rng(3)
+    for B, din, hid in ((1, 6144, 512), (3, 100, 7), (5, 2048, 33)):
+        x = g.standard_normal((B, din)).astype(np.float32)
+        W1 = (g.standard_normal((hid, din)) * 0.02).astype(np.float32)
+        b1 = (g.standard_normal(hid) * 0.1).astype(np.float32)
+        w2 = (g.standard_normal(hid) * 0.02).astype(np.float32)
+        b2 = np.array([0.01], np.float32)
+        dev = lambda a: torch.as_tensor(a, device="cuda")
+        qo, go = ops.oda_recall_score(dev(x), dev(W1), dev(b1), dev(w2), dev(b2), theta=0.0)
+        qo, go = qo.cpu().numpy(), go.cpu().numpy()
+        for b in range(B):
+            ref = oracle.recall.recall_score(x[b], W1, b1, w2, b2)
+            assert abs(qo[b] - ref) <= 1e-5 * max(1.0, abs(ref)), (qo[b], ref)
+            if abs(ref) >= 1e-4:
+                assert bool(go[b]) == oracle.recall.gate(ref, 0.0)
+
+
+def test_gate_scores_and_modes():
+    from sparse_kv_recall_amd import ops
+    s = torch.tensor([0.5, 0.0, -0.0, -1.0, 1e-30, float("nan")], device="cuda")
+    out = ops.oda_gate_scores(s, 0.0).cpu().numpy()
+    assert out.tolist() == [1, 0, 0, 0, 1, 0]
+    fb = torch.tensor([0, 2, 2, 0, 0, 2], dtype=torch.int32, device="cuda")
+    out = ops.oda_gate_scores(s, 0.0, fallback=fb).cpu().numpy()
+    assert out.tolist() == [1, 2, 2, 0, 1, 2]
+
+
+def test_invalid_lengths_set_device_error_and_zero_rows():
+    from sparse_kv_recall_amd import ops
+    Hq, Hkv = 8, 2
+    hc = HostCache(Hq, Hkv, [50, 60], seed=50)
+    hc.set_lens([0, 60])
+    ws = ops.workspace(2, Hq)
+    q = _q(Hq, 2, seed=13)
+    out = torch.full((2, Hq, 128), 3.0, device="cuda")
+    ops.oda_decode_full(torch.as_tensor(q, device="cuda"), hc.kv, out=out, ws=ws)
+    err = ops.workspace_error(ws)
+    assert err & 2
+    got = out.cpu().numpy()
+    assert (got[0] == 0).all()
+    ref = attention.attend(q[1], hc.k[1], hc.v[1], keysets.full_keys(60), SCALE)
+    check_close(got[1], ref, abs_tol=1e-5, row_rel_tol=1e-4)
+
+
+def test_kv_write_read_roundtrip_and_layout():
+    from sparse_kv_recall_amd import ops
+    Hq, Hkv = 32, 8
+    hc = HostCache(Hq, Hkv, [77], seed=60, permute=True)
+    k, v = ops.kv_read(hc.kv, 0, 0, 77)
+    assert np.array_equal(bf16_tensor_to_bits(k), hc.k[0][:77])
+    assert np.array_equal(bf16_tensor_to_bits(v), hc.v[0][:77])
+    # documented tile byte order
+    kp = bf16_tensor_to_bits(hc.kv.k_pool).reshape(hc.kv.num_phys_blocks, Hkv, 2048)
+    vp = bf16_tensor_to_bits(hc.kv.v_pool).reshape(hc.kv.num_phys_blocks, Hkv, 2048)
+    for pos in (0, 5, 16, 40, 76):
+        blk, t = pos // 16, pos % 16
+        p = hc.bt[0][blk]
+        for g in (0, 7):
+            for d in (0, 7, 8, 31, 32, 100, 127):
+                assert kp[p, g, ((d // 8) * 256 + t * 16 + (d % 8) * 2) // 2] == hc.k[0][pos, g, d]
+                off = (d // 32) * 1024 + (t // 4) * 256 + (d % 16) * 16 + ((d // 16) % 2) * 8 + (t % 4) * 2
+                assert vp[p, g, off // 2] == hc.v[0][pos, g, d]
+
+
+def test_deterministic_replay():
+    from sparse_kv_recall_amd import ops
+    Hq, Hkv = 32, 8
+    hc = HostCache(Hq, Hkv, [40000, 3000], seed=70, poison=False)
+    q = torch.as_tensor(_q(Hq, 2, seed=14), device="cuda")
+    a = ops.oda_decode_full(q, hc.kv).cpu().numpy()
+    b = ops.oda_decode_full(q, hc.kv).cpu().numpy()
+    assert np.array_equal(a, b)
