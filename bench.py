@@ -1,0 +1,248 @@
+#!/usr/bin/env python3
+"""Decode-attention throughput of On-Demand Attention at a 128K context, 12.5 % recall.
+
+Workload (synthetic, seeded; stands in for the ODA summary page's 128K-input / 1K-output
+vLLM measurement in "Main results"): a 36-layer attention stack with 32 query / 8 KV
+heads, head dim 128, bf16 paged KV (block 16) holding 131072 history positions that
+grows by one position per decode step, batch 1. Every step runs, per layer, the Local
+view (4 sinks + 2048-position window, current token committed), then the on-device
+gate, then the gated Full view over the whole history (recomputing the step and
+committing the Full candidate) on exactly 128 of the 1024 steps.
+
+One step = one replay of a HIP graph holding: the input feed (synthetic projections:
+the step's q / k / v candidates and the length n), 36 Local launches, the gate, and 36
+gated Full launches. Inputs are resident in HBM before timing starts.
+
+Output: one JSON line (metric, tokens/s, ms per step, the roofline of the dominant
+kernel -- the Full view at n ~ 132K -- and the fp64 oracle timed on the host cores).
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode-attn tokens/s at 128K ctx, 12.5% recall rate; achieved HBM GB/s vs peak"
+HBM_PEAK_GBS = 8000.0
+
+
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def build_stack(wl, device):
+    import torch
+    from sparse_kv_recall_amd.stack import ODAStack
+    from synth import device as sdev
+    from synth.workloads import C_KHIST, C_VHIST
+
+    bt = torch.as_tensor(wl.block_tables, device=device)
+    seq_lens = torch.zeros(wl.batch, dtype=torch.int32, device=device)
+    stack = ODAStack(wl.layers, wl.batch, wl.Hq, wl.Hkv, wl.num_phys_blocks, wl.max_blocks, bt, seq_lens,
+                     sinks=wl.sinks, window=wl.window, device=device)
+    H0 = int(wl.H0[0])
+    from sparse_kv_recall_amd import ops
+    stage_k = torch.empty((H0, wl.Hkv, 128), dtype=torch.bfloat16, device=device)
+    stage_v = torch.empty_like(stage_k)
+    for l in range(wl.layers):
+        sdev.fill_normal_(stage_k, wl.key(C_KHIST, l), 0)
+        sdev.fill_normal_(stage_v, wl.key(C_VHIST, l), 0)
+        ops.kv_write(stack.caches[l], 0, 0, stage_k, stage_v)
+    torch.cuda.synchronize()
+    del stage_k, stage_v
+    return stack
+
+
+def capture_step(stack, feeder):
+    from sparse_kv_recall_amd.stack import capture_graph
+    q, k, v = feeder.q, feeder.k, feeder.v
+
+    def step():
+        feeder.step()
+        stack.local_pass(q[:, 0, :], k[:, 0, :], v[:, 0, :])
+        stack.gate_from_scores(feeder.scores, 0.0)
+        stack.full_pass(q[:, 1, :], k[:, 1, :], v[:, 1, :], gated=True)
+
+    return capture_graph(step)
+
+
+def roofline_full(stack, feeder, reps):
+    """Average duration of the Full-view kernel over all layers at the current n, with HIP
+    events on the launching stream; every launch runs (no gate)."""
+    import torch
+    q, k, v = feeder.q, feeder.k, feeder.v
+    stack.full_pass(q[:, 1, :], k[:, 1, :], v[:, 1, :], gated=False)  # warm
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        stack.full_pass(q[:, 1, :], k[:, 1, :], v[:, 1, :], gated=False)
+    e1.record()
+    e1.synchronize()
+    return e0.elapsed_time(e1) / (reps * stack.layers)
+
+
+def copy_calibration(device):
+    """A plain copy of known size (512 MiB) for scaling the HBM counters."""
+    import torch
+    a = torch.empty(256 << 20, dtype=torch.int16, device=device)
+    b = torch.empty_like(a)
+    a.fill_(1)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    return a.numel() * 2
+
+
+def cpu_baseline(wl, recall_rate, budget_s=20.0):
+    """The fp64 oracle, as it stands, on a bounded sample of the same workload: Local
+    layer-steps and one Full layer-step at step 0 (n = 131073), timed on the host cores.
+    Input generation is not timed. Tokens/s = 1 / (L * t_local + rate * L * t_full)."""
+    import numpy as np
+    import oracle
+    from synth.workloads import C_KHIST, C_VHIST  # noqa: F401
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    H0 = int(wl.H0[0])
+    n = H0 + 1
+    scale = 1.0 / math.sqrt(128.0)
+    t_local, n_local = 0.0, 0
+    layer_full = 1
+    # Local sample: the positions the Local view reads, per layer
+    for l in range(4):
+        k = np.zeros((n, wl.Hkv, 128), np.uint16)
+        v = np.zeros((n, wl.Hkv, 128), np.uint16)
+        k[:4] = wl.hist_bits("k", l, 0, 4)
+        v[:4] = wl.hist_bits("v", l, 0, 4)
+        k[n - 2048:n - 1] = wl.hist_bits("k", l, n - 2048, 2047)
+        v[n - 2048:n - 1] = wl.hist_bits("v", l, n - 2048, 2047)
+        q = wl.cand_q(0, l, 0, 0)
+        kn, vn = wl.cand_kv(0, l, 0, 0)
+        t0 = time.perf_counter()
+        oracle.oda.local_pass(q, kn, vn, k, v, n, scale)
+        t_local += time.perf_counter() - t0
+        n_local += 1
+    t_local /= n_local
+    k = np.empty((n, wl.Hkv, 128), np.uint16)
+    v = np.empty((n, wl.Hkv, 128), np.uint16)
+    k[:H0] = wl.hist_bits("k", layer_full, 0, H0)
+    v[:H0] = wl.hist_bits("v", layer_full, 0, H0)
+    q = wl.cand_q(0, layer_full, 1, 0)
+    kn, vn = wl.cand_kv(0, layer_full, 1, 0)
+    t0 = time.perf_counter()
+    oracle.oda.full_pass(q, kn, vn, k, v, n, scale)
+    t_full = time.perf_counter() - t0
+    step_s = wl.layers * t_local + recall_rate * wl.layers * t_full
+    return {"value": 1.0 / step_s, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": ("fp64 oracle at step 0 (n=131073): %d Local layer-steps (%.4f s each) and 1 Full "
+                       "layer-step (%.3f s); per-step time = 36*t_local + 0.125*36*t_full; input "
+                       "generation not timed" % (n_local, t_local, t_full))}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1024)
+    ap.add_argument("--warmup", type=int, default=16)
+    ap.add_argument("--roofline-reps", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the decode path here is built and measured on a single "
+              "MI355X (see DESIGN.md for how it would shard); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from synth import workloads
+    from synth.device import Feeder
+
+    device = "cuda"
+    torch.cuda.init()
+    wl = workloads.oda_stack128k()
+    if args.steps < 1 or args.steps > wl.steps:
+        print("--steps must be in 1..%d (the workload's decode steps)" % wl.steps, file=sys.stderr)
+        sys.exit(2)
+    log("staging %d layers x %d positions of bf16 KV" % (wl.layers, int(wl.H0[0])))
+    t0 = time.time()
+    stack = build_stack(wl, device)
+    feeder = Feeder(wl, stack.seq_lens, device=device, with_scores=True)
+    log("staged in %.1f s; capturing the step graph" % (time.time() - t0))
+    graph = capture_step(stack, feeder)
+
+    for _ in range(args.warmup):
+        graph.replay()
+    feeder.set_step(0)
+    torch.cuda.synchronize()
+    log("warmup done; timing %d steps" % args.steps)
+
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_total = e0.elapsed_time(e1)
+    ms_per_step = ms_total / args.steps
+    tok_s = args.steps * wl.batch / (ms_total / 1e3)
+    recalls = int((wl.sched_scores[:args.steps, 0] > 0).sum())
+    assert torch.isfinite(stack.out).all().item(), "non-finite decode output"
+    log("timed: %.3f ms/step (%.1f tok/s, wall %.2f s), %d recall steps" % (ms_per_step, tok_s, wall, recalls))
+
+    # dominant kernel: the Full view at the last step's n, every layer, no gate
+    n_now = int(stack.seq_lens[0].item())
+    full_ms = roofline_full(stack, feeder, args.roofline_reps)
+    bytes_full = n_now * wl.Hkv * 128 * 2 * 2 + 2 * wl.Hq * 128 * 4 + 2 * wl.Hkv * 128 * 2
+    achieved = bytes_full / (full_ms * 1e-3) / 1e9
+    log("Full-view kernel at n=%d: %.1f us per launch, %.0f GB/s" % (n_now, full_ms * 1e3, achieved))
+    copy_calibration(device)
+
+    # step bytes (algorithmic): Local reads min(n, 2052) positions per layer, Full n on recall steps
+    ns = wl.H0[0] + 1 + np.arange(args.steps)
+    rec = wl.sched_scores[:args.steps, 0] > 0
+    bpt = wl.Hkv * 128 * 4
+    step_bytes = (wl.layers * (np.minimum(ns, wl.sinks + wl.window) + np.where(rec, ns, 0)) * bpt).sum()
+    step_gbs = step_bytes / (ms_total * 1e-3) / 1e9
+
+    res = {
+        "metric": METRIC,
+        "value": round(tok_s, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 KV, fp32 q/softmax/accumulate",
+        "data": "synthetic (seeded counter-based N(0,1)-like values; no dataset or trained weights)",
+        "config": {"workload": "oda_stack128k: 36 layers, 32 q / 8 kv heads, head_dim 128, history 131072 "
+                               "+1 per step, batch 1, local s=4 w=2048, %d/%d recall steps" % (recalls, args.steps),
+                   "global_batch": 1, "seq_len": int(ns[-1]), "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "decode_kernel<full> (oda_decode_full), n=%d, 36-layer rotation" % n_now,
+                     "us_per_launch": round(full_ms * 1e3, 2), "algorithmic_bytes_per_launch": int(bytes_full)},
+        "step_hbm_gbs": round(float(step_gbs), 1),
+        "wall_s_timed": round(wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        log("timing the fp64 oracle on the host (bounded sample)")
+        del stack
+        torch.cuda.empty_cache()
+        res["cpu_baseline"] = cpu_baseline(wl, recalls / args.steps)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -25,13 +25,18 @@
 //    split order, so results are deterministic.
 #include <math.h>
 
+#include <algorithm>
+
 #include "sk_internal.h"
 
 namespace sk {
 namespace {
 
 enum { kFull = 0, kLocal = 1, kList = 2 };
-constexpr int kMinTilesPerSplit = 2 * kWavesPerWG;  // one pair of tiles per wave
+constexpr int kThreads = 64 * kWavesPerWG;
+constexpr int kMinTilesPerSplit = 2 * kWavesPerWG;  // two tiles per wave
+constexpr int kMaxSplits = 256;                     // splits per (request, KV head)
+constexpr int kGridCap = 256;                       // decode workgroups per launch (one per CU)
 constexpr float kLog2e = 1.4426950408889634f;
 
 struct DecodeParams {
@@ -57,8 +62,9 @@ struct Tile {
   int phys, lo, hi;
 };
 
+template <bool HAS_SEL>
 __device__ inline bool request_active(const DecodeParams& P, int b) {
-  return P.sel == nullptr || P.sel[b] == P.sel_value;
+  return !HAS_SEL || P.sel[b] == P.sel_value;
 }
 
 template <int MODE>
@@ -115,8 +121,28 @@ __device__ inline Tile tile_at(const DecodeParams& P, int b, int n, int i) {
 
 __device__ inline bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+// Split partials cross workgroups (and XCDs). They are written and read with
+// device-scope relaxed atomic accesses, which gfx950 performs at the device coherence
+// point (sc1), so publishing them needs only the completion of the stores before the
+// ticket increment -- not an agent-scope fence, which would write back the whole L2.
+__device__ inline void publish(float* p, float v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+__device__ inline float fetch_published(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline f32x4 fetch_published4(const float* p) {
+  return f32x4{fetch_published(p), fetch_published(p + 1), fetch_published(p + 2), fetch_published(p + 3)};
+}
+// s_waitcnt vmcnt(0): all of this wave's stores have completed (gfx9 counts stores in vmcnt).
+__device__ inline void wait_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 __device__ inline f32x4 mfma(u32x4 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), b, c, 0, 0, 0);
+}
+
+// 16x16x16 bf16: lane l supplies A[l%16][4(l/16)..+3] and B[4(l/16)..+3][l%16].
+__device__ inline f32x4 mfma16(u32x2 a, bf16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, b), c, 0,
+                                                  0, 0);
 }
 
 __device__ inline float bf16_to_f32(__bf16 x) { return float(x); }
@@ -198,8 +224,26 @@ __device__ inline void mask_v(u32x4 (&vr)[4], int lo, int hi, int grp) {
   }
 }
 
-template <int MODE>
-__global__ __launch_bounds__(256) void decode_kernel(DecodeParams P) {
+// Loads the K and V tiles (4 KiB each) of one KV head of one physical block into this
+// lane's MFMA operand registers: four 16-byte loads per tile, 1 KiB per wave instruction.
+// The KV stream is read once per launch, so the loads carry the non-temporal hint.
+// Branch-free: an empty descriptor (bad block id) points at block 0, whose positions the
+// caller masks out, so the registers never have to be selected between two sources.
+__device__ inline void load_tile(const uint8_t* kpool, const uint8_t* vpool, int phys, int g, int Hkv, int lane,
+                                 u32x4 (&k)[4], u32x4 (&v)[4]) {
+  const size_t off = (size_t(phys) * Hkv + g) * kTileBytes + 16 * lane;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    k[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kpool + off + 1024 * c));
+    v[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vpool + off + 1024 * c));
+  }
+}
+
+// HAS_SEL: requests are filtered by sel[b] == sel_value (gated / per-request views).
+// Without a selector a separate instance runs, so a profile tells gated launches
+// (which exit at once on non-recall steps) apart from unconditional ones.
+template <int MODE, bool HAS_SEL>
+__global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
   constexpr int W = kWavesPerWG;
   extern __shared__ float smem[];
   const int tid = threadIdx.x;
@@ -207,27 +251,37 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams P) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int B = P.kv.batch, Hkv = P.kv.num_kv_heads, Hq = P.kv.num_q_heads, G = Hq / Hkv;
   const int maxb = P.kv.max_blocks;
+  const int acc_region = max(W * G * kHeadDim, 2 * kMaxSplits * G + 4 * kThreads);
 
-  // LDS: acc [W][G][128] | m [W][16] | l [W][16] | tiles [B] | start [B+1] | misc
-  float* s_acc = smem;
-  float* s_m = s_acc + W * G * kHeadDim;
+  // LDS: q operands [4][2][64] x 16 B | acc [W][G][128] (merge scratch later) | m [W][16] | l [W][16] |
+  //      tiles [B] | start [B+1] | misc
+  u32x4* s_q = reinterpret_cast<u32x4*>(smem);
+  float* s_acc = smem + 4 * kThreads;
+  float* s_m = s_acc + acc_region;
   float* s_l = s_m + W * 16;
   int* s_tiles = reinterpret_cast<int*>(s_l + W * 16);
   int* s_start = s_tiles + B;
-  int* s_misc = s_start + B + 1;  // [0] tile sum, [1] T, [2] active requests, [3] last flag
+  int* s_misc = s_start + B + 1;  // [0] tile sum, [1] T, [2] active requests, [3] last flag, [4] max tiles
 
   if (tid == 0) {
     s_misc[0] = 0;
     s_misc[2] = 0;
+    s_misc[4] = 0;
+  }
+  // Gated launches: every workgroup except the first leaves at once when no request is
+  // selected (the first one still handles invalid requests below).
+  if (HAS_SEL && blockIdx.x != 0 && B <= 64) {
+    const bool any = (lane < B) && P.sel[lane] == P.sel_value;
+    if (__builtin_amdgcn_readfirstlane(__ballot(any) != 0) == 0) return;
   }
   __syncthreads();
 
   // ---- plan: tiles per request (identical in every workgroup)
   {
-    int my_sum = 0, my_active = 0;
+    int my_sum = 0, my_active = 0, my_max = 0;
     for (int b = tid; b < B; b += blockDim.x) {
       int tiles = 0;
-      if (request_active(P, b)) {
+      if (request_active<HAS_SEL>(P, b)) {
         int n = P.kv.seq_lens[b];
         bool valid = n >= 1 && n <= maxb * kBlock;
         if (valid) tiles = request_tiles<MODE>(P, b, n);
@@ -243,18 +297,23 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams P) {
       s_tiles[b] = tiles;
       my_sum += tiles;
       my_active += tiles > 0;
+      my_max = max(my_max, tiles);
     }
     if (my_sum) atomicAdd(&s_misc[0], my_sum);
     if (my_active) atomicAdd(&s_misc[2], my_active);
+    if (my_max) atomicMax(&s_misc[4], my_max);
   }
   __syncthreads();
   if (tid == 0) {
+    // tiles per split: enough that the work items fit the grid, never fewer than one pair
+    // per wave, and at most kMaxSplits splits per (request, KV head)
     int total = s_misc[0];
-    int budget = kTargetItems / Hkv - s_misc[2];
+    int budget = int(gridDim.x) / Hkv - s_misc[2];
     if (budget < 1) budget = 1;
     int T = (total + budget - 1) / budget;
+    int T_cap = (s_misc[4] + kMaxSplits - 1) / kMaxSplits;
+    if (T < T_cap) T = T_cap;
     if (T < kMinTilesPerSplit) T = kMinTilesPerSplit;
-    T += T & 1;
     s_misc[1] = T;
   }
   __syncthreads();
@@ -278,8 +337,17 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams P) {
   __syncthreads();
   const int total_items = s_start[B];
 
+  // XCD-aware order: consecutive items (the splits of one (request, KV head)) go to
+  // workgroups that the dispatcher places on the same XCD (round-robin over 8 XCDs),
+  // so the merge reads partials written through the same L2.
+  const int per_xcd = int(gridDim.x) / 8;
+  const int item_first = (per_xcd > 0) ? int(blockIdx.x % 8) * per_xcd + int(blockIdx.x / 8) : int(blockIdx.x);
+
   const int ncol = lane & 15, grp = lane >> 4;
-  for (int item = blockIdx.x; item < total_items; item += gridDim.x) {
+  const uint8_t* kpool = reinterpret_cast<const uint8_t*>(P.kv.k_pool);
+  const uint8_t* vpool = reinterpret_cast<const uint8_t*>(P.kv.v_pool);
+
+  for (int item = item_first; item < total_items; item += gridDim.x) {
     // locate the request: largest b with start[b] <= item (it always has items)
     int lo_b = 0, hi_b = B - 1;
     while (lo_b < hi_b) {
@@ -293,7 +361,6 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams P) {
     const int g = local / splits, split = local % splits;
     const int n = P.kv.seq_lens[b];
     const int t_begin = split * T, t_end = min(t_begin + T, tiles_b);
-    const int npairs = (t_end - t_begin + 1) >> 1;
 
     // which tile receives the current token (-1: none attended here)
     int commit_tile = -1;
@@ -308,125 +375,134 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams P) {
       }
     }
 
-    // q of the G heads of KV head g -> MFMA B operands (hi and lo bf16 parts)
-    bf16x8 qh[4], ql[4];
+    // Tiles of this wave: wave, wave + W, ... of the split. The tile that receives the
+    // current token (the request's last tile) is always the owning wave's last tile; it
+    // is handled after the pipelined loop so that the loop body has no branches.
+    const int my_tiles = (t_end - t_begin > wave) ? (t_end - t_begin - wave + W - 1) / W : 0;
+    const bool own_commit = commit_tile >= t_begin && commit_tile < t_end && (commit_tile - t_begin) % W == wave;
+    const int loop_tiles = my_tiles - (own_commit ? 1 : 0);
+
+    // descriptors (physical block, valid range) of this wave's first 64 tiles, lane r for
+    // tile r; loaded before q so that both loads are in flight together
+    int dphys = 0, dlohi = 0;
+    auto load_desc = [&](int c0) {
+      const int ti = t_begin + wave + (c0 + lane) * W;
+      Tile tt = Tile{0, 0, 0};
+      if (c0 + lane < loop_tiles) tt = tile_at<MODE>(P, b, n, ti);
+      dphys = tt.phys;
+      dlohi = tt.lo | (tt.hi << 8);
+    };
+    load_desc(0);
+
+    // q of the G heads of KV head g -> MFMA B operands (hi and lo bf16 parts), staged in LDS:
+    // entry (c, part, lane) holds dims 8*(4c + lane/16) .. +7 of head lane%16.
     {
-      const float* qrow = P.q + (int64_t(b) * Hq + g * G + ncol) * kHeadDim;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        float x[8];
-        if (ncol < G) {
-          f32x4 a0 = *reinterpret_cast<const f32x4*>(qrow + 8 * (4 * c + grp));
-          f32x4 a1 = *reinterpret_cast<const f32x4*>(qrow + 8 * (4 * c + grp) + 4);
-          x[0] = a0.x; x[1] = a0.y; x[2] = a0.z; x[3] = a0.w;
-          x[4] = a1.x; x[5] = a1.y; x[6] = a1.z; x[7] = a1.w;
-        } else {
-#pragma unroll
-          for (int i = 0; i < 8; ++i) x[i] = 0.f;
-        }
+      const int c = tid >> 7, part = (tid >> 6) & 1, ln = tid & 63;
+      const int qcol = ln & 15, qgrp = ln >> 4;
+      u32x4 packed = {0u, 0u, 0u, 0u};
+      if (qcol < G) {
+        const float* qrow = P.q + (int64_t(b) * Hq + g * G + qcol) * kHeadDim + 8 * (4 * c + qgrp);
+        f32x4 a0 = *reinterpret_cast<const f32x4*>(qrow);
+        f32x4 a1 = *reinterpret_cast<const f32x4*>(qrow + 4);
+        float x[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+        bf16x8 o;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           float v = x[i] * P.qscale;
           __bf16 hi = __bf16(v);
-          qh[c][i] = hi;
-          ql[c][i] = __bf16(v - bf16_to_f32(hi));
+          o[i] = part ? __bf16(v - bf16_to_f32(hi)) : hi;
         }
+        packed = __builtin_bit_cast(u32x4, o);
       }
+      s_q[tid] = packed;
     }
+    __syncthreads();
 
     float m_run = -INFINITY, l_run = 0.f;
     f32x4 acc[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    const uint8_t* kpool = reinterpret_cast<const uint8_t*>(P.kv.k_pool);
-    const uint8_t* vpool = reinterpret_cast<const uint8_t*>(P.kv.v_pool);
-
-    for (int p = wave; p < npairs; p += W) {
-      const int i0 = t_begin + 2 * p, i1 = i0 + 1;
-      const bool has1 = i1 < t_end;
-      Tile T0 = tile_at<MODE>(P, b, n, i0);
-      Tile T1 = has1 ? tile_at<MODE>(P, b, n, i1) : Tile{0, 0, 0};
-      const size_t off0 = (size_t(T0.phys) * Hkv + g) * kTileBytes;
-      const size_t off1 = (size_t(T1.phys) * Hkv + g) * kTileBytes;
-      u32x4 kr0[4], vr0[4], kr1[4], vr1[4];
-      if (T0.hi > T0.lo) {
+    auto process = [&](u32x4 (&k)[4], u32x4 (&v)[4], int lohi) {
+      const int lo = lohi & 255, hi = lohi >> 8;
+      mask_v(v, lo, hi, grp);
+      // S = K q^T: lane holds positions 4*grp + jj of head ncol
+      f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          kr0[c] = *reinterpret_cast<const u32x4*>(kpool + off0 + 1024 * c + 16 * lane);
-          vr0[c] = *reinterpret_cast<const u32x4*>(vpool + off0 + 1024 * c + 16 * lane);
-        }
-      } else {
+      for (int c = 0; c < 4; ++c) s = mfma(k[c], __builtin_bit_cast(bf16x8, s_q[c * 128 + lane]), s);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) kr0[c] = vr0[c] = u32x4{0u, 0u, 0u, 0u};
+      for (int c = 0; c < 4; ++c) s = mfma(k[c], __builtin_bit_cast(bf16x8, s_q[c * 128 + 64 + lane]), s);
+      float sv[4];
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int t = 4 * grp + jj;
+        sv[jj] = (t >= lo && t < hi) ? s[jj] : -INFINITY;
       }
-      if (T1.hi > T1.lo) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          kr1[c] = *reinterpret_cast<const u32x4*>(kpool + off1 + 1024 * c + 16 * lane);
-          vr1[c] = *reinterpret_cast<const u32x4*>(vpool + off1 + 1024 * c + 16 * lane);
-        }
-      } else {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) kr1[c] = vr1[c] = u32x4{0u, 0u, 0u, 0u};
-      }
-      if (i0 == commit_tile)
-        substitute_and_commit(P, b, g, tl, lane, reinterpret_cast<uint8_t*>(P.kv.k_pool) + off0 + 16 * lane,
-                              reinterpret_cast<uint8_t*>(P.kv.v_pool) + off0, kr0, vr0);
-      if (has1 && i1 == commit_tile)
-        substitute_and_commit(P, b, g, tl, lane, reinterpret_cast<uint8_t*>(P.kv.k_pool) + off1 + 16 * lane,
-                              reinterpret_cast<uint8_t*>(P.kv.v_pool) + off1, kr1, vr1);
-      if (T0.lo > 0 || T0.hi < kBlock) mask_v(vr0, T0.lo, T0.hi, grp);
-      if (T1.lo > 0 || T1.hi < kBlock) mask_v(vr1, T1.lo, T1.hi, grp);
-
-      // S = K q^T for both tiles: lane holds tokens 4*grp + j of head ncol
-      f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        s0 = mfma(kr0[c], qh[c], s0);
-        s0 = mfma(kr0[c], ql[c], s0);
-        s1 = mfma(kr1[c], qh[c], s1);
-        s1 = mfma(kr1[c], ql[c], s1);
-      }
-      float sv[8];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        int t = 4 * grp + j;
-        sv[j] = (t >= T0.lo && t < T0.hi) ? s0[j] : -INFINITY;
-        sv[4 + j] = (t >= T1.lo && t < T1.hi) ? s1[j] : -INFINITY;
-      }
-      float mx = sv[0];
-#pragma unroll
-      for (int j = 1; j < 8; ++j) mx = fmaxf(mx, sv[j]);
+      float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
       mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       const float m_new = fmaxf(m_run, mx);
       const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-      float pv[8], psum = 0.f;
+      float pv[4];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        pv[j] = __builtin_amdgcn_exp2f(sv[j] - m_use);
-        psum += pv[j];
-      }
-      l_run = l_run * alpha + psum;
+      for (int jj = 0; jj < 4; ++jj) pv[jj] = __builtin_amdgcn_exp2f(sv[jj] - m_use);
+      l_run = l_run * alpha + ((pv[0] + pv[1]) + (pv[2] + pv[3]));
       m_run = m_new;
-      bf16x8 ph, pl;
+      bf16x4 ph, pl;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        __bf16 hi = __bf16(pv[j]);
-        ph[j] = hi;
-        pl[j] = __bf16(pv[j] - bf16_to_f32(hi));
+      for (int jj = 0; jj < 4; ++jj) {
+        __bf16 h16 = __bf16(pv[jj]);
+        ph[jj] = h16;
+        pl[jj] = __bf16(pv[jj] - bf16_to_f32(h16));
       }
+      // O^T += V^T P^T, 16 dims at a time: the lane's V operand is 4 positions of one dim
 #pragma unroll
       for (int dc = 0; dc < 8; ++dc) {
         const int c = dc >> 1;
-        u32x4 a = (dc & 1) ? u32x4{vr0[c].z, vr0[c].w, vr1[c].z, vr1[c].w}
-                           : u32x4{vr0[c].x, vr0[c].y, vr1[c].x, vr1[c].y};
+        const u32x2 a = (dc & 1) ? u32x2{v[c].z, v[c].w} : u32x2{v[c].x, v[c].y};
         acc[dc] *= alpha;
-        acc[dc] = mfma(a, ph, acc[dc]);
-        acc[dc] = mfma(a, pl, acc[dc]);
+        acc[dc] = mfma16(a, ph, acc[dc]);
+        acc[dc] = mfma16(a, pl, acc[dc]);
       }
+    };
+
+    // Pipelined loop over chunks of up to 64 tiles: lane r holds the descriptor (physical
+    // block, valid range) of chunk tile r; a ring of three tile buffers keeps two tiles in
+    // flight while the third is computed. Fetch indices past the end are clamped to the
+    // chunk's last tile (a cache hit), so the loop body has no data-dependent branches.
+    u32x4 k0[4], v0[4], k1[4], v1[4], k2[4], v2[4];
+    for (int c0 = 0; c0 < loop_tiles; c0 += 64) {
+      const int nt = min(64, loop_tiles - c0);
+      if (c0 > 0) load_desc(c0);
+      const int last = nt - 1;
+#define SK_FETCH(K, V, J) load_tile(kpool, vpool, __builtin_amdgcn_readlane(dphys, min((J), last)), g, Hkv, lane, K, V)
+#define SK_LOHI(J) __builtin_amdgcn_readlane(dlohi, (J))
+      SK_FETCH(k0, v0, 0);
+      SK_FETCH(k1, v1, 1);
+      int j = 0;
+      for (; j + 3 <= nt; j += 3) {
+        SK_FETCH(k2, v2, j + 2);
+        process(k0, v0, SK_LOHI(j));
+        SK_FETCH(k0, v0, j + 3);
+        process(k1, v1, SK_LOHI(j + 1));
+        SK_FETCH(k1, v1, j + 4);
+        process(k2, v2, SK_LOHI(j + 2));
+      }
+      if (j < nt) process(k0, v0, SK_LOHI(j));
+      if (j + 1 < nt) process(k1, v1, SK_LOHI(j + 1));
+#undef SK_FETCH
+#undef SK_LOHI
+    }
+    if (own_commit) {
+      Tile tt = tile_at<MODE>(P, b, n, commit_tile);
+      load_tile(kpool, vpool, tt.phys, g, Hkv, lane, k0, v0);
+      if (tt.hi > tt.lo) {
+        const size_t off = (size_t(tt.phys) * Hkv + g) * kTileBytes;
+        substitute_and_commit(P, b, g, tl, lane, reinterpret_cast<uint8_t*>(P.kv.k_pool) + off + 16 * lane,
+                              reinterpret_cast<uint8_t*>(P.kv.v_pool) + off, k0, v0);
+      }
+      process(k0, v0, tt.lo | (tt.hi << 8));
     }
 
     // ---- combine the waves of this workgroup
@@ -436,7 +512,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams P) {
 #pragma unroll
       for (int dc = 0; dc < 8; ++dc)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) s_acc[(wave * G + ncol) * kHeadDim + 16 * dc + 4 * grp + j] = acc[dc][j];
+        for (int jj = 0; jj < 4; ++jj) s_acc[(wave * G + ncol) * kHeadDim + 16 * dc + 4 * grp + jj] = acc[dc][jj];
       if (grp == 0) {
         s_m[wave * 16 + ncol] = m_run;
         s_l[wave * 16 + ncol] = l_run;
@@ -460,17 +536,20 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams P) {
       if (splits == 1) {
         P.out[(int64_t(b) * Hq + g * G + h) * kHeadDim + d] = (L > 0.f) ? A / L : 0.f;
       } else {
-        part[h * kHeadDim + d] = A;
+        publish(part + h * kHeadDim + d, A);
         if (d == 0) {
-          part[G * kHeadDim + h] = M;
-          part[G * (kHeadDim + 1) + h] = L;
+          publish(part + G * kHeadDim + h, M);
+          publish(part + G * (kHeadDim + 1) + h, L);
         }
       }
     }
 
-    // ---- the last split of (b, g) to finish merges all splits
+    // ---- the last split of (b, g) to finish merges all splits, in split order
     if (splits > 1) {
-      __threadfence();
+      // The partials were written with device-coherent stores; every wave waits for its
+      // stores to complete before the barrier, then one thread takes the ticket. The last
+      // arrival reads the partials with device-coherent loads. No L2 write-back is needed.
+      wait_stores();
       __syncthreads();
       if (tid == 0) {
         unsigned prev = atomicAdd(&P.tickets[b * Hkv + g], 1u);
@@ -478,23 +557,76 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams P) {
       }
       __syncthreads();
       if (s_misc[3]) {
-        __threadfence();
-        const int item0 = s_start[b] + g * splits;
+        const int S = splits;
         const size_t stride = size_t(G) * (kHeadDim + 2);
-        const float* base = P.partials + size_t(item0) * stride;
-        for (int idx = tid; idx < G * kHeadDim; idx += blockDim.x) {
-          const int h = idx >> 7, d = idx & (kHeadDim - 1);
+        const float* base = P.partials + size_t(s_start[b] + g * splits) * stride;
+        float* sm = s_acc;             // [S][G] maxima, then weights
+        float* sl = sm + S * G;        // [S][G] sums
+        float* red = sl + S * G;       // [NG][G*32] float4 partial sums
+        float* sL = s_l;               // [G] merged sums
+        const int F = G * 32;          // float4 outputs of this KV head
+        const int NG = kThreads / F;   // split groups
+        const int fi = tid % F, sg = tid / F;
+        for (int e = tid; e < S * G; e += blockDim.x) {
+          const int s = e / G, h = e % G;
+          sm[e] = fetch_published(base + s * stride + G * kHeadDim + h);
+          sl[e] = fetch_published(base + s * stride + G * (kHeadDim + 1) + h);
+        }
+        // issue this thread's first chunk of partial loads before the barrier
+        f32x4 xs[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int s = sg + u * NG;
+          xs[u] = (sg < NG && s < S) ? fetch_published4(base + s * stride + 4 * fi) : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        __syncthreads();
+        for (int h = wave; h < G; h += W) {
           float M = -INFINITY;
-          for (int s = 0; s < splits; ++s) M = fmaxf(M, base[s * stride + G * kHeadDim + h]);
+          for (int s = lane; s < S; s += 64) M = fmaxf(M, sm[s * G + h]);
+#pragma unroll
+          for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
           const float Mu = (M == -INFINITY) ? 0.f : M;
-          float L = 0.f, A = 0.f;
-          for (int s = 0; s < splits; ++s) {
-            const float* ps = base + s * stride;
-            float e = __builtin_amdgcn_exp2f(ps[G * kHeadDim + h] - Mu);
-            L += ps[G * (kHeadDim + 1) + h] * e;
-            A += ps[h * kHeadDim + d] * e;
+          float L = 0.f;
+          for (int s = lane; s < S; s += 64) {
+            const float w = __builtin_amdgcn_exp2f(sm[s * G + h] - Mu);
+            sm[s * G + h] = w;
+            L += sl[s * G + h] * w;
           }
-          P.out[(int64_t(b) * Hq + g * G + h) * kHeadDim + d] = (L > 0.f) ? A / L : 0.f;
+#pragma unroll
+          for (int off = 32; off > 0; off >>= 1) L += __shfl_xor(L, off);
+          if (lane == 0) sL[h] = L;
+        }
+        __syncthreads();
+        if (sg < NG) {
+          const int h = fi >> 5;
+          f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const int s = sg + u * NG;
+            if (s < S) a += xs[u] * sm[s * G + h];
+          }
+          for (int s0 = sg + 8 * NG; s0 < S; s0 += 8 * NG) {
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+              const int s = s0 + u * NG;
+              xs[u] = (s < S) ? fetch_published4(base + s * stride + 4 * fi) : f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+              const int s = s0 + u * NG;
+              if (s < S) a += xs[u] * sm[s * G + h];
+            }
+          }
+          *reinterpret_cast<f32x4*>(red + 4 * (sg * F + fi)) = a;
+        }
+        __syncthreads();
+        for (int f = tid; f < F; f += blockDim.x) {
+          f32x4 a = {0.f, 0.f, 0.f, 0.f};
+          for (int q = 0; q < NG; ++q) a += *reinterpret_cast<const f32x4*>(red + 4 * (q * F + f));
+          const float L = sL[f >> 5];
+          const float inv = (L > 0.f) ? 1.f / L : 0.f;
+          a *= inv;
+          *reinterpret_cast<f32x4*>(P.out + (int64_t(b) * Hq + g * G) * kHeadDim + 4 * f) = a;
         }
         if (tid == 0) P.tickets[b * Hkv + g] = 0u;
       }
@@ -594,17 +726,22 @@ int launch_decode(const float* q, sk_paged_kv kv, const void* k_new, const void*
   P.window = window;
   P.qscale = scale * kLog2e;
   const int G = kv.num_q_heads / kv.num_kv_heads;
-  // upper bound of the work items, so that tiny launches do not dispatch idle workgroups
+  // Grid: one workgroup per CU at most, fewer for small launches (an upper bound of the
+  // work items from max_blocks), rounded to a multiple of the 8 XCDs.
   int64_t tiles_max = (MODE == kLocal)
                           ? int64_t((sinks + kBlock - 1) / kBlock) + (window + kBlock - 1) / kBlock + 1
                           : int64_t(kv.max_blocks);
   if (tiles_max > kv.max_blocks) tiles_max = kv.max_blocks;
   int64_t bound = int64_t(kv.batch) * kv.num_kv_heads * ((tiles_max + kMinTilesPerSplit - 1) / kMinTilesPerSplit);
-  int grid = int(bound < kTargetItems ? bound : kTargetItems);
-  if (grid < 1) grid = 1;
-  size_t lds = size_t(kWavesPerWG) * G * kHeadDim * 4 + size_t(kWavesPerWG) * 16 * 4 * 2 +
-               size_t(2 * kv.batch + 1 + 4) * 4;
-  hipLaunchKernelGGL(decode_kernel<MODE>, dim3(grid), dim3(64 * kWavesPerWG), lds, stream, P);
+  int64_t grid = bound < kGridCap ? bound : kGridCap;
+  grid = (grid + 7) / 8 * 8;
+  const int acc_region = std::max(kWavesPerWG * G * kHeadDim, 2 * kMaxSplits * G + 4 * kThreads);
+  size_t lds = size_t(kThreads) * 16 + size_t(acc_region) * 4 + size_t(kWavesPerWG) * 16 * 4 * 2 +
+               size_t(2 * kv.batch + 1 + 8) * 4;
+  if (sel)
+    hipLaunchKernelGGL((decode_kernel<MODE, true>), dim3(unsigned(grid)), dim3(kThreads), lds, stream, P);
+  else
+    hipLaunchKernelGGL((decode_kernel<MODE, false>), dim3(unsigned(grid)), dim3(kThreads), lds, stream, P);
   return launch_status(hipGetLastError());
 }
 

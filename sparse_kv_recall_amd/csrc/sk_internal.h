@@ -19,15 +19,17 @@ constexpr size_t kWsHeaderBytes = 256;
 constexpr int kMaxTickets = kMaxBatch * 16;        // (request, kv-head) pairs
 constexpr size_t kTicketBytes = size_t(kMaxTickets) * 4;
 constexpr size_t kPartialsOffset = kWsHeaderBytes + kTicketBytes;
-// Decode launches use at most this many work items (split partials) plus one per
-// (request, kv-head) for rounding; every item stores G * (128 + 2) floats.
+// Decode launches use at most this many workgroups, hence work items (split partials),
+// plus one per (request, kv-head) for rounding; every item stores G * (128 + 2) floats.
 constexpr int kTargetItems = 1024;
-constexpr int kWavesPerWG = 4;
+constexpr int kWavesPerWG = 8;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 inline int launch_status(hipError_t e) { return e == hipSuccess ? SK_OK : SK_E_LAUNCH_BASE - int(e); }
 

@@ -1,0 +1,123 @@
+"""Decode-step drivers: the order in which one step calls the C ABI.
+
+ODA step (On-Demand Attention summary page, "Approach"; Figure 1 caption):
+  1. every layer runs the Local view, committing its candidate KV at n-1;
+  2. the recall score gives the gate on the device (recall-head GEMV, or given scores);
+  3. every layer runs the Full view gated by that flag: its workgroups exit at once
+     when the gate is 0, otherwise it commits the Full candidate (overwriting the
+     Local one) and overwrites the layer's output with the Full result.
+The step never reads the gate on the host, so it can be captured once as a HIP
+graph and replayed ("Developer perspective": one GPU execution flow).
+
+Ragged-batch step: a per-request view is chosen on the device from the scores
+(Full when score > theta, else the request's fallback), then the three views are
+launched with selectors, each request being served by exactly one of them.
+
+This module only sequences library calls; it computes nothing itself.
+"""
+
+import math
+
+import torch
+
+from . import ops
+
+
+class ODAStack:
+    """Paged caches of an L-layer attention stack that share block tables and lengths."""
+
+    def __init__(self, layers, batch, Hq, Hkv, num_phys_blocks, max_blocks, block_tables, seq_lens,
+                 sinks=4, window=2048, scale=None, device="cuda", separate_outputs=False):
+        self.layers, self.batch, self.Hq, self.Hkv = layers, batch, Hq, Hkv
+        self.sinks, self.window = sinks, window
+        self.scale = 1.0 / math.sqrt(ops.HEAD_DIM) if scale is None else scale
+        self.seq_lens = seq_lens
+        self.block_tables = block_tables
+        self.caches = [ops.PagedKVCache(num_phys_blocks, batch, Hq, Hkv, max_blocks, device=device,
+                                        block_tables=block_tables, seq_lens=seq_lens) for _ in range(layers)]
+        self.ws = ops.workspace(batch, Hq, device)
+        shape = (layers, batch, Hq, ops.HEAD_DIM)
+        self.out = torch.zeros(shape, dtype=torch.float32, device=device)
+        self.out_full = torch.zeros(shape, dtype=torch.float32, device=device) if separate_outputs else self.out
+        self.gate = torch.zeros(batch, dtype=torch.int32, device=device)
+        self.qscore = torch.zeros(batch, dtype=torch.float32, device=device)
+
+    def local_pass(self, q, k, v):
+        """q: [L][B][Hq][128] fp32, k, v: [L][B][Hkv][128] bf16 (Local candidates)."""
+        for l in range(self.layers):
+            ops.oda_decode_local(q[l], self.caches[l], k[l], v[l], self.sinks, self.window, self.scale,
+                                 out=self.out[l], ws=self.ws)
+
+    def gate_from_scores(self, scores, theta=0.0):
+        ops.oda_gate_scores(scores, theta, out=self.gate)
+
+    def gate_from_recall_head(self, x, W1, b1, w2, b2, theta=0.0):
+        ops.oda_recall_score(x, W1, b1, w2, b2, theta, q_out=self.qscore, gate_out=self.gate, ws=self.ws)
+
+    def full_pass(self, q, k, v, gated=True):
+        sel = self.gate if gated else None
+        for l in range(self.layers):
+            ops.oda_decode_full(q[l], self.caches[l], k[l], v[l], self.scale, sel=sel, sel_value=1,
+                                out=self.out_full[l], ws=self.ws)
+
+
+class RaggedBatch:
+    """One attention layer over a ragged batch with per-request views."""
+
+    def __init__(self, cache, fallback, keep_mask, sinks=4, window=2048, scale=None, device="cuda"):
+        self.cache = cache
+        self.fallback = fallback
+        self.keep_mask = keep_mask
+        self.sinks, self.window = sinks, window
+        self.scale = 1.0 / math.sqrt(ops.HEAD_DIM) if scale is None else scale
+        B, mb = cache.batch, cache.max_blocks
+        self.ws = ops.workspace(B, cache.num_q_heads, device)
+        self.mode = torch.zeros(B, dtype=torch.int32, device=device)
+        self.out = torch.zeros((B, cache.num_q_heads, ops.HEAD_DIM), dtype=torch.float32, device=device)
+        self.gathered = torch.zeros((B, mb), dtype=torch.int32, device=device)
+        self.gathered_cnt = torch.zeros((B, mb), dtype=torch.int32, device=device)
+        self.num_kept = torch.zeros(B, dtype=torch.int32, device=device)
+
+    def step(self, q, k, v, scores, theta=0.0):
+        """q: [B][Hq][128] fp32; k, v: [B][Hkv][128] bf16; scores: [B] fp32."""
+        ops.oda_gate_scores(scores, theta, fallback=self.fallback, out=self.mode)
+        ops.oda_decode_full(q, self.cache, k, v, self.scale, sel=self.mode, sel_value=ops.MODE_FULL,
+                            out=self.out, ws=self.ws)
+        ops.oda_decode_local(q, self.cache, k, v, self.sinks, self.window, self.scale, sel=self.mode,
+                             sel_value=ops.MODE_LOCAL, out=self.out, ws=self.ws)
+        ops.da_decode_blocks(q, self.cache, self.keep_mask, k, v, self.scale, sel=self.mode,
+                             sel_value=ops.MODE_BLOCKS, out=self.out, gathered=self.gathered,
+                             gathered_cnt=self.gathered_cnt, num_kept=self.num_kept, ws=self.ws)
+
+
+class DAStep:
+    """One attention layer driven by Declarative-Attention declarations."""
+
+    def __init__(self, cache, local_tokens=1024, scale=None, device="cuda"):
+        self.cache = cache
+        self.local_tokens = local_tokens
+        self.scale = 1.0 / math.sqrt(ops.HEAD_DIM) if scale is None else scale
+        B, mb = cache.batch, cache.max_blocks
+        self.ws = ops.workspace(B, cache.num_q_heads, device)
+        self.mask = torch.zeros((B, (mb + 31) // 32), dtype=torch.int32, device=device)
+        self.out = torch.zeros((B, cache.num_q_heads, ops.HEAD_DIM), dtype=torch.float32, device=device)
+        self.gathered = torch.zeros((B, mb), dtype=torch.int32, device=device)
+        self.gathered_cnt = torch.zeros((B, mb), dtype=torch.int32, device=device)
+        self.num_kept = torch.zeros(B, dtype=torch.int32, device=device)
+
+    def step(self, q, k, v, decl):
+        ops.da_keep_mask(decl, self.cache, self.local_tokens, mask=self.mask)
+        ops.da_decode_blocks(q, self.cache, self.mask, k, v, self.scale, out=self.out, gathered=self.gathered,
+                             gathered_cnt=self.gathered_cnt, num_kept=self.num_kept, ws=self.ws)
+
+
+def capture_graph(fn):
+    """Capture the launches made by fn() into a HIP graph (replayed with .replay())."""
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            fn()
+    torch.cuda.current_stream().wait_stream(s)
+    return g

@@ -56,41 +56,44 @@ struct FeedParams {
   int32_t* decl_out;  // [B][4]
 };
 
+// Element indices stay below 2^31 for every workload here (the host checks), so the
+// decomposition uses 32-bit arithmetic.
 __global__ __launch_bounds__(256) void feed_kernel(FeedParams F) {
   __shared__ int s_last;
   const int t = F.state[0] % F.num_steps;
-  const int64_t nq = int64_t(F.L) * F.P * F.B * F.Hq * 128;
-  const int64_t nkv = int64_t(F.L) * F.P * F.B * F.Hkv * 128;
-  const int64_t nx = F.x_out ? int64_t(F.B) * F.x_dim : 0;
-  const int64_t total = nq + nkv + nx + F.B;
-  for (int64_t i = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; i < total; i += int64_t(gridDim.x) * blockDim.x) {
+  const int rq = F.Hq * 128, rkv = F.Hkv * 128;
+  const int nq = F.L * F.P * F.B * rq;
+  const int nkv = F.L * F.P * F.B * rkv;
+  const int nx = F.x_out ? F.B * F.x_dim : 0;
+  const int total = nq + nkv + nx + F.B;
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < total; i += gridDim.x * blockDim.x) {
     if (i < nq) {
-      int64_t e = i % (int64_t(F.Hq) * 128);
-      int64_t r = i / (int64_t(F.Hq) * 128);
-      int b = int(r % F.B);
+      const int e = i % rq;
+      int r = i / rq;
+      const int b = r % F.B;
       r /= F.B;
-      int p = int(r % F.P);
-      int l = int(r / F.P);
-      int pe = (l == 0) ? 0 : p;
-      uint64_t gi = uint64_t((((int64_t(t) * F.L + l) * F.P + pe) * F.B + b) * F.Hq * 128 + e);
+      const int p = r % F.P;
+      const int l = r / F.P;
+      const int pe = (l == 0) ? 0 : p;
+      const uint64_t gi = uint64_t(((int64_t(t) * F.L + l) * F.P + pe) * F.B + b) * rq + e;
       F.q_out[i] = normal_at(F.key_q, gi, F.scale);
     } else if (i < nq + nkv) {
-      int64_t j = i - nq;
-      int64_t e = j % (int64_t(F.Hkv) * 128);
-      int64_t r = j / (int64_t(F.Hkv) * 128);
-      int b = int(r % F.B);
+      const int j = i - nq;
+      const int e = j % rkv;
+      int r = j / rkv;
+      const int b = r % F.B;
       r /= F.B;
-      int p = int(r % F.P);
-      int l = int(r / F.P);
-      int pe = (l == 0) ? 0 : p;
-      uint64_t gi = uint64_t((((int64_t(t) * F.L + l) * F.P + pe) * F.B + b) * F.Hkv * 128 + e);
+      const int p = r % F.P;
+      const int l = r / F.P;
+      const int pe = (l == 0) ? 0 : p;
+      const uint64_t gi = uint64_t(((int64_t(t) * F.L + l) * F.P + pe) * F.B + b) * rkv + e;
       F.k_out[j] = bf16_rne(normal_at(F.key_k, gi, F.scale));
       F.v_out[j] = bf16_rne(normal_at(F.key_v, gi, F.scale));
     } else if (i < nq + nkv + nx) {
-      int64_t j = i - nq - nkv;
+      const int j = i - nq - nkv;
       F.x_out[j] = normal_at(F.key_x, uint64_t(int64_t(t) * F.B * F.x_dim + j), F.scale);
     } else {
-      int b = int(i - nq - nkv - nx);
+      const int b = i - nq - nkv - nx;
       F.seq_lens[b] = F.H0[b] + t + 1;
       if (F.score_out)
         F.score_out[b] = F.sched ? F.sched[int64_t(t) * F.B + b]
@@ -99,7 +102,8 @@ __global__ __launch_bounds__(256) void feed_kernel(FeedParams F) {
         for (int k = 0; k < 4; ++k) F.decl_out[4 * b + k] = F.decl_table[(int64_t(t) * F.B + b) * 4 + k];
     }
   }
-  __threadfence();
+  // every block has read state[0] above; the last block to arrive advances the step
+  // (no fence: the outputs only need to be visible after the kernel ends)
   __syncthreads();
   if (threadIdx.x == 0) s_last = (atomicAdd(&F.state[1], 1) == int(gridDim.x) - 1);
   __syncthreads();
@@ -140,9 +144,13 @@ int synth_feed(int32_t* state, int32_t* seq_lens, const int32_t* H0, int B, int 
                int num_steps, uint64_t key_q, uint64_t key_k, uint64_t key_v, uint64_t key_x, uint64_t key_score,
                float scale, float* q_out, uint16_t* k_out, uint16_t* v_out, int x_dim, float* x_out,
                const float* sched, float* score_out, const int32_t* decl_table, int32_t* decl_out, hipStream_t s) {
+  const int64_t total = int64_t(L) * P * B * (Hq + Hkv) * 128 + (x_out ? int64_t(B) * x_dim : 0) + B;
+  if (total >= (int64_t(1) << 31) || B < 1 || num_steps < 1) return -4;
   FeedParams F{state, seq_lens, H0, B, L, P, Hq, Hkv, num_steps, key_q, key_k, key_v, key_x, key_score, scale,
                q_out, k_out, v_out, x_dim, x_out, sched, score_out, decl_table, decl_out};
-  hipLaunchKernelGGL(feed_kernel, dim3(256), dim3(256), 0, s, F);
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 256) blocks = 256;
+  hipLaunchKernelGGL(feed_kernel, dim3(unsigned(blocks)), dim3(256), 0, s, F);
   return status(hipGetLastError());
 }
 
