@@ -1,0 +1,67 @@
+"""GPU parity of whole decode steps on the five seeded workloads, at their full sizes,
+in the launch configuration the benchmark times (a captured HIP graph per step).
+
+Outputs are checked on sampled layers / requests / steps that the fp64 oracle can
+compute one by one; decisions, gathered block lists and commits are checked on every
+step. See tests/harness.py for what each run compares.
+"""
+
+import numpy as np
+import pytest
+
+from synth import workloads
+from tests.helpers import requires_gpu
+
+pytestmark = [pytest.mark.gpu, requires_gpu]
+
+
+def test_oda_small_every_step():
+    from tests.harness import OdaStackRun
+    wl = workloads.oda_small()
+    rep = OdaStackRun(wl, check_layers=[0]).run(check_feed_steps=(0, 5))
+    assert rep.decisions == 64 and rep.checked_outputs == 64 + rep.recalls
+    print("oda_small: recalls %d/64, max-abs %.2e, row-rel %.2e" % (rep.recalls, rep.max_abs, rep.max_row_rel))
+
+
+def test_oda_stack16k_recall_head():
+    from tests.harness import OdaStackRun
+    wl = workloads.oda_stack16k()
+    rep = OdaStackRun(wl, check_layers=[0, 1, 27]).run()
+    assert rep.decisions == 256
+    assert 0 < rep.recalls < 256
+    print("oda_stack16k: recalls %d/256 (%d in the 1e-4 band), max-abs %.2e, row-rel %.2e"
+          % (rep.recalls, rep.decisions_in_band, rep.max_abs, rep.max_row_rel))
+
+
+@pytest.mark.slow
+def test_oda_stack128k_metric_workload():
+    from tests.harness import OdaStackRun
+    wl = workloads.oda_stack128k()
+    recall_steps = np.flatnonzero(wl.sched_scores[:, 0] > 0)
+    sample = set(int(x) for x in np.random.default_rng(3).choice(recall_steps, size=3, replace=False))
+    sample.add(int(recall_steps[-1]))
+    rep = OdaStackRun(wl, check_layers=[0, 35]).run(full_check_steps=sample)
+    assert rep.decisions == 1024 and rep.recalls == 128
+    print("oda_stack128k: local checked every step on layers 0, 35; full checked at steps %s; "
+          "max-abs %.2e, row-rel %.2e" % (sorted(sample), rep.max_abs, rep.max_row_rel))
+
+
+def test_da_32k_every_step():
+    from tests.harness import DaRun
+    wl = workloads.da_32k()
+    rep = DaRun(wl).run()
+    assert rep.checked_outputs == 512
+    print("da_32k: max-abs %.2e, row-rel %.2e" % (rep.max_abs, rep.max_row_rel))
+
+
+@pytest.mark.slow
+def test_ragged32_sampled_requests():
+    from tests.harness import RaggedRun
+    wl = workloads.ragged32()
+    order = np.argsort(wl.H0)
+    check = sorted(set([int(order[0]), int(order[-1]), int(order[len(order) // 2])] +
+                       [int(x) for x in np.random.default_rng(4).choice(wl.batch, size=3, replace=False)]))
+    rep = RaggedRun(wl, check_requests=check).run(check_steps=set(range(0, wl.steps, 8)) | {wl.steps - 1})
+    assert rep.decisions == wl.batch * wl.steps
+    print("ragged32: requests %s, full views %d of %d, max-abs %.2e, row-rel %.2e"
+          % (check, rep.recalls, rep.decisions, rep.max_abs, rep.max_row_rel))
