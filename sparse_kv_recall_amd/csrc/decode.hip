@@ -34,7 +34,7 @@ namespace {
 
 enum { kFull = 0, kLocal = 1, kList = 2 };
 constexpr int kThreads = 64 * kWavesPerWG;
-constexpr int kMinTilesPerSplit = 2 * kWavesPerWG;  // two tiles per wave
+constexpr int kMinTilesPerSplit = 8;                   // small launches: many short splits
 constexpr int kMaxSplits = 256;                     // splits per (request, KV head)
 constexpr int kGridCap = 256;                       // decode workgroups per launch (one per CU)
 constexpr float kLog2e = 1.4426950408889634f;
@@ -173,30 +173,25 @@ __device__ inline void commit_token_lanes(const DecodeParams& P, int b, int g, i
   }
 }
 
-// Replace token tl of a loaded tile (this lane's K / V operand registers) by the
-// current token's key / value, and write those values into the pool tile.
-__device__ inline void substitute_and_commit(const DecodeParams& P, int b, int g, int tl, int lane,
-                                             uint8_t* ktile_lane, uint8_t* vtile, u32x4 (&kr)[4],
-                                             u32x4 (&vr)[4]) {
-  const int Hkv = P.kv.num_kv_heads;
+// Replace position tl of a loaded tile (this lane's K / V operand registers) by the
+// current token, staged in LDS as 64 words of K then 64 words of V (bf16 pairs).
+__device__ inline void substitute_token(const uint32_t* s_new, int tl, int lane, u32x4 (&kr)[4], u32x4 (&vr)[4]) {
   const int m = lane & 15, grp = lane >> 4;
-  const uint16_t* kn = P.k_new + (int64_t(b) * Hkv + g) * kHeadDim;
-  const uint16_t* vn = P.v_new + (int64_t(b) * Hkv + g) * kHeadDim;
   if (m == tl) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      kr[c] = *reinterpret_cast<const u32x4*>(kn + 8 * (4 * c + grp));
-      *reinterpret_cast<u32x4*>(ktile_lane + 1024 * c) = kr[c];
+      const int w = 4 * (4 * c + grp);  // dims 8*(4c+grp) .. +7
+      kr[c] = u32x4{s_new[w], s_new[w + 1], s_new[w + 2], s_new[w + 3]};
     }
   }
   if (grp == (tl >> 2)) {
     const int j = tl & 3;
+    const uint16_t* vn = reinterpret_cast<const uint16_t*>(s_new + 64);
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        uint32_t val = vn[32 * c + 16 * h + m];
-        *reinterpret_cast<uint16_t*>(vtile + 1024 * c + 256 * grp + 16 * m + 8 * h + 2 * j) = uint16_t(val);
+        const uint32_t val = vn[32 * c + 16 * h + m];
         uint32_t w = (j >> 1) ? (h ? vr[c].w : vr[c].y) : (h ? vr[c].z : vr[c].x);
         w = (j & 1) ? ((w & 0x0000FFFFu) | (val << 16)) : ((w & 0xFFFF0000u) | val);
         if (j >> 1) {
@@ -206,6 +201,22 @@ __device__ inline void substitute_and_commit(const DecodeParams& P, int b, int g
         }
       }
     }
+  }
+}
+
+// Store the current token (LDS copy) into position tl of the (phys, g) tiles.
+__device__ inline void commit_from_lds(const DecodeParams& P, const uint32_t* s_new, int phys, int g, int tl,
+                                       int lane) {
+  const size_t tile = (size_t(phys) * P.kv.num_kv_heads + g) * kTileBytes;
+  uint8_t* kt = reinterpret_cast<uint8_t*>(P.kv.k_pool) + tile;
+  uint8_t* vt = reinterpret_cast<uint8_t*>(P.kv.v_pool) + tile;
+  if (lane < 16)  // K: 16 chunks of 8 dims
+    *reinterpret_cast<u32x4*>(kt + lane * 256 + tl * 16) =
+        u32x4{s_new[4 * lane], s_new[4 * lane + 1], s_new[4 * lane + 2], s_new[4 * lane + 3]};
+  const uint16_t* vn = reinterpret_cast<const uint16_t*>(s_new + 64);
+  for (int d = lane; d < kHeadDim; d += 64) {
+    const uint32_t off = (d >> 5) * 1024 + (tl >> 2) * 256 + (d & 15) * 16 + ((d >> 4) & 1) * 8 + (tl & 3) * 2;
+    *reinterpret_cast<uint16_t*>(vt + off) = vn[d];
   }
 }
 
@@ -253,10 +264,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
   const int maxb = P.kv.max_blocks;
   const int acc_region = max(W * G * kHeadDim, 2 * kMaxSplits * G + 4 * kThreads);
 
-  // LDS: q operands [4][2][64] x 16 B | acc [W][G][128] (merge scratch later) | m [W][16] | l [W][16] |
-  //      tiles [B] | start [B+1] | misc
+  // LDS: q operands [4][2][64] x 16 B | current token K,V [128] words | acc [W][G][128] (merge scratch
+  //      later) | m [W][16] | l [W][16] | tiles [B] | start [B+1] | misc
   u32x4* s_q = reinterpret_cast<u32x4*>(smem);
-  float* s_acc = smem + 4 * kThreads;
+  uint32_t* s_new = reinterpret_cast<uint32_t*>(smem + 4 * kThreads);  // current token: K [64] | V [64] words
+  float* s_acc = smem + 4 * kThreads + 128;
   float* s_m = s_acc + acc_region;
   float* s_l = s_m + W * 16;
   int* s_tiles = reinterpret_cast<int*>(s_l + W * 16);
@@ -268,9 +280,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
     s_misc[2] = 0;
     s_misc[4] = 0;
   }
-  // Gated launches: every workgroup except the first leaves at once when no request is
-  // selected (the first one still handles invalid requests below).
-  if (HAS_SEL && blockIdx.x != 0 && B <= 64) {
+  // Gated launches: when no request is selected there is nothing to do (not even the
+  // invalid-request handling, which only concerns selected requests), so every
+  // workgroup leaves before touching the plan.
+  if (HAS_SEL && B <= 64) {
     const bool any = (lane < B) && P.sel[lane] == P.sel_value;
     if (__builtin_amdgcn_readfirstlane(__ballot(any) != 0) == 0) return;
   }
@@ -376,11 +389,17 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
     }
 
     // Tiles of this wave: wave, wave + W, ... of the split. The tile that receives the
-    // current token (the request's last tile) is always the owning wave's last tile; it
-    // is handled after the pipelined loop so that the loop body has no branches.
+    // current token (the request's last tile) is the owning wave's last tile; its key and
+    // value come from LDS, staged below together with q, so the pipeline never waits on
+    // them.
     const int my_tiles = (t_end - t_begin > wave) ? (t_end - t_begin - wave + W - 1) / W : 0;
-    const bool own_commit = commit_tile >= t_begin && commit_tile < t_end && (commit_tile - t_begin) % W == wave;
+    const bool split_commits = commit_tile >= t_begin && commit_tile < t_end;
+    const bool own_commit = split_commits && (commit_tile - t_begin) % W == wave;
     const int loop_tiles = my_tiles - (own_commit ? 1 : 0);
+    if (split_commits && tid < 128) {
+      const uint16_t* src = (tid < 64 ? P.k_new : P.v_new) + (int64_t(b) * Hkv + g) * kHeadDim;
+      s_new[tid] = reinterpret_cast<const uint32_t*>(src)[tid & 63];
+    }
 
     // descriptors (physical block, valid range) of this wave's first 64 tiles, lane r for
     // tile r; loaded before q so that both loads are in flight together
@@ -468,10 +487,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
     };
 
     // Pipelined loop over chunks of up to 64 tiles: lane r holds the descriptor (physical
-    // block, valid range) of chunk tile r; a ring of three tile buffers keeps two tiles in
-    // flight while the third is computed. Fetch indices past the end are clamped to the
+    // block, valid range) of chunk tile r; two tile buffers alternate, so the next tile is
+    // in flight while this one is computed (a deeper ring measured slower: more loads in
+    // flight per wave only added queueing). A fetch index past the end is clamped to the
     // chunk's last tile (a cache hit), so the loop body has no data-dependent branches.
-    u32x4 k0[4], v0[4], k1[4], v1[4], k2[4], v2[4];
+    u32x4 k0[4], v0[4], k1[4], v1[4];
     for (int c0 = 0; c0 < loop_tiles; c0 += 64) {
       const int nt = min(64, loop_tiles - c0);
       if (c0 > 0) load_desc(c0);
@@ -479,30 +499,25 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
 #define SK_FETCH(K, V, J) load_tile(kpool, vpool, __builtin_amdgcn_readlane(dphys, min((J), last)), g, Hkv, lane, K, V)
 #define SK_LOHI(J) __builtin_amdgcn_readlane(dlohi, (J))
       SK_FETCH(k0, v0, 0);
-      SK_FETCH(k1, v1, 1);
       int j = 0;
-      for (; j + 3 <= nt; j += 3) {
-        SK_FETCH(k2, v2, j + 2);
+      for (; j + 2 <= nt; j += 2) {
+        SK_FETCH(k1, v1, j + 1);
         process(k0, v0, SK_LOHI(j));
-        SK_FETCH(k0, v0, j + 3);
+        SK_FETCH(k0, v0, j + 2);
         process(k1, v1, SK_LOHI(j + 1));
-        SK_FETCH(k1, v1, j + 4);
-        process(k2, v2, SK_LOHI(j + 2));
       }
       if (j < nt) process(k0, v0, SK_LOHI(j));
-      if (j + 1 < nt) process(k1, v1, SK_LOHI(j + 1));
 #undef SK_FETCH
 #undef SK_LOHI
     }
     if (own_commit) {
+      // the request's last tile: attend with the current token substituted from LDS, then
+      // write the token into its slot of the pool
       Tile tt = tile_at<MODE>(P, b, n, commit_tile);
       load_tile(kpool, vpool, tt.phys, g, Hkv, lane, k0, v0);
-      if (tt.hi > tt.lo) {
-        const size_t off = (size_t(tt.phys) * Hkv + g) * kTileBytes;
-        substitute_and_commit(P, b, g, tl, lane, reinterpret_cast<uint8_t*>(P.kv.k_pool) + off + 16 * lane,
-                              reinterpret_cast<uint8_t*>(P.kv.v_pool) + off, k0, v0);
-      }
+      substitute_token(s_new, tl, lane, k0, v0);
       process(k0, v0, tt.lo | (tt.hi << 8));
+      if (tt.hi > tt.lo) commit_from_lds(P, s_new, tt.phys, g, tl, lane);
     }
 
     // ---- combine the waves of this workgroup
@@ -736,7 +751,7 @@ int launch_decode(const float* q, sk_paged_kv kv, const void* k_new, const void*
   int64_t grid = bound < kGridCap ? bound : kGridCap;
   grid = (grid + 7) / 8 * 8;
   const int acc_region = std::max(kWavesPerWG * G * kHeadDim, 2 * kMaxSplits * G + 4 * kThreads);
-  size_t lds = size_t(kThreads) * 16 + size_t(acc_region) * 4 + size_t(kWavesPerWG) * 16 * 4 * 2 +
+  size_t lds = size_t(kThreads) * 16 + 128 * 4 + size_t(acc_region) * 4 + size_t(kWavesPerWG) * 16 * 4 * 2 +
                size_t(2 * kv.batch + 1 + 8) * 4;
   if (sel)
     hipLaunchKernelGGL((decode_kernel<MODE, true>), dim3(unsigned(grid)), dim3(kThreads), lds, stream, P);
