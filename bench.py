@@ -86,6 +86,41 @@ def roofline_full(stack, feeder, reps):
     return e0.elapsed_time(e1) / (reps * stack.layers)
 
 
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("sparse_kv_recall_amd/csrc/decode.hip", "sparse_kv_recall_amd/csrc/sk_internal.h"):
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def profiled_traffic(bytes_now):
+    """HBM bytes per Full-view launch from the committed rocprofv3 counter summary
+    (FETCH_SIZE and WRITE_SIZE, each scaled by its copy-kernel calibration), rescaled
+    from the profiled n to this launch's algorithmic bytes. None when the summary is
+    missing or was taken on a different kernel source."""
+    path = os.path.join(ROOT, "profiles", "decode_128k_hbm_counters.md")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and not line.startswith(("#", "|", "`")):
+                k, _, v = line.partition(":")
+                vals[k.strip()] = v.strip()
+    try:
+        if vals["source_hash"] != kernel_source_hash():
+            return None
+        measured = (float(vals["full_fetch_kib"]) * float(vals["fetch_scale"]) +
+                    float(vals["full_write_kib"]) * float(vals["write_scale"])) * 1024.0
+        n_prof = int(vals["full_n"])
+    except (KeyError, ValueError):
+        return None
+    alg_prof = n_prof * 8 * 128 * 4 + 2 * 32 * 128 * 4 + 2 * 8 * 128 * 2
+    return measured * bytes_now / alg_prof
+
+
 def copy_calibration(device):
     """A plain copy of known size (512 MiB) for scaling the HBM counters."""
     import torch
@@ -204,6 +239,8 @@ def main():
     bytes_full = n_now * wl.Hkv * 128 * 2 * 2 + 2 * wl.Hq * 128 * 4 + 2 * wl.Hkv * 128 * 2
     achieved = bytes_full / (full_ms * 1e-3) / 1e9
     log("Full-view kernel at n=%d: %.1f us per launch, %.0f GB/s" % (n_now, full_ms * 1e3, achieved))
+    traffic = profiled_traffic(bytes_full)
+    traffic = None if traffic is None else int(round(traffic))
     copy_calibration(device)
 
     # step bytes (algorithmic): Local reads min(n, 2052) positions per layer, Full n on recall steps
@@ -230,9 +267,11 @@ def main():
                                "+1 per step, batch 1, local s=4 w=2048, %d/%d recall steps" % (recalls, args.steps),
                    "global_batch": 1, "seq_len": int(ns[-1]), "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": "decode_kernel<full> (oda_decode_full), n=%d, 36-layer rotation" % n_now,
-                     "us_per_launch": round(full_ms * 1e3, 2), "algorithmic_bytes_per_launch": int(bytes_full)},
+                     "us_per_launch": round(full_ms * 1e3, 2), "algorithmic_bytes_per_launch": int(bytes_full),
+                     "traffic_source": "profiles/decode_128k_hbm_counters.md (rocprofv3 FETCH_SIZE x2.0 + "
+                                       "WRITE_SIZE x1.0, rescaled to this n); null if the kernel changed"},
         "step_hbm_gbs": round(float(step_gbs), 1),
         "wall_s_timed": round(wall, 3),
     }
