@@ -86,6 +86,57 @@ def roofline_full(stack, feeder, reps):
     return e0.elapsed_time(e1) / (reps * stack.layers)
 
 
+def roofline_blocks(stack, feeder, reps, seed=11):
+    """Block-list (Declarative-Attention) decode over the same 36 pools at the current n,
+    through a seeded permutation of the block table, keeping (a) every block and (b) a
+    seeded 12.5 % of the blocks plus the last one. Times the whole da_decode_blocks call
+    (gather + attention) with HIP events; returns achieved GB/s of algorithmic bytes."""
+    import numpy as np
+    import torch
+    from sparse_kv_recall_amd import ops
+    c0 = stack.caches[0]
+    n = int(stack.seq_lens[0].item())
+    nb = (n + 15) // 16
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([3, 30, seed])))
+    perm = np.full((1, c0.max_blocks), -1, np.int32)
+    perm[0, :nb] = g.permutation(c0.num_phys_blocks)[:nb]
+    bt = torch.as_tensor(perm, device="cuda")
+    views = [ops.PagedKVCache(c.num_phys_blocks, 1, c.num_q_heads, c.num_kv_heads, c.max_blocks,
+                              block_tables=bt, seq_lens=stack.seq_lens, k_pool=c.k_pool, v_pool=c.v_pool)
+             for c in stack.caches]
+    words = (c0.max_blocks + 31) // 32
+    out = {}
+    for name, frac in (("all_blocks", 1.0), ("keep_12.5pct", 0.125)):
+        kept = np.arange(nb) if frac >= 1.0 else np.union1d(
+            g.choice(nb, size=int(round(frac * nb)), replace=False), [nb - 1])
+        mask = np.zeros(words, np.uint32)
+        for b in kept:
+            mask[b // 32] |= np.uint32(1 << (int(b) % 32))
+        mt = torch.as_tensor(mask.view(np.int32)[None], device="cuda")
+        gat = torch.zeros((1, c0.max_blocks), dtype=torch.int32, device="cuda")
+        cnt = torch.zeros_like(gat)
+        num = torch.zeros(1, dtype=torch.int32, device="cuda")
+        positions = int(sum(min(16, n - 16 * int(b)) for b in kept))
+
+        def run():
+            for l, v in enumerate(views):
+                ops.da_decode_blocks(feeder.q[l, 1], v, mt, scale=stack.scale, out=stack.out[l], gathered=gat,
+                                     gathered_cnt=cnt, num_kept=num, ws=stack.ws)
+        run()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            run()
+        e1.record()
+        e1.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / (reps * len(views))
+        nbytes = positions * stack.Hkv * 128 * 4 + 2 * stack.Hq * 128 * 4
+        out[name] = {"kept_positions": positions, "us_per_call": round(us, 2),
+                     "achieved_GBs": round(nbytes / (us * 1e-6) / 1e9, 1),
+                     "frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+    return out
+
+
 def kernel_source_hash():
     import hashlib
     h = hashlib.sha256()
@@ -239,6 +290,8 @@ def main():
     bytes_full = n_now * wl.Hkv * 128 * 2 * 2 + 2 * wl.Hq * 128 * 4 + 2 * wl.Hkv * 128 * 2
     achieved = bytes_full / (full_ms * 1e-3) / 1e9
     log("Full-view kernel at n=%d: %.1f us per launch, %.0f GB/s" % (n_now, full_ms * 1e3, achieved))
+    blocks = roofline_blocks(stack, feeder, args.roofline_reps)
+    log("block-list view: %s" % json.dumps(blocks))
     traffic = profiled_traffic(bytes_full)
     traffic = None if traffic is None else int(round(traffic))
     copy_calibration(device)
@@ -272,6 +325,8 @@ def main():
                      "us_per_launch": round(full_ms * 1e3, 2), "algorithmic_bytes_per_launch": int(bytes_full),
                      "traffic_source": "profiles/decode_128k_hbm_counters.md (rocprofv3 FETCH_SIZE x2.0 + "
                                        "WRITE_SIZE x1.0, rescaled to this n); null if the kernel changed"},
+        "roofline_block_sparse": dict(blocks, kernel="da_decode_blocks (gather + decode_kernel<list>), permuted "
+                                      "block table, 36-layer rotation, n=%d" % n_now),
         "step_hbm_gbs": round(float(step_gbs), 1),
         "wall_s_timed": round(wall, 3),
     }

@@ -650,68 +650,54 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
   }
 }
 
-// Keep-mask -> ascending list of (physical block, valid positions). One workgroup per
-// request; block-wide exclusive scan of per-thread popcounts keeps the order.
+// Keep-mask -> ascending list of (physical block, valid positions). One thread per
+// logical block, 256 blocks per workgroup, many workgroups per request: a workgroup
+// counts the kept blocks of all mask words before its range (one wave, popcounts),
+// ranks its own blocks with ballots, and writes its entries coalesced. The workgroup
+// that holds block ceil(n/16)-1 writes the count.
 __global__ __launch_bounds__(256) void gather_kernel(sk_paged_kv kv, const uint32_t* __restrict__ mask,
                                                      const int32_t* __restrict__ sel, int sel_value,
                                                      int32_t* __restrict__ gathered, int32_t* __restrict__ cnt,
                                                      int32_t* __restrict__ num_kept, int32_t* err) {
   __shared__ int s_wave[4];
-  __shared__ int s_base;
-  const int b = blockIdx.x;
+  __shared__ int s_prefix;
+  const int b = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (sel && sel[b] != sel_value) return;
   const int n = kv.seq_lens[b];
   const int maxb = kv.max_blocks;
-  const int words_row = (maxb + 31) / 32;
   if (n < 1 || n > maxb * kBlock) {
-    if (tid == 0) {
+    if (blockIdx.x == 0 && tid == 0) {
       num_kept[b] = 0;
       set_error(err, SK_DEVERR_SEQ_LEN);
     }
     return;
   }
   const int nb = (n + kBlock - 1) / kBlock;
-  const int words = (nb + 31) / 32;
-  const uint32_t* mrow = mask + int64_t(b) * words_row;
-  const int32_t* bt = kv.block_tables + int64_t(b) * maxb;
-  int32_t* grow = gathered + int64_t(b) * maxb;
-  int32_t* crow = cnt + int64_t(b) * maxb;
-  if (tid == 0) s_base = 0;
-  __syncthreads();
-  for (int w0 = 0; w0 < words; w0 += blockDim.x) {
-    const int w = w0 + tid;
-    uint32_t bits = 0u;
-    if (w < words) {
-      bits = mrow[w];
-      int valid = nb - 32 * w;  // blocks of this word below nb
-      if (valid < 32) bits &= (1u << valid) - 1u;
-    }
-    int c = __popc(bits);
-    int x = c;
+  const int base = blockIdx.x * 256;
+  if (base >= nb) return;
+  const uint32_t* mrow = mask + int64_t(b) * ((maxb + 31) / 32);
+  if (wave == 0) {  // kept blocks before this workgroup's range (all full words)
+    int c = 0;
+    for (int w = lane; w < base / 32; w += 64) c += __popc(mrow[w]);
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      int y = __shfl_up(x, off);
-      if (lane >= off) x += y;
-    }
-    if (lane == 63) s_wave[wave] = x;
-    __syncthreads();
-    int wbase = 0;
-    for (int i = 0; i < wave; ++i) wbase += s_wave[i];
-    int pos = s_base + wbase + x - c;
-    while (bits) {
-      int bit = __ffs(bits) - 1;
-      bits &= bits - 1u;
-      int blk = 32 * w + bit;
-      grow[pos] = bt[blk];
-      crow[pos] = min(kBlock, n - kBlock * blk);
-      ++pos;
-    }
-    __syncthreads();
-    if (tid == 0) s_base += s_wave[0] + s_wave[1] + s_wave[2] + s_wave[3];
-    __syncthreads();
+    for (int off = 32; off > 0; off >>= 1) c += __shfl_xor(c, off);
+    if (lane == 0) s_prefix = c;
   }
-  if (tid == 0) num_kept[b] = s_base;
+  const int blk = base + tid;
+  const bool kept = blk < nb && ((mrow[blk >> 5] >> (blk & 31)) & 1u);
+  const uint64_t bal = __ballot(kept);
+  const int rank = __popcll(bal & ((1ull << lane) - 1ull));
+  if (lane == 0) s_wave[wave] = __popcll(bal);
+  __syncthreads();
+  int pos = s_prefix + rank;
+  for (int i = 0; i < wave; ++i) pos += s_wave[i];
+  if (kept) {
+    gathered[int64_t(b) * maxb + pos] = kv.block_tables[int64_t(b) * maxb + blk];
+    cnt[int64_t(b) * maxb + pos] = min(kBlock, n - kBlock * blk);
+  }
+  if (tid == 0 && (nb - 1) / 256 == int(blockIdx.x))
+    num_kept[b] = s_prefix + s_wave[0] + s_wave[1] + s_wave[2] + s_wave[3];
 }
 
 template <int MODE>
@@ -789,8 +775,9 @@ int da_decode_blocks(const float* q, sk_paged_kv kv, const void* k_new, const vo
   int st = check_kv(kv);
   if (st) return st;
   if (!keep_mask || !gathered || !gathered_cnt || !num_kept || !ws) return SK_E_NULL;
-  hipLaunchKernelGGL(gather_kernel, dim3(kv.batch), dim3(256), 0, stream, kv, keep_mask, sel, sel_value, gathered,
-                     gathered_cnt, num_kept, reinterpret_cast<int32_t*>(ws));
+  hipLaunchKernelGGL(gather_kernel, dim3(unsigned((kv.max_blocks + 255) / 256), unsigned(kv.batch)), dim3(256), 0,
+                     stream, kv, keep_mask, sel, sel_value, gathered, gathered_cnt, num_kept,
+                     reinterpret_cast<int32_t*>(ws));
   st = launch_status(hipGetLastError());
   if (st) return st;
   return launch_decode<kList>(q, kv, k_new, v_new, 0, 1, scale, sel, sel_value, gathered, gathered_cnt, num_kept,
