@@ -129,9 +129,6 @@ __device__ inline void publish(float* p, float v) { __hip_atomic_store(p, v, __A
 __device__ inline float fetch_published(const float* p) {
   return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ inline f32x4 fetch_published4(const float* p) {
-  return f32x4{fetch_published(p), fetch_published(p + 1), fetch_published(p + 2), fetch_published(p + 3)};
-}
 // s_waitcnt vmcnt(0): all of this wave's stores have completed (gfx9 counts stores in vmcnt).
 __device__ inline void wait_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
@@ -287,25 +284,67 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
     const bool any = (lane < B) && P.sel[lane] == P.sel_value;
     if (__builtin_amdgcn_readfirstlane(__ballot(any) != 0) == 0) return;
   }
-  __syncthreads();
 
-  // ---- plan: tiles per request (identical in every workgroup)
-  {
+  // ---- plan: tiles per request, tiles per split, first work item of each request --
+  // identical in every workgroup. Tiles per split: enough that the work items fit the
+  // grid, never fewer than kMinTilesPerSplit, at most kMaxSplits splits per (request,
+  // KV head).
+  auto split_size = [&](int total, int active, int max_tiles) {
+    int budget = int(gridDim.x) / Hkv - active;
+    if (budget < 1) budget = 1;
+    int T = (total + budget - 1) / budget;
+    const int T_cap = (max_tiles + kMaxSplits - 1) / kMaxSplits;
+    if (T < T_cap) T = T_cap;
+    if (T < kMinTilesPerSplit) T = kMinTilesPerSplit;
+    return T;
+  };
+  auto bad_request = [&](int b, int n, bool valid) {  // all-zero output row (+ commit if possible)
+    set_error(P.err, valid ? SK_DEVERR_EMPTY : SK_DEVERR_SEQ_LEN);
+    float* o = P.out + int64_t(b) * Hq * kHeadDim;
+    for (int i = 0; i < Hq * kHeadDim; ++i) o[i] = 0.f;
+    if (valid && P.k_new)
+      for (int g = 0; g < Hkv; ++g)
+        for (int l = 0; l < 64; ++l) commit_token_lanes(P, b, g, n, l);
+  };
+  int T, total_items;
+  int w_tiles = 0, w_start = 0;  // small batches: lane b holds request b's tiles and first item
+  if (B <= 64) {
+    // every wave plans on its own with shuffles; no workgroup barrier
+    int tiles = 0;
+    if (lane < B && request_active<HAS_SEL>(P, lane)) {
+      const int n = P.kv.seq_lens[lane];
+      const bool valid = n >= 1 && n <= maxb * kBlock;
+      if (valid) tiles = request_tiles<MODE>(P, lane, n);
+      if (blockIdx.x == 0 && wave == 0 && (!valid || tiles == 0)) bad_request(lane, n, valid);
+    }
+    int sum = tiles, act = tiles > 0, mx = tiles;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      sum += __shfl_xor(sum, off);
+      act += __shfl_xor(act, off);
+      mx = max(mx, __shfl_xor(mx, off));
+    }
+    T = split_size(sum, act, mx);
+    const int items = ((tiles + T - 1) / T) * Hkv;
+    int x = items;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(x, off);
+      if (lane >= off) x += y;
+    }
+    w_tiles = tiles;
+    w_start = x - items;
+    total_items = __shfl(x, 63);
+  } else {
+    __syncthreads();
     int my_sum = 0, my_active = 0, my_max = 0;
     for (int b = tid; b < B; b += blockDim.x) {
       int tiles = 0;
       if (request_active<HAS_SEL>(P, b)) {
-        int n = P.kv.seq_lens[b];
-        bool valid = n >= 1 && n <= maxb * kBlock;
+        const int n = P.kv.seq_lens[b];
+        const bool valid = n >= 1 && n <= maxb * kBlock;
         if (valid) tiles = request_tiles<MODE>(P, b, n);
-        if (blockIdx.x == 0 && (!valid || tiles == 0)) {
-          set_error(P.err, valid ? SK_DEVERR_EMPTY : SK_DEVERR_SEQ_LEN);
-          float* o = P.out + int64_t(b) * Hq * kHeadDim;
-          for (int i = 0; i < Hq * kHeadDim; ++i) o[i] = 0.f;
-          if (valid && P.k_new)
-            for (int g = 0; g < Hkv; ++g)
-              for (int l = 0; l < 64; ++l) commit_token_lanes(P, b, g, n, l);
-        }
+        if (blockIdx.x == 0 && (!valid || tiles == 0)) bad_request(b, n, valid);
       }
       s_tiles[b] = tiles;
       my_sum += tiles;
@@ -315,40 +354,29 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
     if (my_sum) atomicAdd(&s_misc[0], my_sum);
     if (my_active) atomicAdd(&s_misc[2], my_active);
     if (my_max) atomicMax(&s_misc[4], my_max);
-  }
-  __syncthreads();
-  if (tid == 0) {
-    // tiles per split: enough that the work items fit the grid, never fewer than one pair
-    // per wave, and at most kMaxSplits splits per (request, KV head)
-    int total = s_misc[0];
-    int budget = int(gridDim.x) / Hkv - s_misc[2];
-    if (budget < 1) budget = 1;
-    int T = (total + budget - 1) / budget;
-    int T_cap = (s_misc[4] + kMaxSplits - 1) / kMaxSplits;
-    if (T < T_cap) T = T_cap;
-    if (T < kMinTilesPerSplit) T = kMinTilesPerSplit;
-    s_misc[1] = T;
-  }
-  __syncthreads();
-  const int T = s_misc[1];
-  if (wave == 0) {
-    int carry = 0;
-    for (int base = 0; base < B; base += 64) {
-      int b = base + lane;
-      int items = (b < B) ? ((s_tiles[b] + T - 1) / T) * Hkv : 0;
-      int x = items;
+    __syncthreads();
+    if (tid == 0) s_misc[1] = split_size(s_misc[0], s_misc[2], s_misc[4]);
+    __syncthreads();
+    T = s_misc[1];
+    if (wave == 0) {
+      int carry = 0;
+      for (int base = 0; base < B; base += 64) {
+        const int b = base + lane;
+        const int items = (b < B) ? ((s_tiles[b] + T - 1) / T) * Hkv : 0;
+        int x = items;
 #pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        int y = __shfl_up(x, off);
-        if (lane >= off) x += y;
+        for (int off = 1; off < 64; off <<= 1) {
+          const int y = __shfl_up(x, off);
+          if (lane >= off) x += y;
+        }
+        if (b < B) s_start[b] = carry + x - items;
+        carry += __shfl(x, 63);
       }
-      if (b < B) s_start[b] = carry + x - items;
-      carry += __shfl(x, 63);
+      if (lane == 0) s_start[B] = carry;
     }
-    if (lane == 0) s_start[B] = carry;
+    __syncthreads();
+    total_items = s_start[B];
   }
-  __syncthreads();
-  const int total_items = s_start[B];
 
   // XCD-aware order: consecutive items (the splits of one (request, KV head)) go to
   // workgroups that the dispatcher places on the same XCD (round-robin over 8 XCDs),
@@ -361,16 +389,25 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
   const uint8_t* vpool = reinterpret_cast<const uint8_t*>(P.kv.v_pool);
 
   for (int item = item_first; item < total_items; item += gridDim.x) {
-    // locate the request: largest b with start[b] <= item (it always has items)
-    int lo_b = 0, hi_b = B - 1;
-    while (lo_b < hi_b) {
-      int mid = (lo_b + hi_b + 1) >> 1;
-      if (s_start[mid] <= item) lo_b = mid; else hi_b = mid - 1;
+    // locate the request: the one whose item range holds `item` (it has items)
+    int b, tiles_b, item_base;
+    if (B <= 64) {
+      const int end = w_start + ((w_tiles + T - 1) / T) * Hkv;
+      b = __builtin_amdgcn_readfirstlane(__popcll(__ballot(lane < B && end <= item)));
+      tiles_b = __builtin_amdgcn_readlane(w_tiles, b);
+      item_base = __builtin_amdgcn_readlane(w_start, b);
+    } else {
+      int lo_b = 0, hi_b = B - 1;
+      while (lo_b < hi_b) {
+        const int mid = (lo_b + hi_b + 1) >> 1;
+        if (s_start[mid] <= item) lo_b = mid; else hi_b = mid - 1;
+      }
+      b = lo_b;
+      tiles_b = s_tiles[b];
+      item_base = s_start[b];
     }
-    const int b = lo_b;
-    const int tiles_b = s_tiles[b];
     const int splits = (tiles_b + T - 1) / T;
-    const int local = item - s_start[b];
+    const int local = item - item_base;
     const int g = local / splits, split = local % splits;
     const int n = P.kv.seq_lens[b];
     const int t_begin = split * T, t_end = min(t_begin + T, tiles_b);
@@ -572,76 +609,42 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
       }
       __syncthreads();
       if (s_misc[3]) {
+        // one thread per output element: all splits' (m, l, acc) are loaded at once,
+        // 32 splits per batch of independent loads, and combined in split order
         const int S = splits;
         const size_t stride = size_t(G) * (kHeadDim + 2);
-        const float* base = P.partials + size_t(s_start[b] + g * splits) * stride;
-        float* sm = s_acc;             // [S][G] maxima, then weights
-        float* sl = sm + S * G;        // [S][G] sums
-        float* red = sl + S * G;       // [NG][G*32] float4 partial sums
-        float* sL = s_l;               // [G] merged sums
-        const int F = G * 32;          // float4 outputs of this KV head
-        const int NG = kThreads / F;   // split groups
-        const int fi = tid % F, sg = tid / F;
-        for (int e = tid; e < S * G; e += blockDim.x) {
-          const int s = e / G, h = e % G;
-          sm[e] = fetch_published(base + s * stride + G * kHeadDim + h);
-          sl[e] = fetch_published(base + s * stride + G * (kHeadDim + 1) + h);
-        }
-        // issue this thread's first chunk of partial loads before the barrier
-        f32x4 xs[8];
+        const float* base = P.partials + size_t(item_base + g * splits) * stride;
+        for (int idx = tid; idx < G * kHeadDim; idx += blockDim.x) {
+          const int h = idx >> 7, d = idx & (kHeadDim - 1);
+          float M = -INFINITY, L = 0.f, A = 0.f;
+          for (int s0 = 0; s0 < S; s0 += 32) {
+            float ms[32], ls[32], as[32];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int s = sg + u * NG;
-          xs[u] = (sg < NG && s < S) ? fetch_published4(base + s * stride + 4 * fi) : f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-        __syncthreads();
-        for (int h = wave; h < G; h += W) {
-          float M = -INFINITY;
-          for (int s = lane; s < S; s += 64) M = fmaxf(M, sm[s * G + h]);
-#pragma unroll
-          for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-          const float Mu = (M == -INFINITY) ? 0.f : M;
-          float L = 0.f;
-          for (int s = lane; s < S; s += 64) {
-            const float w = __builtin_amdgcn_exp2f(sm[s * G + h] - Mu);
-            sm[s * G + h] = w;
-            L += sl[s * G + h] * w;
-          }
-#pragma unroll
-          for (int off = 32; off > 0; off >>= 1) L += __shfl_xor(L, off);
-          if (lane == 0) sL[h] = L;
-        }
-        __syncthreads();
-        if (sg < NG) {
-          const int h = fi >> 5;
-          f32x4 a = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int u = 0; u < 8; ++u) {
-            const int s = sg + u * NG;
-            if (s < S) a += xs[u] * sm[s * G + h];
-          }
-          for (int s0 = sg + 8 * NG; s0 < S; s0 += 8 * NG) {
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-              const int s = s0 + u * NG;
-              xs[u] = (s < S) ? fetch_published4(base + s * stride + 4 * fi) : f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int u = 0; u < 32; ++u) {
+              const float* ps = base + size_t(min(s0 + u, S - 1)) * stride;
+              ms[u] = fetch_published(ps + G * kHeadDim + h);
+              ls[u] = fetch_published(ps + G * (kHeadDim + 1) + h);
+              as[u] = fetch_published(ps + h * kHeadDim + d);
             }
+            float Mc = M;
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-              const int s = s0 + u * NG;
-              if (s < S) a += xs[u] * sm[s * G + h];
+            for (int u = 0; u < 32; ++u)
+              if (s0 + u < S) Mc = fmaxf(Mc, ms[u]);
+            const float Mu = (Mc == -INFINITY) ? 0.f : Mc;
+            const float r = __builtin_amdgcn_exp2f(M - Mu);
+            L *= r;
+            A *= r;
+#pragma unroll
+            for (int u = 0; u < 32; ++u) {
+              if (s0 + u < S) {
+                const float e = __builtin_amdgcn_exp2f(ms[u] - Mu);
+                L += ls[u] * e;
+                A += as[u] * e;
+              }
             }
+            M = Mc;
           }
-          *reinterpret_cast<f32x4*>(red + 4 * (sg * F + fi)) = a;
-        }
-        __syncthreads();
-        for (int f = tid; f < F; f += blockDim.x) {
-          f32x4 a = {0.f, 0.f, 0.f, 0.f};
-          for (int q = 0; q < NG; ++q) a += *reinterpret_cast<const f32x4*>(red + 4 * (q * F + f));
-          const float L = sL[f >> 5];
-          const float inv = (L > 0.f) ? 1.f / L : 0.f;
-          a *= inv;
-          *reinterpret_cast<f32x4*>(P.out + (int64_t(b) * Hq + g * G) * kHeadDim + 4 * f) = a;
+          P.out[(int64_t(b) * Hq + g * G + h) * kHeadDim + d] = (L > 0.f) ? A / L : 0.f;
         }
         if (tid == 0) P.tickets[b * Hkv + g] = 0u;
       }
