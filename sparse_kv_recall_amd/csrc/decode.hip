@@ -37,6 +37,7 @@ constexpr int kThreads = 64 * kWavesPerWG;
 constexpr int kMinTilesPerSplit = 8;                   // small launches: many short splits
 constexpr int kMaxSplits = 256;                     // splits per (request, KV head)
 constexpr int kGridCap = 256;                       // decode workgroups per launch (one per CU)
+constexpr int kMergeBatch = 48;                     // split accumulators loaded together in the merge
 constexpr float kLog2e = 1.4426950408889634f;
 
 struct DecodeParams {
@@ -129,6 +130,32 @@ __device__ inline void publish(float* p, float v) { __hip_atomic_store(p, v, __A
 __device__ inline float fetch_published(const float* p) {
   return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// Wave reductions: DPP within each row of 16 lanes (swap neighbours, swap pairs, rotate
+// by 4, rotate by 8), then the four row results read into scalar registers. The result
+// is the same in every lane (taken from lanes 0, 16, 32, 48), so it is deterministic.
+template <int CTRL>
+__device__ inline float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+__device__ inline float lane_value(float v, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
+constexpr int kDppSwap1 = 0xB1, kDppSwap2 = 0x4E, kDppRor4 = 0x124, kDppRor8 = 0x128;
+__device__ inline float wave_max(float v) {
+  v = fmaxf(v, dpp<kDppSwap1>(v));
+  v = fmaxf(v, dpp<kDppSwap2>(v));
+  v = fmaxf(v, dpp<kDppRor4>(v));
+  v = fmaxf(v, dpp<kDppRor8>(v));
+  return fmaxf(fmaxf(lane_value(v, 0), lane_value(v, 16)), fmaxf(lane_value(v, 32), lane_value(v, 48)));
+}
+__device__ inline float wave_sum(float v) {
+  v += dpp<kDppSwap1>(v);
+  v += dpp<kDppSwap2>(v);
+  v += dpp<kDppRor4>(v);
+  v += dpp<kDppRor8>(v);
+  return (lane_value(v, 0) + lane_value(v, 16)) + (lane_value(v, 32) + lane_value(v, 48));
+}
+
 // s_waitcnt vmcnt(0): all of this wave's stores have completed (gfx9 counts stores in vmcnt).
 __device__ inline void wait_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
@@ -262,7 +289,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
   const int acc_region = max(W * G * kHeadDim, 2 * kMaxSplits * G + 4 * kThreads);
 
   // LDS: q operands [4][2][64] x 16 B | current token K,V [128] words | acc [W][G][128] (merge scratch
-  //      later) | m [W][16] | l [W][16] | tiles [B] | start [B+1] | misc
+  //      later) | m [W][16] | l [W][16] | tiles [B] | start [B+1] | len [B] | misc
   u32x4* s_q = reinterpret_cast<u32x4*>(smem);
   uint32_t* s_new = reinterpret_cast<uint32_t*>(smem + 4 * kThreads);  // current token: K [64] | V [64] words
   float* s_acc = smem + 4 * kThreads + 128;
@@ -270,7 +297,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
   float* s_l = s_m + W * 16;
   int* s_tiles = reinterpret_cast<int*>(s_l + W * 16);
   int* s_start = s_tiles + B;
-  int* s_misc = s_start + B + 1;  // [0] tile sum, [1] T, [2] active requests, [3] last flag, [4] max tiles
+  int* s_len = s_start + B + 1;  // [B] sequence lengths (large batches)
+  int* s_misc = s_len + B;  // [0] tile sum, [1] T, [2] active requests, [3] last flag, [4] max tiles
 
   if (tid == 0) {
     s_misc[0] = 0;
@@ -307,7 +335,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
         for (int l = 0; l < 64; ++l) commit_token_lanes(P, b, g, n, l);
   };
   int T, total_items;
-  int w_tiles = 0, w_start = 0;  // small batches: lane b holds request b's tiles and first item
+  int w_tiles = 0, w_start = 0, w_len = 0;  // small batches: lane b holds request b's tiles,
+                                             // first item and sequence length
   if (B <= 64) {
     // every wave plans on its own with shuffles; no workgroup barrier
     int tiles = 0;
@@ -333,6 +362,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
       if (lane >= off) x += y;
     }
     w_tiles = tiles;
+    w_len = (lane < B) ? P.kv.seq_lens[lane] : 0;
     w_start = x - items;
     total_items = __shfl(x, 63);
   } else {
@@ -347,6 +377,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
         if (blockIdx.x == 0 && (!valid || tiles == 0)) bad_request(b, n, valid);
       }
       s_tiles[b] = tiles;
+      s_len[b] = P.kv.seq_lens[b];
       my_sum += tiles;
       my_active += tiles > 0;
       my_max = max(my_max, tiles);
@@ -390,11 +421,12 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
 
   for (int item = item_first; item < total_items; item += gridDim.x) {
     // locate the request: the one whose item range holds `item` (it has items)
-    int b, tiles_b, item_base;
+    int b, tiles_b, item_base, n;
     if (B <= 64) {
       const int end = w_start + ((w_tiles + T - 1) / T) * Hkv;
       b = __builtin_amdgcn_readfirstlane(__popcll(__ballot(lane < B && end <= item)));
       tiles_b = __builtin_amdgcn_readlane(w_tiles, b);
+      n = __builtin_amdgcn_readlane(w_len, b);
       item_base = __builtin_amdgcn_readlane(w_start, b);
     } else {
       int lo_b = 0, hi_b = B - 1;
@@ -404,13 +436,21 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
       }
       b = lo_b;
       tiles_b = s_tiles[b];
+      n = s_len[b];
       item_base = s_start[b];
     }
     const int splits = (tiles_b + T - 1) / T;
     const int local = item - item_base;
     const int g = local / splits, split = local % splits;
-    const int n = P.kv.seq_lens[b];
     const int t_begin = split * T, t_end = min(t_begin + T, tiles_b);
+
+    // q rows of the G heads of KV head g for the operand staging below, requested first so
+    // that their latency overlaps the descriptor loads. Lanes past the G heads read head 0
+    // (and stage zeros).
+    const int qc = tid >> 7, qpart = (tid >> 6) & 1, qcol = lane & 15, qgrp = lane >> 4;
+    const float* qrow = P.q + (int64_t(b) * Hq + g * G + (qcol < G ? qcol : 0)) * kHeadDim + 8 * (4 * qc + qgrp);
+    const f32x4 qa0 = *reinterpret_cast<const f32x4*>(qrow);
+    const f32x4 qa1 = *reinterpret_cast<const f32x4*>(qrow + 4);
 
     // which tile receives the current token (-1: none attended here)
     int commit_tile = -1;
@@ -433,13 +473,15 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
     const bool split_commits = commit_tile >= t_begin && commit_tile < t_end;
     const bool own_commit = split_commits && (commit_tile - t_begin) % W == wave;
     const int loop_tiles = my_tiles - (own_commit ? 1 : 0);
-    if (split_commits && tid < 128) {
-      const uint16_t* src = (tid < 64 ? P.k_new : P.v_new) + (int64_t(b) * Hkv + g) * kHeadDim;
-      s_new[tid] = reinterpret_cast<const uint32_t*>(src)[tid & 63];
-    }
+    // the current token's K and V words (staged in LDS below); without a commit here the
+    // load reads q instead and is discarded, so no branch separates it from its use
+    const uint32_t* tok = reinterpret_cast<const uint32_t*>(P.q);
+    if (split_commits)
+      tok = reinterpret_cast<const uint32_t*>(((tid & 64) ? P.v_new : P.k_new) + (int64_t(b) * Hkv + g) * kHeadDim);
+    const uint32_t tok_word = tok[lane];
 
     // descriptors (physical block, valid range) of this wave's first 64 tiles, lane r for
-    // tile r; loaded before q so that both loads are in flight together
+    // tile r
     int dphys = 0, dlohi = 0;
     auto load_desc = [&](int c0) {
       const int ti = t_begin + wave + (c0 + lane) * W;
@@ -450,27 +492,24 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
     };
     load_desc(0);
 
-    // q of the G heads of KV head g -> MFMA B operands (hi and lo bf16 parts), staged in LDS:
-    // entry (c, part, lane) holds dims 8*(4c + lane/16) .. +7 of head lane%16.
+    // q -> MFMA B operands (hi and lo bf16 parts), staged in LDS: entry (c, part, lane) holds
+    // dims 8*(4c + lane/16) .. +7 of head lane%16. The wave's first tile is requested
+    // before the q rows are used, so its latency overlaps the staging. Straight-line code
+    // (no branch between loads and use): a wave without loop tiles requests its first
+    // descriptor (block 0 of the pool when it has none) and never uses it.
+    u32x4 k0[4], v0[4], k1[4], v1[4];
+    load_tile(kpool, vpool, __builtin_amdgcn_readfirstlane(dphys), g, Hkv, lane, k0, v0);
+    if (split_commits && tid < 128) s_new[tid] = tok_word;
     {
-      const int c = tid >> 7, part = (tid >> 6) & 1, ln = tid & 63;
-      const int qcol = ln & 15, qgrp = ln >> 4;
-      u32x4 packed = {0u, 0u, 0u, 0u};
-      if (qcol < G) {
-        const float* qrow = P.q + (int64_t(b) * Hq + g * G + qcol) * kHeadDim + 8 * (4 * c + qgrp);
-        f32x4 a0 = *reinterpret_cast<const f32x4*>(qrow);
-        f32x4 a1 = *reinterpret_cast<const f32x4*>(qrow + 4);
-        float x[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-        bf16x8 o;
+      const float x[8] = {qa0.x, qa0.y, qa0.z, qa0.w, qa1.x, qa1.y, qa1.z, qa1.w};
+      bf16x8 o;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          float v = x[i] * P.qscale;
-          __bf16 hi = __bf16(v);
-          o[i] = part ? __bf16(v - bf16_to_f32(hi)) : hi;
-        }
-        packed = __builtin_bit_cast(u32x4, o);
+      for (int i = 0; i < 8; ++i) {
+        const float v = x[i] * P.qscale;
+        const __bf16 hi = __bf16(v);
+        o[i] = qpart ? __bf16(v - bf16_to_f32(hi)) : hi;
       }
-      s_q[tid] = packed;
+      s_q[tid] = (qcol < G) ? __builtin_bit_cast(u32x4, o) : u32x4{0u, 0u, 0u, 0u};
     }
     __syncthreads();
 
@@ -528,14 +567,15 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
     // in flight while this one is computed (a deeper ring measured slower: more loads in
     // flight per wave only added queueing). A fetch index past the end is clamped to the
     // chunk's last tile (a cache hit), so the loop body has no data-dependent branches.
-    u32x4 k0[4], v0[4], k1[4], v1[4];
     for (int c0 = 0; c0 < loop_tiles; c0 += 64) {
       const int nt = min(64, loop_tiles - c0);
-      if (c0 > 0) load_desc(c0);
       const int last = nt - 1;
 #define SK_FETCH(K, V, J) load_tile(kpool, vpool, __builtin_amdgcn_readlane(dphys, min((J), last)), g, Hkv, lane, K, V)
 #define SK_LOHI(J) __builtin_amdgcn_readlane(dlohi, (J))
-      SK_FETCH(k0, v0, 0);
+      if (c0 > 0) {
+        load_desc(c0);
+        SK_FETCH(k0, v0, 0);
+      }
       int j = 0;
       for (; j + 2 <= nt; j += 2) {
         SK_FETCH(k1, v1, j + 1);
@@ -609,42 +649,40 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
       }
       __syncthreads();
       if (s_misc[3]) {
-        // one thread per output element: all splits' (m, l, acc) are loaded at once,
-        // 32 splits per batch of independent loads, and combined in split order
+        // Merge in split order, kMergeBatch splits at a time, without LDS: all 64 lanes of
+        // a wave work on one head, lane u holds the (m, l) of split u of the batch, and
+        // each lane loads the accumulators of its output element for the whole batch in
+        // the same round of independent loads. The batch maximum and weighted sum of l
+        // are wave reductions; lane u's weight is broadcast (readlane) to scale split u's
+        // accumulator, in split order.
         const int S = splits;
-        const size_t stride = size_t(G) * (kHeadDim + 2);
+        const uint32_t stride = uint32_t(G) * (kHeadDim + 2);  // floats per split partial
         const float* base = P.partials + size_t(item_base + g * splits) * stride;
         for (int idx = tid; idx < G * kHeadDim; idx += blockDim.x) {
-          const int h = idx >> 7, d = idx & (kHeadDim - 1);
+          const int h = idx >> 7;  // uniform in the wave
           float M = -INFINITY, L = 0.f, A = 0.f;
-          for (int s0 = 0; s0 < S; s0 += 32) {
-            float ms[32], ls[32], as[32];
+          for (int s0 = 0; s0 < S; s0 += kMergeBatch) {
+            const int nb = min(kMergeBatch, S - s0);
+            const uint32_t ml = uint32_t(s0 + min(lane, nb - 1)) * stride + G * kHeadDim + h;
+            const float mv = fetch_published(base + ml);
+            const float lv = fetch_published(base + ml + G);
+            float as[kMergeBatch];
 #pragma unroll
-            for (int u = 0; u < 32; ++u) {
-              const float* ps = base + size_t(min(s0 + u, S - 1)) * stride;
-              ms[u] = fetch_published(ps + G * kHeadDim + h);
-              ls[u] = fetch_published(ps + G * (kHeadDim + 1) + h);
-              as[u] = fetch_published(ps + h * kHeadDim + d);
-            }
-            float Mc = M;
-#pragma unroll
-            for (int u = 0; u < 32; ++u)
-              if (s0 + u < S) Mc = fmaxf(Mc, ms[u]);
-            const float Mu = (Mc == -INFINITY) ? 0.f : Mc;
+            for (int u = 0; u < kMergeBatch; ++u)
+              as[u] = fetch_published(base + (uint32_t(s0 + min(u, nb - 1)) * stride + uint32_t(idx)));
+            const float Mn = fmaxf(M, wave_max((lane < nb) ? mv : -INFINITY));
+            const float Mu = (Mn == -INFINITY) ? 0.f : Mn;
             const float r = __builtin_amdgcn_exp2f(M - Mu);
-            L *= r;
+            const float e = (lane < nb) ? __builtin_amdgcn_exp2f(mv - Mu) : 0.f;
+            L = L * r + wave_sum(e * lv);
             A *= r;
+            // weights past the batch are zero and their (repeated) accumulators finite
 #pragma unroll
-            for (int u = 0; u < 32; ++u) {
-              if (s0 + u < S) {
-                const float e = __builtin_amdgcn_exp2f(ms[u] - Mu);
-                L += ls[u] * e;
-                A += as[u] * e;
-              }
-            }
-            M = Mc;
+            for (int u = 0; u < kMergeBatch; ++u)
+              A += lane_value(e, u) * as[u];
+            M = Mn;
           }
-          P.out[(int64_t(b) * Hq + g * G + h) * kHeadDim + d] = (L > 0.f) ? A / L : 0.f;
+          P.out[(int64_t(b) * Hq + g * G + h) * kHeadDim + (idx & (kHeadDim - 1))] = (L > 0.f) ? A / L : 0.f;
         }
         if (tid == 0) P.tickets[b * Hkv + g] = 0u;
       }
@@ -741,7 +779,7 @@ int launch_decode(const float* q, sk_paged_kv kv, const void* k_new, const void*
   grid = (grid + 7) / 8 * 8;
   const int acc_region = std::max(kWavesPerWG * G * kHeadDim, 2 * kMaxSplits * G + 4 * kThreads);
   size_t lds = size_t(kThreads) * 16 + 128 * 4 + size_t(acc_region) * 4 + size_t(kWavesPerWG) * 16 * 4 * 2 +
-               size_t(2 * kv.batch + 1 + 8) * 4;
+               size_t(3 * kv.batch + 1 + 8) * 4;
   if (sel)
     hipLaunchKernelGGL((decode_kernel<MODE, true>), dim3(unsigned(grid)), dim3(kThreads), lds, stream, P);
   else
