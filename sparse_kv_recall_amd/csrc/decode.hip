@@ -12,17 +12,18 @@
 //  * Work item = (request, KV head, split of consecutive tiles); a tile is one
 //    16-position block of one KV head (4 KiB of K and 4 KiB of V). Every workgroup
 //    derives the same plan from seq_lens / selectors, so no planning launch is needed.
-//  * One workgroup = 4 waves; a wave takes pairs of tiles (32 positions). K and V
-//    tiles are stored in the byte order of the v_mfma_f32_16x16x32_bf16 operands, so
-//    each lane issues plain coalesced 16-byte loads (1 KiB per wave instruction) that
-//    are already its MFMA operand registers: no LDS staging, no shuffles.
+//  * One workgroup = 8 waves sharing one work item; wave w takes tiles w, w+8, ... of the
+//    split through a two-deep register ring (the next tile's loads in flight while the
+//    current one is computed). K and V tiles are stored in the byte order of the MFMA
+//    operands, so each lane issues plain coalesced 16-byte loads (1 KiB per wave
+//    instruction) that are already its operand registers: no LDS staging, no shuffles.
 //  * S = K q^T and O += V^T P^T run on the matrix cores. q (fp32) and p (fp32) are
 //    split into bf16 hi + lo parts, so the products keep ~16 mantissa bits; the
 //    accumulation is fp32. All query heads of a KV head share one read of K and V.
 //  * Online softmax in base 2 (q pre-scaled by scale*log2 e), max reduced across the
 //    four lane groups with shuffles; waves combine through LDS; splits are merged by
-//    the last workgroup to finish (atomic ticket per (request, KV head)), in a fixed
-//    split order, so results are deterministic.
+//    the last workgroup to finish (atomic ticket per (request, KV head)) in registers,
+//    in a fixed split order, so results are deterministic.
 #include <math.h>
 
 #include <algorithm>
