@@ -231,6 +231,61 @@ def cpu_baseline(wl, recall_rate, budget_s=20.0):
                        "generation not timed" % (n_local, t_local, t_full))}
 
 
+def always_full_rate(stack, feeder, wl, steps):
+    """Always-Full decoding on the same stack and kernels (every step attends all n keys
+    and commits its candidate; no Local pass, no gate): the baseline ODA is set against.
+    Replays the first `steps` steps again."""
+    import torch
+    from sparse_kv_recall_amd.stack import capture_graph
+    q, k, v = feeder.q, feeder.k, feeder.v
+
+    def step():
+        feeder.step()
+        stack.full_pass(q[:, 1, :], k[:, 1, :], v[:, 1, :], gated=False)
+
+    graph = capture_graph(step)
+    feeder.set_step(0)
+    graph.replay()
+    torch.cuda.synchronize()
+    feeder.set_step(0)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    del graph
+    return {"steps": steps, "tok_s": round(steps * wl.batch / (ms / 1e3), 2), "ms_per_step": round(ms / steps, 4)}
+
+
+def hybrid_rate(stack, feeder, wl, steps):
+    """Decode rate of the same workload with per-layer access control: three of every
+    four layers restricted to the Local range (their recall pass runs the Local view).
+    Replays the first `steps` steps again (rewriting the positions they committed)."""
+    import torch
+
+    saved = stack.local_only
+    stack.local_only = frozenset(l for l in range(wl.layers) if l % 4 != 3)
+    graph = capture_step(stack, feeder)
+    feeder.set_step(0)
+    graph.replay()
+    torch.cuda.synchronize()
+    feeder.set_step(0)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    stack.local_only = saved
+    del graph
+    return {"local_only_layers": sum(1 for l in range(wl.layers) if l % 4 != 3),
+            "steps": steps, "recall_steps": int((wl.sched_scores[:steps, 0] > 0).sum()),
+            "tok_s": round(steps * wl.batch / (ms / 1e3), 2), "ms_per_step": round(ms / steps, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -292,6 +347,10 @@ def main():
     log("Full-view kernel at n=%d: %.1f us per launch, %.0f GB/s" % (n_now, full_ms * 1e3, achieved))
     blocks = roofline_blocks(stack, feeder, args.roofline_reps)
     log("block-list view: %s" % json.dumps(blocks))
+    full_only = always_full_rate(stack, feeder, wl, min(64, args.steps))
+    log("always-Full baseline: %s" % json.dumps(full_only))
+    hybrid = hybrid_rate(stack, feeder, wl, min(256, args.steps))
+    log("hybrid access control: %s" % json.dumps(hybrid))
     traffic = profiled_traffic(bytes_full)
     traffic = None if traffic is None else int(round(traffic))
     copy_calibration(device)
@@ -302,6 +361,7 @@ def main():
     bpt = wl.Hkv * 128 * 4
     step_bytes = (wl.layers * (np.minimum(ns, wl.sinks + wl.window) + np.where(rec, ns, 0)) * bpt).sum()
     step_gbs = step_bytes / (ms_total * 1e-3) / 1e9
+    full_bytes = (wl.layers * ns * bpt).sum()  # always-Full reads every key of every layer each step
 
     res = {
         "metric": METRIC,
@@ -327,6 +387,9 @@ def main():
                                        "WRITE_SIZE x1.0, rescaled to this n); null if the kernel changed"},
         "roofline_block_sparse": dict(blocks, kernel="da_decode_blocks (gather + decode_kernel<list>), permuted "
                                       "block table, 36-layer rotation, n=%d" % n_now),
+        "always_full_baseline": dict(full_only, speedup_of_oda=round(tok_s / full_only["tok_s"], 3),
+                                     attention_bytes_ratio=round(float(full_bytes / step_bytes), 3)),
+        "hybrid_local_only": hybrid,
         "step_hbm_gbs": round(float(step_gbs), 1),
         "wall_s_timed": round(wall, 3),
     }

@@ -29,12 +29,18 @@ Parity status of each function (pinned by the ``-m "not gpu"`` tests):
 * attention.attend ..................................... pinned
 * recall.recall_score / recall.gate .................... pinned
 * gather.gather_blocks / gather.da_mode_blocks ......... pinned
-* oda.oda_layer_step / oda.request_mode ................ pinned by definition only
-  (the pages print no worked example of a stack step; the commit and select
-  rules are checked against their restatement, brute force and invariants)
-* cost.* ............................................... attention-only ratio
-  pinned; the pages' whole-model 24.26% figure is parity unpinned (it needs
-  dense-layer sizes the pages do not give).
+* oda.local_pass / full_pass / blocks_pass / recall_pass / select / request_mode
+  ...................................................... pinned by definition only
+  (the pages print no worked example of a stack step; the commit, select and
+  per-layer access rules are checked against their restatement, perturbation
+  invariants and the Local = Full identity within s + w)
+* cost.* (attention-only) .............................. pinned (golden ratio,
+  closed forms)
+* cost.DenseShape / decode_flops_ratio / decode_bytes_ratio  pinned to the pages'
+  whole-model 24.26 % to within 0.1 point, under one reading: Qwen3-1.7B's
+  dense sizes (MLP 6144, vocabulary 151936, tied embeddings) are the model's
+  published configuration, not the pages'; also pinned by a loop count of a
+  tiny decoder and by the exact reduction to the attention-only ratio.
 """
 
 from . import attention, cost, gather, keysets, oda, recall  # noqa: F401

@@ -38,6 +38,20 @@ def full_pass(q, k_new, v_new, hist_k, hist_v, n, scale):
     return attention.attend(q, hist_k, hist_v, keysets.full_keys(n), scale)
 
 
+def recall_pass(q, k_new, v_new, hist_k, hist_v, n, scale, local_only, sinks=4, window=2048):
+    """One layer's part of the recall pass under per-layer access control.
+
+    ODA summary page, "Developer perspective", the note on hybrid backbones: the
+    runtime may restrict chosen layers to the Local range. Reading: a layer so
+    restricted attends its Local view in the recall pass too (it never reads past
+    the sinks and the window); the other layers attend the full history. Either way
+    the recall pass's candidate is committed.
+    """
+    if local_only:
+        return local_pass(q, k_new, v_new, hist_k, hist_v, n, scale, sinks, window)
+    return full_pass(q, k_new, v_new, hist_k, hist_v, n, scale)
+
+
 def blocks_pass(q, k_new, v_new, hist_k, hist_v, n, kept_blocks, scale, block_size=16):
     """DA step: commit, then attend the kept blocks only."""
     commit(hist_k, hist_v, n, k_new, v_new)

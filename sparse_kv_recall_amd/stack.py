@@ -9,6 +9,11 @@ ODA step (On-Demand Attention summary page, "Approach"; Figure 1 caption):
 The step never reads the gate on the host, so it can be captured once as a HIP
 graph and replayed ("Developer perspective": one GPU execution flow).
 
+Per-layer access control ("Developer perspective", the note on hybrid backbones: the
+runtime may restrict chosen layers to the Local range): a layer marked local-only runs
+its Local view in step 3 as well, under the same gate, so it never reads beyond the
+sinks and the window; the recall pass's candidate is still the one committed.
+
 Ragged-batch step: a per-request view is chosen on the device from the scores
 (Full when score > theta, else the request's fallback), then the three views are
 launched with selectors, each request being served by exactly one of them.
@@ -27,8 +32,11 @@ class ODAStack:
     """Paged caches of an L-layer attention stack that share block tables and lengths."""
 
     def __init__(self, layers, batch, Hq, Hkv, num_phys_blocks, max_blocks, block_tables, seq_lens,
-                 sinks=4, window=2048, scale=None, device="cuda", separate_outputs=False):
+                 sinks=4, window=2048, scale=None, device="cuda", separate_outputs=False, local_only=()):
         self.layers, self.batch, self.Hq, self.Hkv = layers, batch, Hq, Hkv
+        self.local_only = frozenset(int(l) for l in local_only)
+        if any(l < 0 or l >= layers for l in self.local_only):
+            raise ValueError("local_only names a layer outside [0, %d)" % layers)
         self.sinks, self.window = sinks, window
         self.scale = 1.0 / math.sqrt(ops.HEAD_DIM) if scale is None else scale
         self.seq_lens = seq_lens
@@ -55,10 +63,15 @@ class ODAStack:
         ops.oda_recall_score(x, W1, b1, w2, b2, theta, q_out=self.qscore, gate_out=self.gate, ws=self.ws)
 
     def full_pass(self, q, k, v, gated=True):
+        """The recall pass: Full view per layer, Local view for local-only layers."""
         sel = self.gate if gated else None
         for l in range(self.layers):
-            ops.oda_decode_full(q[l], self.caches[l], k[l], v[l], self.scale, sel=sel, sel_value=1,
-                                out=self.out_full[l], ws=self.ws)
+            if l in self.local_only:
+                ops.oda_decode_local(q[l], self.caches[l], k[l], v[l], self.sinks, self.window, self.scale,
+                                     sel=sel, sel_value=1, out=self.out_full[l], ws=self.ws)
+            else:
+                ops.oda_decode_full(q[l], self.caches[l], k[l], v[l], self.scale, sel=sel, sel_value=1,
+                                    out=self.out_full[l], ws=self.ws)
 
 
 class RaggedBatch:

@@ -68,16 +68,21 @@ class OdaStackRun:
     """ODA stack (Local every step, on-device gate, gated Full) with host mirrors of
     ``check_layers``."""
 
-    def __init__(self, wl, check_layers, steps=None, use_graph=True):
+    def __init__(self, wl, check_layers, steps=None, use_graph=True, local_only=(), same_candidates=False):
         self.wl = wl
         self.steps = wl.steps if steps is None else steps
         self.check_layers = list(check_layers)
         self.use_graph = use_graph
+        self.local_only = frozenset(local_only)
+        # same_candidates: the recall pass is fed the Local pass's q / k / v (what a model
+        # computes when no earlier layer's result changed), instead of its own stream
+        self.rpass = 0 if same_candidates else 1
         H0 = int(wl.H0[0])
         bt = torch.as_tensor(wl.block_tables, device="cuda")
         seq = torch.zeros(1, dtype=torch.int32, device="cuda")
         self.stack = ODAStack(wl.layers, 1, wl.Hq, wl.Hkv, wl.num_phys_blocks, wl.max_blocks, bt, seq,
-                              sinks=wl.sinks, window=wl.window, separate_outputs=True)
+                              sinks=wl.sinks, window=wl.window, separate_outputs=True,
+                              local_only=self.local_only)
         for l in range(wl.layers):
             _fill_history(self.stack.caches[l], wl, l, H0)
         self.recall_head = wl.x_dim > 0
@@ -97,7 +102,8 @@ class OdaStackRun:
             s.gate_from_recall_head(f.x, *self.dev_w, theta=self.wl.theta)
         else:
             s.gate_from_scores(f.scores, self.wl.theta)
-        s.full_pass(f.q[:, 1], f.k[:, 1], f.v[:, 1], gated=True)
+        p = self.rpass
+        s.full_pass(f.q[:, p], f.k[:, p], f.v[:, p], gated=True)
 
     def run(self, full_check_steps=None, check_feed_steps=(0,)):
         wl, rep = self.wl, Report()
@@ -142,13 +148,17 @@ class OdaStackRun:
                 oL = oracle.oda.local_pass(qL, kL, vL, hk, hv, n, SCALE, wl.sinks, wl.window)
                 rep.add(out_l[l, 0], oL, "local t=%d layer=%d" % (t, l))
                 if gate:
-                    qF = wl.cand_q(t, l, 1, 0)
-                    kF, vF = wl.cand_kv(t, l, 1, 0)
+                    qF = wl.cand_q(t, l, self.rpass, 0)
+                    kF, vF = wl.cand_kv(t, l, self.rpass, 0)
                     if full_check_steps is None or t in full_check_steps:
-                        oF = oracle.oda.full_pass(qF, kF, vF, hk, hv, n, SCALE)
-                        rep.add(out_f[l, 0], oF, "full t=%d layer=%d" % (t, l))
+                        oF = oracle.oda.recall_pass(qF, kF, vF, hk, hv, n, SCALE, l in self.local_only,
+                                                    wl.sinks, wl.window)
+                        rep.add(out_f[l, 0], oF, "recall t=%d layer=%d" % (t, l))
                     else:
                         oracle.oda.commit(hk, hv, n, kF, vF)
+                    if self.rpass == 0 and l in self.local_only:
+                        # the same kernel on the same inputs: the recall result is the Local one
+                        assert np.array_equal(out_f[l, 0], out_l[l, 0]), (t, l)
         # committed slots hold the selected candidates, bit for bit
         for l in self.check_layers:
             hk, hv = self.mirror[l]

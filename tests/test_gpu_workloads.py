@@ -65,3 +65,23 @@ def test_ragged32_sampled_requests():
     assert rep.decisions == wl.batch * wl.steps
     print("ragged32: requests %s, full views %d of %d, max-abs %.2e, row-rel %.2e"
           % (check, rep.recalls, rep.decisions, rep.max_abs, rep.max_row_rel))
+
+
+def test_hybrid_local_only_layers():
+    # per-layer access control: three of every four layers restricted to the Local range
+    from tests.harness import OdaStackRun
+    wl = workloads.oda_stack16k(steps=48)
+    local_only = [l for l in range(wl.layers) if l % 4 != 3]
+    rep = OdaStackRun(wl, check_layers=[0, 3, 26, 27], local_only=local_only).run()
+    assert rep.decisions == 48 and rep.recalls > 0
+    print("hybrid: recalls %d/48, max-abs %.2e, row-rel %.2e" % (rep.recalls, rep.max_abs, rep.max_row_rel))
+
+
+def test_all_layers_local_only_equals_local():
+    # with every layer local-only and the recall pass fed what the Local pass saw, the
+    # step's output is the Local output bit for bit, and so are the commits
+    from tests.harness import OdaStackRun
+    wl = workloads.oda_stack16k(steps=24, layers=4)
+    rep = OdaStackRun(wl, check_layers=[0, 1, 2, 3], local_only=range(4), same_candidates=True).run()
+    assert rep.recalls > 0
+    print("all local-only: recalls %d/24, max-abs %.2e" % (rep.recalls, rep.max_abs))

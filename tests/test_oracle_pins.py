@@ -383,6 +383,60 @@ def test_commit_holds_selected_candidate():
         assert out is (o_f if g else o_l)
 
 
+def test_recall_pass_access_control():
+    # NEXT-1 (per-layer access control): a local-only layer's recall pass reads the
+    # sinks and the window only -- perturbing any other position leaves its output
+    # unchanged, perturbing a position inside changes it -- while an unrestricted
+    # layer's recall pass reads everything. Both commit the recall candidate.
+    n, s, w = 40, 2, 6
+    q, k, v = rand_case(n, 4, 2, seed=21)
+    kc, vc = to_bf16_bits(np.full((2, 128), 0.25)), to_bf16_bits(np.full((2, 128), -0.75))
+    inside = set(range(s)) | set(range(n - w, n))
+    outside = [j for j in range(n - 1) if j not in inside]
+    base = {}
+    for lo in (True, False):
+        hk, hv = k.copy(), v.copy()
+        base[lo] = oda.recall_pass(q, kc, vc, hk, hv, n, SCALE, lo, sinks=s, window=w)
+        assert np.array_equal(hk[n - 1], kc) and np.array_equal(hv[n - 1], vc)
+    for j in (outside[0], outside[len(outside) // 2], outside[-1]):
+        hk, hv = k.copy(), v.copy()
+        hk[j] = to_bf16_bits(np.full((2, 128), 3.0))
+        hv[j] = to_bf16_bits(np.full((2, 128), 9.0))
+        o_lo = oda.recall_pass(q, kc, vc, hk.copy(), hv.copy(), n, SCALE, True, sinks=s, window=w)
+        o_full = oda.recall_pass(q, kc, vc, hk.copy(), hv.copy(), n, SCALE, False, sinks=s, window=w)
+        assert np.array_equal(o_lo, base[True])
+        assert np.abs(o_full - base[False]).max() > 1e-3
+    for j in (0, n - w, n - 2):
+        hk, hv = k.copy(), v.copy()
+        hv[j] = to_bf16_bits(np.full((2, 128), 9.0))
+        o_lo = oda.recall_pass(q, kc, vc, hk, hv, n, SCALE, True, sinks=s, window=w)
+        assert np.abs(o_lo - base[True]).max() > 1e-3
+    # history within s + w: both restrictions read the same positions
+    m = s + w
+    hk, hv = k.copy(), v.copy()
+    o_lo = oda.recall_pass(q, kc, vc, hk, hv, m, SCALE, True, sinks=s, window=w)
+    o_full = oda.recall_pass(q, kc, vc, hk, hv, m, SCALE, False, sinks=s, window=w)
+    assert np.allclose(o_lo, o_full, rtol=0, atol=1e-14)
+
+
+def test_all_layers_local_only_equals_local():
+    # NEXT-1 test from the scope table: with every layer local-only, an ODA step
+    # that recalls gives the Local result and commits the same candidate, layer by
+    # layer, when the recall pass sees the candidates the Local pass saw (as it does
+    # in a model, where every earlier layer then computes the same thing).
+    n, L = 3000, 3
+    for lay in range(L):
+        q, k, v = rand_case(n, 4, 2, seed=30 + lay)
+        kc, vc = to_bf16_bits(np.full((2, 128), 0.5)), to_bf16_bits(np.full((2, 128), 0.125))
+        hk1, hv1 = k.copy(), v.copy()
+        o_local = oda.local_pass(q, kc, vc, hk1, hv1, n, SCALE)
+        hk2, hv2 = k.copy(), v.copy()
+        o_l2 = oda.local_pass(q, kc, vc, hk2, hv2, n, SCALE)
+        o_rec = oda.recall_pass(q, kc, vc, hk2, hv2, n, SCALE, True)
+        assert np.array_equal(oda.select(True, o_l2, o_rec), o_local)
+        assert np.array_equal(hk1, hk2) and np.array_equal(hv1, hv2)
+
+
 def test_request_mode():
     assert oda.request_mode(0.1, 0.0, oda.MODE_LOCAL) == oda.MODE_FULL
     assert oda.request_mode(0.0, 0.0, oda.MODE_BLOCKS) == oda.MODE_BLOCKS
@@ -410,3 +464,83 @@ def test_cost_counters():
     assert cost.kv_bytes(131072, 8, 128) == 131072 * 4096
     assert cost.kv_bytes(2052, 2, 128) == 2052 * 1024
     assert cost.attention_flops(10, 32, 128) == 4 * 32 * 128 * 10
+
+
+# ---------------------------------------------------------------- whole-model accounting (NEXT-4)
+
+# Qwen3-1.7B's dense sizes: 28 layers, hidden 2048, 16 q / 8 kv heads of 128 (the pages'
+# workload shape), gated MLP of 6144 and a 151936-token vocabulary with tied embeddings
+# (the model's published configuration; the pages do not print them). Recall head: the
+# ODA summary page's 28,325,889 parameters.
+QWEN3_1_7B = dict(layers=28, hidden=2048, q_heads=16, kv_heads=8, head_dim=128, intermediate=6144,
+                  vocab=151936, recall_params=28325889)
+
+
+def _page_setting():
+    # 128K input (131072 positions), 1K output steps, one step in eight recalls
+    ns = [131072 + 1 + t for t in range(1024)]
+    flags = [t % 8 == 7 for t in range(1024)]
+    return ns, flags
+
+
+def test_whole_model_flops_reproduce_page_figure():
+    # ODA summary page, "Main results": 24.26 % of always-Full decode FLOPs
+    m = cost.DenseShape(**QWEN3_1_7B)
+    ns, flags = _page_setting()
+    r = float(cost.decode_flops_ratio(m, ns, flags))
+    print("whole-model ODA / Full decode FLOPs: %.4f %% (page: 24.26 %%)" % (100 * r))
+    assert abs(100 * r - 24.26) < 0.1
+    # attention alone would give much less: the dense terms are what the figure adds
+    assert float(cost.oda_over_full(ns, flags)) < 0.15 < r
+    # the shape has the size its name says
+    assert abs(m.params() / 1.7e9 - 1) < 0.03
+
+
+def test_whole_model_accounting_reduces_to_attention_only():
+    # with no dense weights and no recall head the whole-model ratio is the
+    # attention-only one, exactly (any double-counted or missing pass breaks this)
+    m = cost.DenseShape(layers=3, hidden=0, q_heads=4, kv_heads=2, head_dim=128, intermediate=0, vocab=0)
+    for ns, flags in (([5000, 5001, 5002], [False, True, False]), ([100, 3000], [True, True]), _page_setting()):
+        assert cost.decode_flops_ratio(m, ns, flags) == cost.oda_over_full(ns, flags)
+
+
+def test_whole_model_flops_brute_force():
+    # count multiply-adds of a tiny decoder's forward pass with explicit loops
+    m = cost.DenseShape(layers=2, hidden=6, q_heads=2, kv_heads=1, head_dim=3, intermediate=5, vocab=7)
+    macs = 0
+
+    def matvec(rows, cols):
+        nonlocal macs
+        for _ in range(rows):
+            for _ in range(cols):
+                macs += 1
+
+    keys = 9
+    for _ in range(m.layers):
+        matvec(m.q_heads * m.head_dim, m.hidden)        # q
+        matvec(m.kv_heads * m.head_dim, m.hidden)       # k
+        matvec(m.kv_heads * m.head_dim, m.hidden)       # v
+        for _ in range(m.q_heads):
+            matvec(keys, m.head_dim)                    # scores
+            matvec(m.head_dim, keys)                    # weighted values
+        matvec(m.hidden, m.q_heads * m.head_dim)        # o
+        matvec(m.intermediate, m.hidden)                # gate
+        matvec(m.intermediate, m.hidden)                # up
+        matvec(m.hidden, m.intermediate)                # down
+    matvec(m.vocab, m.hidden)                           # LM head
+    assert 2 * macs == cost.step_flops_full(m, keys)
+    # an ODA step that recalls costs a Local step, the head and a Full step
+    m.recall_params = 11
+    n = 5000
+    assert (cost.step_flops_oda(m, n, True) - cost.step_flops_oda(m, n, False)) == cost.step_flops_full(m, n)
+    assert cost.step_flops_oda(m, n, False) == cost.step_flops_full(m, cost.local_size(n)) + 22
+
+
+def test_whole_model_bytes_bound_the_page_speedup():
+    # ODA summary page, "Main results": 75.54 -> 149.52 tokens/s (1.98x) in vLLM. A
+    # bandwidth-bound decoder cannot beat the ratio of bytes moved per token.
+    m = cost.DenseShape(**QWEN3_1_7B)
+    ns, flags = _page_setting()
+    bound = float(cost.decode_bytes_ratio(m, ns, flags))
+    print("always-Full / ODA bytes per token: %.3f (page's measured speedup 1.98)" % bound)
+    assert 149.52 / 75.54 < bound < 1 / float(cost.oda_over_full(ns, flags))
