@@ -259,6 +259,57 @@ def always_full_rate(stack, feeder, wl, steps):
     return {"steps": steps, "tok_s": round(steps * wl.batch / (ms / 1e3), 2), "ms_per_step": round(ms / steps, 4)}
 
 
+def da_tags_rate(device, reps=2):
+    """Declaration-driven DA decode at 32K (the ``da_tags_32k`` workload): per step the
+    input token advances the device parser (declaration + keep mask), then the kept
+    blocks are gathered and attended. Returns the average step time over the 512 steps."""
+    import torch
+    from sparse_kv_recall_amd import ops
+    from sparse_kv_recall_amd.stack import DATagStep, capture_graph
+    from synth import device as sdev
+    from synth import workloads
+    from synth.workloads import C_KHIST, C_VHIST
+
+    wl = workloads.da_tags_32k()
+    H0 = int(wl.H0[0])
+    seq = torch.zeros(1, dtype=torch.int32, device=device)
+    cache = ops.PagedKVCache(wl.num_phys_blocks, 1, wl.Hq, wl.Hkv, wl.max_blocks,
+                             block_tables=torch.as_tensor(wl.block_tables, device=device), seq_lens=seq)
+    stage_k = torch.empty((H0, wl.Hkv, 128), dtype=torch.bfloat16, device=device)
+    stage_v = torch.empty_like(stage_k)
+    sdev.fill_normal_(stage_k, wl.key(C_KHIST, 0), 0)
+    sdev.fill_normal_(stage_v, wl.key(C_VHIST, 0), 0)
+    ops.kv_write(cache, 0, 0, stage_k, stage_v)
+    da = DATagStep(cache, wl.da_tags, torch.as_tensor(wl.output_begin, device=device),
+                   segments=torch.as_tensor(wl.segments, device=device), local_tokens=wl.da_local_tokens)
+    feeder = sdev.Feeder(wl, seq, device=device, with_tokens=True)
+
+    def step():
+        feeder.step()
+        da.step(feeder.q[0, 0], feeder.k[0, 0], feeder.v[0, 0], feeder.tokens)
+
+    graph = capture_graph(step)
+    graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    best = None
+    for _ in range(reps):
+        feeder.set_step(0)
+        da.state.zero_()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(wl.steps):
+            graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        best = ms if best is None else min(best, ms)
+    del graph
+    return {"workload": "da_tags_32k: 1 layer, 32 q / 8 kv heads, context 32768 + 512 steps, declarations "
+                        "parsed on the device from a seeded token stream", "steps": wl.steps,
+            "us_per_step": round(best * 1e3 / wl.steps, 2)}
+
+
 def hybrid_rate(stack, feeder, wl, steps):
     """Decode rate of the same workload with per-layer access control: three of every
     four layers restricted to the Local range (their recall pass runs the Local view).
@@ -351,6 +402,8 @@ def main():
     log("always-Full baseline: %s" % json.dumps(full_only))
     hybrid = hybrid_rate(stack, feeder, wl, min(256, args.steps))
     log("hybrid access control: %s" % json.dumps(hybrid))
+    da_tags = da_tags_rate(device)
+    log("declaration-driven DA step: %s" % json.dumps(da_tags))
     traffic = profiled_traffic(bytes_full)
     traffic = None if traffic is None else int(round(traffic))
     copy_calibration(device)
@@ -390,6 +443,7 @@ def main():
         "always_full_baseline": dict(full_only, speedup_of_oda=round(tok_s / full_only["tok_s"], 3),
                                      attention_bytes_ratio=round(float(full_bytes / step_bytes), 3)),
         "hybrid_local_only": hybrid,
+        "da_declared_step": da_tags,
         "step_hbm_gbs": round(float(step_gbs), 1),
         "wall_s_timed": round(wall, 3),
     }

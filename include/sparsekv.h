@@ -214,6 +214,42 @@ int oda_gate_scores(const float* scores, int32_t batch, float theta,
 int da_keep_mask(const int32_t* decl, sk_paged_kv kv, int32_t local_tokens,
                  uint32_t* keep_mask, hipStream_t stream);
 
+/* Token ids of the mode tags ([DA] review page, section 1 "Key Terms"; chatpaper
+ * abstract: the model writes <global>, <focus> and <local> into its chain of
+ * thought, and a focus names one context segment, a "Magic Chunk"). Token
+ * segment_base + k names segment k. The ids are the caller's tokenizer's. */
+typedef struct sk_da_tags {
+  int32_t global_tag;
+  int32_t focus_tag;
+  int32_t local_tag;
+  int32_t segment_base;
+} sk_da_tags;
+
+/* Declaration parsing ([DA] section 3 and the chatpaper abstract: the engine
+ * reads the declarations from the generated text like tool calls and derives
+ * the attention mask). For every request b, this step's input token tokens[b]
+ * advances a parser whose state persists in `state` (int32 [batch][4] =
+ * {mode, focus_begin_block, focus_end_block, focus_pending}; initialise to
+ * {SK_DA_GLOBAL, 0, 0, 0}):
+ *   global_tag -> mode SK_DA_GLOBAL;   local_tag -> mode SK_DA_LOCAL
+ *   (either clears a pending focus);   focus_tag -> focus pending (mode kept);
+ *   any other token while a focus is pending clears it, and if it names
+ *   segment k < num_segments the mode becomes SK_DA_FOCUS on that segment:
+ *     [begin, end) = segments[b][k] (int32 [batch][num_segments][2], context
+ *     positions) -> blocks [begin/16, ceil(end/16)), empty when end <= begin;
+ *   any other token changes nothing.
+ * The new mode applies to this very step (its input token is already parsed).
+ * Then decl[b] = {mode, focus_begin_block, focus_end_block, output_begin[b]}
+ * (the row da_keep_mask reads; output_begin: int32 [batch], the first logical
+ * block of the model's own output) and keep_mask row b is written exactly as
+ * da_keep_mask writes it. One workgroup per request; segments may be NULL
+ * when num_segments == 0. Host-checked: pointers, num_segments >= 0,
+ * local_tokens >= 0, the paged-KV description. */
+int da_declare(const int32_t* tokens, int32_t* state, const int32_t* segments,
+               int32_t num_segments, const int32_t* output_begin, sk_da_tags tags,
+               sk_paged_kv kv, int32_t local_tokens, int32_t* decl,
+               uint32_t* keep_mask, hipStream_t stream);
+
 /* Block-table rewrite plus attention over the kept blocks ([DA] section 3).
  * For every selected request b, the kept logical blocks (bits of keep_mask
  * row b below ceil(n/16)) are compacted in ascending logical order into

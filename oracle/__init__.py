@@ -29,6 +29,9 @@ Parity status of each function (pinned by the ``-m "not gpu"`` tests):
 * attention.attend ..................................... pinned
 * recall.recall_score / recall.gate .................... pinned
 * gather.gather_blocks / gather.da_mode_blocks ......... pinned
+* declare.parse_declarations ........................... pinned by a hand-worked
+  token stream (the pages print none) and by an independent backward-scan
+  formulation on seeded streams
 * oda.local_pass / full_pass / blocks_pass / recall_pass / select / request_mode
   ...................................................... pinned by definition only
   (the pages print no worked example of a stack step; the commit, select and
@@ -43,5 +46,5 @@ Parity status of each function (pinned by the ``-m "not gpu"`` tests):
   tiny decoder and by the exact reduction to the attention-only ratio.
 """
 
-from . import attention, cost, gather, keysets, oda, recall  # noqa: F401
+from . import attention, cost, declare, gather, keysets, oda, recall  # noqa: F401
 from .bf16 import bf16_bits_to_f64  # noqa: F401

@@ -25,6 +25,12 @@ class PagedKVStruct(ctypes.Structure):
                 ("max_blocks", c_int32), ("num_phys_blocks", c_int64)]
 
 
+class DaTagsStruct(ctypes.Structure):
+    """Mirror of ``sk_da_tags`` in include/sparsekv.h."""
+    _fields_ = [("global_tag", c_int32), ("focus_tag", c_int32), ("local_tag", c_int32),
+                ("segment_base", c_int32)]
+
+
 _SIGNATURES = {
     "sk_workspace_bytes": (c_size_t, [c_int32, c_int32]),
     "sk_workspace_init": (c_int32, [c_void_p, c_size_t, c_void_p]),
@@ -41,6 +47,8 @@ _SIGNATURES = {
                                    c_float, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
     "oda_gate_scores": (c_int32, [c_void_p, c_int32, c_float, c_void_p, c_void_p, c_void_p]),
     "da_keep_mask": (c_int32, [c_void_p, PagedKVStruct, c_int32, c_void_p, c_void_p]),
+    "da_declare": (c_int32, [c_void_p, c_void_p, c_void_p, c_int32, c_void_p, DaTagsStruct, PagedKVStruct, c_int32,
+                             c_void_p, c_void_p, c_void_p]),
     "da_decode_blocks": (c_int32, [c_void_p, PagedKVStruct, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                    c_void_p, c_float, c_void_p, c_int32, c_void_p, c_void_p, c_size_t, c_void_p]),
 }

@@ -100,19 +100,12 @@ __global__ void gate_scores_kernel(const float* __restrict__ scores, int B, floa
   if (b < B) out[b] = (scores[b] > theta) ? 1 : (fallback ? fallback[b] : 0);
 }
 
-__global__ void keep_mask_kernel(const int32_t* __restrict__ decl, sk_paged_kv kv, int local_tokens,
-                                 uint32_t* __restrict__ mask) {
-  const int words_row = (kv.max_blocks + 31) / 32;
-  int64_t gid = blockIdx.x * int64_t(blockDim.x) + threadIdx.x;
-  if (gid >= int64_t(kv.batch) * words_row) return;
-  const int b = int(gid / words_row), w = int(gid % words_row);
-  const int n = kv.seq_lens[b];
-  const int nb = (n >= 1 && n <= kv.max_blocks * kBlock) ? (n + kBlock - 1) / kBlock : 0;
-  const int mode = decl[4 * b], fb = decl[4 * b + 1], fe = decl[4 * b + 2], ob = decl[4 * b + 3];
-  const int first_local = (n > local_tokens ? n - local_tokens : 0) / kBlock;
+// Bits of mask word w of one request: block blk is kept when it holds a visible position
+// (blk < nb) and the declared mode keeps it.
+__device__ inline uint32_t keep_word(int mode, int fb, int fe, int ob, int first_local, int nb, int w) {
   uint32_t bits = 0u;
   for (int i = 0; i < 32; ++i) {
-    int blk = 32 * w + i;
+    const int blk = 32 * w + i;
     bool keep = false;
     if (blk < nb) {
       if (mode == SK_DA_GLOBAL) keep = true;
@@ -121,7 +114,78 @@ __global__ void keep_mask_kernel(const int32_t* __restrict__ decl, sk_paged_kv k
     }
     bits |= uint32_t(keep) << i;
   }
-  mask[gid] = bits;
+  return bits;
+}
+
+__device__ inline int visible_blocks(const sk_paged_kv& kv, int n) {
+  return (n >= 1 && n <= kv.max_blocks * kBlock) ? (n + kBlock - 1) / kBlock : 0;
+}
+
+__global__ void keep_mask_kernel(const int32_t* __restrict__ decl, sk_paged_kv kv, int local_tokens,
+                                 uint32_t* __restrict__ mask) {
+  const int words_row = (kv.max_blocks + 31) / 32;
+  int64_t gid = blockIdx.x * int64_t(blockDim.x) + threadIdx.x;
+  if (gid >= int64_t(kv.batch) * words_row) return;
+  const int b = int(gid / words_row), w = int(gid % words_row);
+  const int n = kv.seq_lens[b];
+  const int first_local = (n > local_tokens ? n - local_tokens : 0) / kBlock;
+  mask[gid] = keep_word(decl[4 * b], decl[4 * b + 1], decl[4 * b + 2], decl[4 * b + 3], first_local,
+                        visible_blocks(kv, n), w);
+}
+
+// One workgroup per request: thread 0 advances the request's declaration parser by this
+// step's token, then the workgroup writes the keep mask of the new declaration.
+__global__ __launch_bounds__(256) void declare_kernel(const int32_t* __restrict__ tokens, int32_t* __restrict__ state,
+                                                      const int32_t* __restrict__ segments, int num_segments,
+                                                      const int32_t* __restrict__ output_begin, sk_da_tags tags,
+                                                      sk_paged_kv kv, int local_tokens, int32_t* __restrict__ decl,
+                                                      uint32_t* __restrict__ mask) {
+  __shared__ int s_decl[4];
+  const int b = blockIdx.x;
+  if (threadIdx.x == 0) {
+    int* st = state + 4 * b;
+    int mode = st[0], fb = st[1], fe = st[2], pending = st[3];
+    const int tok = tokens[b];
+    if (tok == tags.global_tag) {
+      mode = SK_DA_GLOBAL;
+      pending = 0;
+    } else if (tok == tags.local_tag) {
+      mode = SK_DA_LOCAL;
+      pending = 0;
+    } else if (tok == tags.focus_tag) {
+      pending = 1;
+    } else if (pending) {
+      pending = 0;
+      const int64_t k = int64_t(tok) - tags.segment_base;
+      if (k >= 0 && k < num_segments) {
+        const int64_t e = (int64_t(b) * num_segments + k) * 2;
+        const int begin = max(segments[e], 0), end = segments[e + 1];
+        mode = SK_DA_FOCUS;
+        fb = begin / kBlock;
+        fe = (end > begin) ? (end + kBlock - 1) / kBlock : fb;
+      }
+    }
+    st[0] = mode;
+    st[1] = fb;
+    st[2] = fe;
+    st[3] = pending;
+    const int ob = output_begin[b];
+    decl[4 * b] = mode;
+    decl[4 * b + 1] = fb;
+    decl[4 * b + 2] = fe;
+    decl[4 * b + 3] = ob;
+    s_decl[0] = mode;
+    s_decl[1] = fb;
+    s_decl[2] = fe;
+    s_decl[3] = ob;
+  }
+  __syncthreads();
+  const int words_row = (kv.max_blocks + 31) / 32;
+  const int n = kv.seq_lens[b];
+  const int first_local = (n > local_tokens ? n - local_tokens : 0) / kBlock;
+  const int nb = visible_blocks(kv, n);
+  for (int w = threadIdx.x; w < words_row; w += blockDim.x)
+    mask[int64_t(b) * words_row + w] = keep_word(s_decl[0], s_decl[1], s_decl[2], s_decl[3], first_local, nb, w);
 }
 
 template <int CHUNKS>
@@ -175,6 +239,19 @@ int da_keep_mask(const int32_t* decl, sk_paged_kv kv, int32_t local_tokens, uint
   int64_t threads = int64_t(kv.batch) * ((kv.max_blocks + 31) / 32);
   hipLaunchKernelGGL(keep_mask_kernel, dim3(unsigned((threads + 255) / 256)), dim3(256), 0, stream, decl, kv,
                      local_tokens, keep_mask);
+  return launch_status(hipGetLastError());
+}
+
+int da_declare(const int32_t* tokens, int32_t* state, const int32_t* segments, int32_t num_segments,
+               const int32_t* output_begin, sk_da_tags tags, sk_paged_kv kv, int32_t local_tokens, int32_t* decl,
+               uint32_t* keep_mask, hipStream_t stream) {
+  int st = check_kv(kv);
+  if (st) return st;
+  if (!tokens || !state || !output_begin || !decl || !keep_mask) return SK_E_NULL;
+  if (num_segments < 0 || local_tokens < 0) return SK_E_RANGE;
+  if (num_segments > 0 && !segments) return SK_E_NULL;
+  hipLaunchKernelGGL(declare_kernel, dim3(unsigned(kv.batch)), dim3(256), 0, stream, tokens, state, segments,
+                     num_segments, output_begin, tags, kv, local_tokens, decl, keep_mask);
   return launch_status(hipGetLastError());
 }
 

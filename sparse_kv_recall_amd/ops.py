@@ -194,6 +194,35 @@ def da_keep_mask(decl, kv, local_tokens=1024, mask=None):
     return mask
 
 
+def da_declare(tokens, state, output_begin, kv, tags, segments=None, local_tokens=1024, decl=None, mask=None):
+    """Advance each request's declaration parser by this step's token and write the
+    step's declaration and keep mask. tokens: int32 [B]; state: int32 [B][4]
+    (persistent, start {DA_GLOBAL, 0, 0, 0}); output_begin: int32 [B]; tags:
+    (global, focus, local, segment_base) token ids; segments: int32 [B][S][2] or None."""
+    B = kv.batch
+    words = (kv.max_blocks + 31) // 32
+    _check(tokens, torch.int32, "tokens", B)
+    _check(state, torch.int32, "state", B * 4)
+    _check(output_begin, torch.int32, "output_begin", B)
+    nseg = 0
+    if segments is not None:
+        if segments.dim() != 3 or segments.shape[0] != B or segments.shape[2] != 2:
+            raise ValueError("segments must be int32 [batch][num_segments][2]")
+        _check(segments, torch.int32, "segments", segments.numel())
+        nseg = int(segments.shape[1])
+    if decl is None:
+        decl = torch.empty((B, 4), dtype=torch.int32, device=tokens.device)
+    _check(decl, torch.int32, "decl", B * 4)
+    if mask is None:
+        mask = torch.empty((B, words), dtype=torch.int32, device=tokens.device)
+    _check(mask, torch.int32, "mask", B * words)
+    t = _lib.DaTagsStruct(*(int(x) for x in tags))
+    _lib.call("da_declare", tokens.data_ptr(), state.data_ptr(), 0 if segments is None else segments.data_ptr(),
+              nseg, output_begin.data_ptr(), t, kv.abi(), int(local_tokens), decl.data_ptr(), mask.data_ptr(),
+              _stream(tokens.device))
+    return decl, mask
+
+
 def da_decode_blocks(q, kv, keep_mask, k_new=None, v_new=None, scale=None, sel=None, sel_value=MODE_BLOCKS,
                      out=None, gathered=None, gathered_cnt=None, num_kept=None, ws=None):
     out, ws = _decode_common(q, kv, k_new, v_new, sel, out, ws)

@@ -124,6 +124,27 @@ class DAStep:
                              gathered_cnt=self.gathered_cnt, num_kept=self.num_kept, ws=self.ws)
 
 
+class DATagStep(DAStep):
+    """One attention layer whose declarations come from the generated tokens: each step
+    the input token advances the per-request parser (mode tags, named segments), which
+    writes the step's declaration and keep mask, then the kept blocks are attended."""
+
+    def __init__(self, cache, tags, output_begin, segments=None, local_tokens=1024, scale=None, device="cuda"):
+        super().__init__(cache, local_tokens, scale, device)
+        B = cache.batch
+        self.tags = tuple(int(x) for x in tags)
+        self.output_begin = output_begin
+        self.segments = segments
+        self.state = torch.zeros((B, 4), dtype=torch.int32, device=device)  # {global, 0, 0, no focus pending}
+        self.decl = torch.zeros((B, 4), dtype=torch.int32, device=device)
+
+    def step(self, q, k, v, tokens):
+        ops.da_declare(tokens, self.state, self.output_begin, self.cache, self.tags, segments=self.segments,
+                       local_tokens=self.local_tokens, decl=self.decl, mask=self.mask)
+        ops.da_decode_blocks(q, self.cache, self.mask, k, v, self.scale, out=self.out, gathered=self.gathered,
+                             gathered_cnt=self.gathered_cnt, num_kept=self.num_kept, ws=self.ws)
+
+
 def capture_graph(fn):
     """Capture the launches made by fn() into a HIP graph (replayed with .replay())."""
     g = torch.cuda.CUDAGraph()

@@ -54,6 +54,8 @@ struct FeedParams {
   float* score_out;   // [B] or null
   const int32_t* decl_table;  // [num_steps][B][4] or null
   int32_t* decl_out;  // [B][4]
+  const int32_t* token_table;  // [num_steps][B] or null
+  int32_t* token_out;  // [B]
 };
 
 // Element indices stay below 2^31 for every workload here (the host checks), so the
@@ -100,6 +102,7 @@ __global__ __launch_bounds__(256) void feed_kernel(FeedParams F) {
                                  : normal_at(F.key_score, uint64_t(int64_t(t) * F.B + b), F.scale);
       if (F.decl_out)
         for (int k = 0; k < 4; ++k) F.decl_out[4 * b + k] = F.decl_table[(int64_t(t) * F.B + b) * 4 + k];
+      if (F.token_out) F.token_out[b] = F.token_table[int64_t(t) * F.B + b];
     }
   }
   // every block has read state[0] above; the last block to arrive advances the step
@@ -143,11 +146,12 @@ int synth_fill_bf16(uint16_t* out, int64_t count, uint64_t key, int64_t index0, 
 int synth_feed(int32_t* state, int32_t* seq_lens, const int32_t* H0, int B, int L, int P, int Hq, int Hkv,
                int num_steps, uint64_t key_q, uint64_t key_k, uint64_t key_v, uint64_t key_x, uint64_t key_score,
                float scale, float* q_out, uint16_t* k_out, uint16_t* v_out, int x_dim, float* x_out,
-               const float* sched, float* score_out, const int32_t* decl_table, int32_t* decl_out, hipStream_t s) {
+               const float* sched, float* score_out, const int32_t* decl_table, int32_t* decl_out,
+               const int32_t* token_table, int32_t* token_out, hipStream_t s) {
   const int64_t total = int64_t(L) * P * B * (Hq + Hkv) * 128 + (x_out ? int64_t(B) * x_dim : 0) + B;
   if (total >= (int64_t(1) << 31) || B < 1 || num_steps < 1) return -4;
   FeedParams F{state, seq_lens, H0, B, L, P, Hq, Hkv, num_steps, key_q, key_k, key_v, key_x, key_score, scale,
-               q_out, k_out, v_out, x_dim, x_out, sched, score_out, decl_table, decl_out};
+               q_out, k_out, v_out, x_dim, x_out, sched, score_out, decl_table, decl_out, token_table, token_out};
   int64_t blocks = (total + 255) / 256;
   if (blocks > 256) blocks = 256;
   hipLaunchKernelGGL(feed_kernel, dim3(unsigned(blocks)), dim3(256), 0, s, F);

@@ -26,7 +26,7 @@ def load():
         lib.synth_fill_f32.argtypes = [vp, i64, u64, i64, f32, vp]
         lib.synth_fill_bf16.argtypes = [vp, i64, u64, i64, f32, vp]
         lib.synth_feed.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, u64, u64, u64, u64, u64, f32,
-                                   vp, vp, vp, i32, vp, vp, vp, vp, vp, vp]
+                                   vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp]
         lib.synth_set_step.argtypes = [vp, i32, vp]
         for f in (lib.synth_fill_f32, lib.synth_fill_bf16, lib.synth_feed, lib.synth_set_step):
             f.restype = i32
@@ -64,7 +64,8 @@ class Feeder:
     a HIP graph and replayed every step.
     """
 
-    def __init__(self, wl, seq_lens, device="cuda", with_x=False, with_scores=False, with_decl=False):
+    def __init__(self, wl, seq_lens, device="cuda", with_x=False, with_scores=False, with_decl=False,
+                 with_tokens=False):
         self.wl = wl
         dev = torch.device(device)
         L, P, B = wl.layers, wl.passes, wl.batch
@@ -80,6 +81,8 @@ class Feeder:
                       if (with_scores and wl.sched_scores is not None) else None)
         self.decl_table = (torch.as_tensor(wl.decl.astype(np.int32), device=dev) if with_decl else None)
         self.decl = torch.empty((B, 4), dtype=torch.int32, device=dev) if with_decl else None
+        self.token_table = (torch.as_tensor(wl.tokens.astype(np.int32), device=dev) if with_tokens else None)
+        self.tokens = torch.empty(B, dtype=torch.int32, device=dev) if with_tokens else None
 
     def _p(self, t):
         return 0 if t is None else t.data_ptr()
@@ -91,7 +94,8 @@ class Feeder:
                               wl.key(C_V), wl.key(C_X), wl.key(C_SCORE), float(rng.unit_scale()),
                               self.q.data_ptr(), self.k.data_ptr(), self.v.data_ptr(), wl.x_dim,
                               self._p(self.x), self._p(self.sched), self._p(self.scores), self._p(self.decl_table),
-                              self._p(self.decl), _stream(self.state)), "synth_feed")
+                              self._p(self.decl), self._p(self.token_table), self._p(self.tokens),
+                              _stream(self.state)), "synth_feed")
 
     def set_step(self, t):
         _ok(load().synth_set_step(self.state.data_ptr(), int(t), _stream(self.state)), "synth_set_step")

@@ -21,6 +21,10 @@ distributions are kept):
    keep-list of 5-20 % of its blocks plus every block from the one holding
    position L_r onwards).
 
+A sixth, ``da_tags_32k``, is ``da_32k``'s shape with the declarations parsed from
+a seeded token stream (mode tags, 16 named segments of the prompt) instead of
+drawn per step.
+
 Conventions: history positions 0 .. H0-1 are synthetic; at step t (0-based)
 the request has n = H0 + t + 1 visible positions and the current token sits at
 position H0 + t. Large arrays come from ``synth.rng`` streams keyed by
@@ -46,7 +50,10 @@ BLOCK = 16
 
 # component ids of the stream keys
 C_KHIST, C_VHIST, C_Q, C_K, C_V, C_X, C_W1, C_W2, C_SCORE = 1, 2, 3, 4, 5, 6, 7, 8, 9
-C_SCHED, C_PERM, C_LEN, C_FALLBACK, C_KEEP, C_MODE = 20, 21, 22, 23, 24, 25
+C_SCHED, C_PERM, C_LEN, C_FALLBACK, C_KEEP, C_MODE, C_TOKENS, C_SEGMENTS = 20, 21, 22, 23, 24, 25, 26, 27
+
+# token ids of the declaration tags in the synthetic vocabulary
+TAG_GLOBAL, TAG_FOCUS, TAG_LOCAL, TAG_SEGMENT_BASE = 5, 6, 7, 100
 
 # per-request views of a ragged batch (same numbers as the C header)
 MODE_LOCAL, MODE_FULL, MODE_BLOCKS = 0, 1, 2
@@ -80,6 +87,10 @@ class Workload:
     da_local_tokens: int = 1024
     fallback: np.ndarray = None       # [batch] int32 (ragged batch)
     keep_mask: np.ndarray = None      # [batch][words] uint32 fixed keep-lists (ragged batch)
+    tokens: np.ndarray = None         # [steps][batch] int32 input token per step (declaration stream)
+    segments: np.ndarray = None       # [batch][S][2] int32 named context segments [begin, end)
+    output_begin: np.ndarray = None   # [batch] int32 first logical block of the model's output
+    da_tags: tuple = None             # (global, focus, local, segment_base) token ids
     extra: dict = field(default_factory=dict)
 
     @property
@@ -201,6 +212,49 @@ def da_32k(steps=512, prompt_blocks=1984, output_blocks=64, focus_blocks=128, lo
     return Workload(wid, "da_32k", layers=1, batch=1, Hq=32, Hkv=8, steps=steps, passes=1,
                     H0=np.array([H0], np.int64), block_tables=perm[None, :], num_phys_blocks=mb,
                     decl=decl, da_local_tokens=local_tokens,
+                    extra=dict(prompt_blocks=prompt_blocks))
+
+
+def da_tags_32k(steps=512, prompt_blocks=1984, output_blocks=64, num_segments=16, local_tokens=1024,
+                tag_rate=0.06):
+    """The ``da_32k`` shape driven by a declaration stream: 16 named segments ("Magic
+    Chunks") of 256-4096 positions at seeded, block-unaligned offsets of the prompt;
+    per step the input token is a mode tag with probability ``tag_rate`` (global,
+    focus, local equally likely), a focus tag is followed by a segment token (a valid
+    segment with probability 0.85, else an out-of-range segment id or an ordinary
+    token), and ordinary tokens are uniform in [1000, 50000)."""
+    wid = 6
+    H0 = (prompt_blocks + output_blocks) * BLOCK
+    mb = _blocks_for(H0 + steps)
+    perm = np_rng(wid, C_PERM).permutation(mb).astype(np.int32)
+    g = np_rng(wid, C_SEGMENTS)
+    lens = g.integers(256, 4097, size=num_segments)
+    begins = g.integers(0, prompt_blocks * BLOCK - 4096, size=num_segments)
+    segments = np.stack([begins, begins + lens], axis=1).astype(np.int32)[None]
+    g = np_rng(wid, C_TOKENS)
+    tokens = np.zeros((steps, 1), np.int32)
+    t = 0
+    while t < steps:
+        if g.random() < tag_rate:
+            tag = (TAG_GLOBAL, TAG_FOCUS, TAG_LOCAL)[int(g.integers(0, 3))]
+            tokens[t, 0] = tag
+            if tag == TAG_FOCUS and t + 1 < steps:
+                t += 1
+                u = g.random()
+                if u < 0.85:
+                    tokens[t, 0] = TAG_SEGMENT_BASE + int(g.integers(0, num_segments))
+                elif u < 0.95:
+                    tokens[t, 0] = TAG_SEGMENT_BASE + num_segments + int(g.integers(0, 4))
+                else:
+                    tokens[t, 0] = int(g.integers(1000, 50000))
+        else:
+            tokens[t, 0] = int(g.integers(1000, 50000))
+        t += 1
+    return Workload(wid, "da_tags_32k", layers=1, batch=1, Hq=32, Hkv=8, steps=steps, passes=1,
+                    H0=np.array([H0], np.int64), block_tables=perm[None, :], num_phys_blocks=mb,
+                    da_local_tokens=local_tokens, tokens=tokens, segments=segments,
+                    output_begin=np.array([prompt_blocks], np.int32),
+                    da_tags=(TAG_GLOBAL, TAG_FOCUS, TAG_LOCAL, TAG_SEGMENT_BASE),
                     extra=dict(prompt_blocks=prompt_blocks))
 
 

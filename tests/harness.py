@@ -224,6 +224,70 @@ class DaRun:
         return rep
 
 
+class DaTagsRun:
+    """Declarative-Attention layer driven by a token stream: per step the input token
+    advances the device parser (checked against the oracle parser: state and
+    declaration bit for bit), then keep mask -> gathered list -> attention."""
+
+    def __init__(self, wl, steps=None, use_graph=True):
+        from sparse_kv_recall_amd.stack import DATagStep
+        self.wl = wl
+        self.steps = wl.steps if steps is None else steps
+        H0 = int(wl.H0[0])
+        bt = torch.as_tensor(wl.block_tables, device="cuda")
+        seq = torch.zeros(1, dtype=torch.int32, device="cuda")
+        self.cache = ops.PagedKVCache(wl.num_phys_blocks, 1, wl.Hq, wl.Hkv, wl.max_blocks, block_tables=bt,
+                                      seq_lens=seq)
+        self.cache.k_pool.view(torch.int16).fill_(0x7FC0)  # unwritten slots are NaN
+        self.cache.v_pool.view(torch.int16).fill_(0x7FC0)
+        _fill_history(self.cache, wl, 0, H0)
+        self.da = DATagStep(self.cache, wl.da_tags, torch.as_tensor(wl.output_begin, device="cuda"),
+                            segments=torch.as_tensor(wl.segments, device="cuda"), local_tokens=wl.da_local_tokens)
+        self.feeder = sdev.Feeder(wl, seq, with_tokens=True)
+        self.mirror = _mirror(wl, 0, H0, self.steps)
+        self.graph = capture_graph(self._step) if use_graph else None
+
+    def _step(self):
+        f = self.feeder
+        f.step()
+        self.da.step(f.q[0, 0], f.k[0, 0], f.v[0, 0], f.tokens)
+
+    def run(self, check_steps=None):
+        wl, rep = self.wl, Report()
+        H0 = int(wl.H0[0])
+        hk, hv = self.mirror
+        rows, states = oracle.declare.parse_declarations(wl.tokens[:self.steps, 0], wl.da_tags,
+                                                          wl.segments[0].tolist(), int(wl.output_begin[0]))
+        for t in range(self.steps):
+            self.graph.replay() if self.graph is not None else self._step()
+            torch.cuda.synchronize()
+            n = H0 + t + 1
+            assert tuple(int(x) for x in self.da.state[0].cpu()) == states[t], t
+            assert tuple(int(x) for x in self.da.decl[0].cpu()) == rows[t], t
+            mode, fb, fe, ob = rows[t]
+            kept = gather.da_mode_blocks(mode, n, fb, fe, ob, local_tokens=wl.da_local_tokens)
+            words = self.da.mask[0].cpu().numpy().view(np.uint32)
+            assert gather.mask_to_blocks(words, n) == kept, t
+            phys, cnt = gather.gather_blocks(wl.block_tables[0], kept, n)
+            num = int(self.da.num_kept[0].item())
+            assert num == len(phys), t
+            assert np.array_equal(self.da.gathered[0, :num].cpu().numpy(), phys), t
+            assert np.array_equal(self.da.gathered_cnt[0, :num].cpu().numpy(), cnt), t
+            q = wl.cand_q(t, 0, 0, 0)
+            kN, vN = wl.cand_kv(t, 0, 0, 0)
+            if check_steps is None or t in check_steps:
+                o = oracle.oda.blocks_pass(q, kN, vN, hk, hv, n, kept, SCALE)
+                rep.add(self.da.out[0].cpu().numpy(), o, "da-tags t=%d mode=%d" % (t, mode))
+            else:
+                oracle.oda.commit(hk, hv, n, kN, vN)
+            rep.decisions += 1
+            rep.recalls += int(mode == gather.FOCUS)
+        k, v = ops.kv_read(self.cache, 0, H0, self.steps)
+        assert np.array_equal(bf16_tensor_to_bits(k), hk[H0:H0 + self.steps])
+        assert np.array_equal(bf16_tensor_to_bits(v), hv[H0:H0 + self.steps])
+        return rep
+
+
 class RaggedRun:
     """Ragged batch: per step each request takes Full (score > theta) or its fallback
     view (Local, or its fixed keep-list); host mirrors for ``check_requests``."""

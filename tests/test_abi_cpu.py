@@ -66,6 +66,12 @@ def test_other_entry_points_validation():
     assert L.oda_gate_scores(FAKE, 0, 0.0, None, FAKE, None) == SK_E_RANGE
     assert L.da_keep_mask(None, kv(), 1024, FAKE, None) == SK_E_NULL
     assert L.da_keep_mask(FAKE, kv(), -1, FAKE, None) == SK_E_RANGE
+    tags = _lib.DaTagsStruct(5, 6, 7, 100)
+    assert L.da_declare(None, FAKE, FAKE, 2, FAKE, tags, kv(), 1024, FAKE, FAKE, None) == SK_E_NULL
+    assert L.da_declare(FAKE, FAKE, None, 2, FAKE, tags, kv(), 1024, FAKE, FAKE, None) == SK_E_NULL
+    assert L.da_declare(FAKE, FAKE, FAKE, -1, FAKE, tags, kv(), 1024, FAKE, FAKE, None) == SK_E_RANGE
+    assert L.da_declare(FAKE, FAKE, None, 0, FAKE, tags, kv(), -1, FAKE, FAKE, None) == SK_E_RANGE
+    assert L.da_declare(FAKE, FAKE, None, 0, FAKE, tags, kv(), 1024, FAKE, None, None) == SK_E_NULL
     assert L.da_decode_blocks(FAKE, kv(), None, None, None, FAKE, FAKE, FAKE, 0.1, None, 2, FAKE, FAKE,
                               1 << 30, None) == SK_E_NULL
     assert L.sk_kv_write(kv(), 1, 0, 1, FAKE, FAKE, None, None) == SK_E_RANGE       # request >= batch

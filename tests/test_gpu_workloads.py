@@ -85,3 +85,12 @@ def test_all_layers_local_only_equals_local():
     rep = OdaStackRun(wl, check_layers=[0, 1, 2, 3], local_only=range(4), same_candidates=True).run()
     assert rep.recalls > 0
     print("all local-only: recalls %d/24, max-abs %.2e" % (rep.recalls, rep.max_abs))
+
+
+def test_da_tag_stream_every_step():
+    # declarations parsed on the device from a token stream (mode tags, named segments)
+    from tests.harness import DaTagsRun
+    wl = workloads.da_tags_32k()
+    rep = DaTagsRun(wl).run()
+    assert rep.checked_outputs == 512 and rep.recalls > 0
+    print("da_tags_32k: focus steps %d/512, max-abs %.2e, row-rel %.2e" % (rep.recalls, rep.max_abs, rep.max_row_rel))

@@ -544,3 +544,70 @@ def test_whole_model_bytes_bound_the_page_speedup():
     bound = float(cost.decode_bytes_ratio(m, ns, flags))
     print("always-Full / ODA bytes per token: %.3f (page's measured speedup 1.98)" % bound)
     assert 149.52 / 75.54 < bound < 1 / float(cost.oda_over_full(ns, flags))
+
+
+# ---------------------------------------------------------------- DA declarations (NEXT-3)
+
+from oracle import declare  # noqa: E402
+
+TAGS = (5, 6, 7, 100)
+
+
+def test_declaration_parsing_golden():
+    rows = read_golden("da_tags.txt")
+    segments = [(0, 40), (100, 200), (33, 34)]
+    tokens = [int(r[1]) for r in rows]
+    decl, states = declare.parse_declarations(tokens, TAGS, segments, 9)
+    for r, d, st in zip(rows, decl, states):
+        mode, fb, fe, pend = (int(x) for x in r[2:])
+        assert st == (mode, fb, fe, pend), r
+        assert d == (mode, fb, fe, 9), r
+
+
+def _backward_reference(tokens, t, segments):
+    # independent formulation: the mode is set by the latest complete declaration at or
+    # before step t (a global / local tag, or a focus tag immediately followed by a
+    # token naming a segment); the focus range is that of the latest complete focus
+    g, f, l, base = TAGS
+    mode, rng_ = None, None
+    for j in range(t, -1, -1):
+        tok = tokens[j]
+        is_focus = 0 <= tok - base < len(segments) and j >= 1 and tokens[j - 1] == f
+        if is_focus and rng_ is None:
+            b, e = segments[tok - base]
+            rng_ = (max(b, 0) // 16, -(-e // 16) if e > max(b, 0) else max(b, 0) // 16)
+        if mode is None:
+            if tok == g:
+                mode = gather.GLOBAL
+            elif tok == l:
+                mode = gather.LOCAL
+            elif is_focus:
+                mode = gather.FOCUS
+        if mode is not None and rng_ is not None:
+            break
+    return (gather.GLOBAL if mode is None else mode), (rng_ or (0, 0))
+
+
+def test_declaration_parsing_against_backward_scan():
+    rng = np.random.default_rng(12)
+    segments = [(int(a), int(a + w)) for a, w in zip(rng.integers(0, 30000, 12), rng.integers(0, 3000, 12))]
+    segments[3] = (500, 500)  # an empty segment
+    g, f, l, base = TAGS
+    choices = [g, f, l, f, base + 1, base + 3, base + 11, base + 12, base + 40, 1000, 1001, 1002]
+    for trial in range(30):
+        toks = [int(x) for x in rng.choice(choices + [2000] * 8, size=200)]
+        rows, _ = declare.parse_declarations(toks, TAGS, segments, 7)
+        for t in range(len(toks)):
+            mode, (fb, fe) = _backward_reference(toks, t, segments)
+            assert rows[t] == (mode, fb, fe, 7), (trial, t)
+
+
+def test_declaration_rows_give_the_declared_blocks():
+    # a focus row keeps exactly the segment's blocks and the output blocks
+    segments = [(16 * 5 + 3, 16 * 9), (0, 1)]
+    rows, _ = declare.parse_declarations([1000, TAGS[1], TAGS[3] + 0], TAGS, segments, 40)
+    mode, fb, fe, ob = rows[-1]
+    kept = gather.da_mode_blocks(mode, 800, fb, fe, ob)
+    assert kept == list(range(5, 9)) + list(range(40, 50))
+    rows, _ = declare.parse_declarations([TAGS[1], TAGS[3] + 1], TAGS, segments, 40)
+    assert gather.da_mode_blocks(*rows[-1][:1], 800, *rows[-1][1:]) == [0] + list(range(40, 50))
