@@ -29,6 +29,14 @@ Parity status of each function (pinned by the ``-m "not gpu"`` tests):
 * attention.attend ..................................... pinned
 * recall.recall_score / recall.gate .................... pinned
 * gather.gather_blocks / gather.da_mode_blocks ......... pinned
+* bf16.f64_to_bf16_bits ................................ pinned (hand values,
+  ties to even, identity on bf16 values, monotone)
+* decoder.rms_norm / rope / silu ....................... pinned (closed forms,
+  textbook RoPE values, norm and relative-position invariants)
+* decoder.Decoder (layer, forward, oda_step) ........... pinned by invariants
+  (zero weights keep the residual stream; Local = Full within s + w; the
+  recall pass's own commits from layer 1 on); the layer structure is the
+  published Qwen3-family layer, not the pages' (they give none)
 * declare.parse_declarations ........................... pinned by a hand-worked
   token stream (the pages print none) and by an independent backward-scan
   formulation on seeded streams
@@ -46,5 +54,5 @@ Parity status of each function (pinned by the ``-m "not gpu"`` tests):
   tiny decoder and by the exact reduction to the attention-only ratio.
 """
 
-from . import attention, cost, declare, gather, keysets, oda, recall  # noqa: F401
-from .bf16 import bf16_bits_to_f64  # noqa: F401
+from . import attention, cost, declare, decoder, gather, keysets, oda, recall  # noqa: F401
+from .bf16 import bf16_bits_to_f64, f64_to_bf16_bits  # noqa: F401

@@ -611,3 +611,117 @@ def test_declaration_rows_give_the_declared_blocks():
     assert kept == list(range(5, 9)) + list(range(40, 50))
     rows, _ = declare.parse_declarations([TAGS[1], TAGS[3] + 1], TAGS, segments, 40)
     assert gather.da_mode_blocks(*rows[-1][:1], 800, *rows[-1][1:]) == [0] + list(range(40, 50))
+
+
+# ---------------------------------------------------------------- weight-bearing decoder (NEXT-2)
+
+from oracle import decoder  # noqa: E402
+from oracle.bf16 import f64_to_bf16_bits  # noqa: E402
+
+
+def test_bf16_rounding_from_f64():
+    v = np.array([1.0, 1 + 2 ** -8, 1 + 3 * 2 ** -8, 1 + 2 ** -8 + 2 ** -40, 1 + 2 ** -8 - 2 ** -40, -2.5,
+                  2.0 ** -126, 0.0, -0.0, 3.4e38])
+    assert [int(b) for b in f64_to_bf16_bits(v)] == [0x3F80, 0x3F80, 0x3F82, 0x3F81, 0x3F80, 0xC020, 0x0080,
+                                                   0x0000, 0x8000, 0x7F80]
+    # every bf16 value is its own rounding, and rounding is monotone
+    allv = np.arange(0, 0x7F80, 7, dtype=np.uint16)
+    x = oracle.bf16_bits_to_f64(allv)
+    assert np.array_equal(f64_to_bf16_bits(x), allv)
+    mid = (x[:-1] + x[1:]) / 2  # ties between neighbours (7 apart here, so not ties) stay between them
+    r = f64_to_bf16_bits(mid)
+    assert np.all((r >= allv[:-1]) & (r <= allv[1:]))
+
+
+def test_rms_norm_and_silu():
+    x = np.array([3.0, 4.0])
+    assert np.allclose(decoder.rms_norm(x, [1.0, 2.0], 0.0), [3 / math.sqrt(12.5), 8 / math.sqrt(12.5)], atol=1e-15)
+    assert decoder.silu(0.0) == 0.0
+    assert abs(decoder.silu(40.0) - 40.0) < 1e-12
+    assert abs(decoder.silu(1.0) - 1.0 / (1.0 + math.exp(-1.0))) < 1e-15
+
+
+def test_rope_values_and_invariants():
+    # rotate-half pairs (i, i + D/2), angle pos * base^(-2i/D): D = 4, base 1e4, pos 1
+    r = decoder.rope(np.array([[1.0, 0.0, 0.0, 0.0], [0.0, 1.0, 0.0, 0.0]]), 1, 1.0e4)
+    assert np.allclose(r[0], [math.cos(1.0), 0.0, math.sin(1.0), 0.0], atol=1e-15)
+    assert np.allclose(r[1], [0.0, math.cos(0.01), 0.0, math.sin(0.01)], atol=1e-15)
+    rng = np.random.default_rng(3)
+    q, k = rng.standard_normal((2, 128)), rng.standard_normal((2, 128))
+    assert np.allclose(decoder.rope(q, 0, 1e6), q, atol=0)
+    for pos in (1, 777, 131071):
+        rq = decoder.rope(q, pos, 1e6)
+        assert np.allclose(np.linalg.norm(rq, axis=1), np.linalg.norm(q, axis=1), rtol=1e-13)
+    # scores depend on the position difference only
+    a = np.sum(decoder.rope(q, 5000, 1e6) * decoder.rope(k, 4990, 1e6), axis=1)
+    b = np.sum(decoder.rope(q, 10, 1e6) * k, axis=1)
+    assert np.allclose(a, b, rtol=1e-9, atol=1e-9)
+
+
+def _tiny_decoder(seed, layers=2, hidden=64, Hq=2, Hkv=1, inter=96, vocab=50, hr=16, zero=False):
+    s = decoder.DecoderShape(layers, hidden, Hq, Hkv, inter, vocab, hr)
+    rng = np.random.default_rng(seed)
+    D = 128
+
+    def mat(*shape, sd=0.05):
+        return f64_to_bf16_bits(np.zeros(shape) if zero else rng.standard_normal(shape) * sd)
+
+    w = {"emb": mat(vocab, hidden, sd=1.0), "g_final": f64_to_bf16_bits(1 + 0.1 * rng.standard_normal(hidden)),
+         "W1": rng.standard_normal((hr, 3 * hidden)) * 0.05, "b1": np.zeros(hr), "w2": rng.standard_normal(hr) * 0.05,
+         "b2": np.zeros(1)}
+    for l in range(layers):
+        w["qkv.%d" % l] = mat((Hq + 2 * Hkv) * D, hidden)
+        w["o.%d" % l] = mat(hidden, Hq * D)
+        w["gu.%d" % l] = mat(2 * inter, hidden)
+        w["down.%d" % l] = mat(hidden, inter)
+        for g, n in (("g_attn", hidden), ("g_mlp", hidden), ("g_q", D), ("g_k", D)):
+            w["%s.%d" % (g, l)] = f64_to_bf16_bits(1 + 0.1 * rng.standard_normal(n))
+    return decoder.Decoder(s, w)
+
+
+def _hist(dec, n, seed):
+    rng = np.random.default_rng(seed)
+    return [(f64_to_bf16_bits(rng.standard_normal((n, dec.s.kv_heads, 128))),
+             f64_to_bf16_bits(rng.standard_normal((n, dec.s.kv_heads, 128)))) for _ in range(dec.s.layers)]
+
+
+def test_decoder_zero_weights_keep_the_residual_stream():
+    dec = _tiny_decoder(1, zero=True)
+    hist = _hist(dec, 300, 2)
+    h = dec.forward(7, hist, 300, False, sinks=4, window=64)
+    assert np.allclose(h, decoder.rms_norm(dec.w["emb"][7], dec.w["g_final"], dec.s.eps), atol=1e-14)
+    for hk, hv in hist:  # the committed key and value are zeros (of either sign)
+        assert not oracle.bf16_bits_to_f64(hk[299]).any() and not oracle.bf16_bits_to_f64(hv[299]).any()
+
+
+def test_decoder_local_equals_full_within_the_window():
+    dec = _tiny_decoder(3)
+    n = 60
+    h1, h2 = _hist(dec, n, 4), _hist(dec, n, 4)
+    a = dec.forward(11, h1, n, False, sinks=4, window=64)
+    b = dec.forward(11, h2, n, True, sinks=4, window=64)
+    assert np.array_equal(a, b)
+    for (k1, v1), (k2, v2) in zip(h1, h2):
+        assert np.array_equal(k1, k2) and np.array_equal(v1, v2)
+
+
+def test_decoder_recall_pass_commits_its_own_candidates():
+    # beyond the window the passes differ: same committed KV at layer 0 (same input),
+    # different from layer 1 on (different attention upstream); the step keeps the
+    # recall pass's commits when it recalls, the Local pass's otherwise
+    dec = _tiny_decoder(5, layers=3)
+    n = 400
+    hl, hf = _hist(dec, n, 6), _hist(dec, n, 6)
+    dec.forward(3, hl, n, False, sinks=4, window=64)
+    dec.forward(3, hf, n, True, sinks=4, window=64)
+    assert np.array_equal(hl[0][0][n - 1], hf[0][0][n - 1])
+    assert not np.array_equal(hl[1][0][n - 1], hf[1][0][n - 1])
+    for decide in (True, False):
+        hist = _hist(dec, n, 6)
+        hs, g, q_t, hL = dec.oda_step(3, np.zeros(dec.s.hidden), hist, n, decide=lambda q: decide,
+                                      sinks=4, window=64)
+        ref = hf if decide else hl
+        assert g == decide
+        for l in range(3):
+            assert np.array_equal(hist[l][0][n - 1], ref[l][0][n - 1])
+        assert np.array_equal(hs, dec.forward(3, _hist(dec, n, 6), n, decide, sinks=4, window=64))
