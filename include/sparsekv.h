@@ -250,6 +250,61 @@ int da_declare(const int32_t* tokens, int32_t* state, const int32_t* segments,
                sk_paged_kv kv, int32_t local_tokens, int32_t* decl,
                uint32_t* keep_mask, hipStream_t stream);
 
+/* ---- Dense layers of the weight-bearing decode step ----
+ * A recall reruns the whole model for the current token ([ODA] "Approach": the
+ * step is recomputed from the same prior state with Full attention), and the
+ * recall head reads the final hidden state of the Local pass, so a decode step
+ * carries the decoder's dense layers too. These entry points run one token
+ * (batch 1) through a Qwen3-family decoder layer (the pages name the family but
+ * give no layer structure; this is its published layer). Weights are bf16,
+ * row-major [rows][cols]; activations fp32. Every call takes the decode calls'
+ * selector: with sel != NULL and sel[0] != sel_value the launch does nothing
+ * (the gated recall pass). Host-checked: pointers and sizes (SK_E_NULL,
+ * SK_E_SHAPE, SK_E_RANGE); nothing is allocated. */
+
+#define SK_PRO_NONE 0    /* x used as given, cols floats */
+#define SK_PRO_RMSNORM 1 /* x <- x / sqrt(mean(x^2) + eps) * gamma, cols floats */
+#define SK_PRO_SWIGLU 2  /* x holds [gate | up], 2*cols floats; x <- SiLU(gate) * up */
+
+/* y[r] = sum_c W[r][c] x'[c] (+ residual[r] when residual != NULL), x' from x by
+ * the prologue, fp32 accumulation in a fixed order (deterministic). W: bf16
+ * [rows][cols]; gamma: bf16 [cols] (SK_PRO_RMSNORM only). cols % 512 == 0 with
+ * cols / 512 in {1, 2, 3, 4, 6, 8, 12, 16, 24, 32}, 1 <= rows; y may be
+ * residual (in place) but not x. */
+int sk_gemv(const uint16_t* W, int32_t rows, int32_t cols, const float* x, int32_t prologue,
+            const uint16_t* gamma, float eps, const float* residual, float* y,
+            const int32_t* sel, int32_t sel_value, hipStream_t stream);
+
+/* Attention inputs of one token: x = h / sqrt(mean(h^2) + eps) * g_attn;
+ * [q; k; v] = W_qkv x with W_qkv bf16 [(Hq + 2 Hkv) * 128][hidden]; each q head
+ * and each k head RMS-normalised over its 128 values with g_q / g_k (bf16
+ * [128]); q and k rotated by RoPE at pos = seq_lens[0] - 1 (rotate-half: pair
+ * (i, i + 64) turns by pos * rope_base^(-i/64), angles and their sines in
+ * fp64). q_out: fp32 [Hq][128]; k_out, v_out: bf16 [Hkv][128], rounded to
+ * nearest even -- the candidate the decode calls commit. hidden % 512 == 0,
+ * 512 <= hidden <= 4096 (hidden / 512 in {1, 2, 3, 4, 6, 8}), 1 <= Hkv,
+ * Hq % Hkv == 0. */
+int sk_qkv_rope(const uint16_t* W_qkv, const float* h, const uint16_t* g_attn,
+                const uint16_t* g_q, const uint16_t* g_k, int32_t hidden, int32_t q_heads,
+                int32_t kv_heads, float eps, float rope_base, const int32_t* seq_lens,
+                float* q_out, uint16_t* k_out, uint16_t* v_out, const int32_t* sel,
+                int32_t sel_value, hipStream_t stream);
+
+/* out = x / sqrt(mean(x^2) + eps) * gamma over dim values (gamma bf16 [dim]);
+ * 1 <= dim <= 16384. */
+int sk_rmsnorm(const float* x, const uint16_t* gamma, int32_t dim, float eps, float* out,
+               const int32_t* sel, int32_t sel_value, hipStream_t stream);
+
+/* out[i] = table[token[0]][i] widened to fp32 (table bf16 [vocab][hidden]), and
+ * the same into out2 when out2 != NULL; a token outside [0, vocab) gives zeros. */
+int sk_embed(const uint16_t* table, int32_t vocab, int32_t hidden, const int32_t* token,
+             float* out, float* out2, const int32_t* sel, int32_t sel_value,
+             hipStream_t stream);
+
+/* out = (gate[0] == gate_value) ? a : b over dim floats (the step select). */
+int sk_select(const int32_t* gate, int32_t gate_value, const float* a, const float* b,
+              int32_t dim, float* out, hipStream_t stream);
+
 /* Block-table rewrite plus attention over the kept blocks ([DA] section 3).
  * For every selected request b, the kept logical blocks (bits of keep_mask
  * row b below ceil(n/16)) are compacted in ascending logical order into

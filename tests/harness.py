@@ -361,3 +361,94 @@ class RaggedRun:
             assert np.array_equal(bf16_tensor_to_bits(k), hk[H0:H0 + self.steps]), r
             assert np.array_equal(bf16_tensor_to_bits(v), hv[H0:H0 + self.steps]), r
         return rep
+
+
+class DecoderRun:
+    """Weight-bearing ODA steps (Local pass through every layer, recall head on the real
+    Local hidden state, gated recall pass, select) against the fp64 decoder oracle."""
+
+    def __init__(self, wl, local_only=()):
+        from sparse_kv_recall_amd.model import DecoderShape, ODADecoder
+        self.wl = wl
+        L, Hkv = wl.layers, wl.kv_heads
+        mb = wl.max_blocks
+        bt = torch.arange(mb, dtype=torch.int32, device="cuda")[None]
+        self.seq = torch.full((1,), wl.H0, dtype=torch.int32, device="cuda")
+        self.caches = [ops.PagedKVCache(mb, 1, wl.q_heads, Hkv, mb, block_tables=bt, seq_lens=self.seq)
+                       for _ in range(L)]
+        self.hist = []
+        for l, c in enumerate(self.caches):
+            k = np.zeros((wl.H0 + wl.steps, Hkv, 128), np.uint16)
+            v = np.zeros_like(k)
+            k[:wl.H0] = wl.hist_bits("k", l, 0, wl.H0)
+            v[:wl.H0] = wl.hist_bits("v", l, 0, wl.H0)
+            ops.kv_write(c, 0, 0, torch.as_tensor(k[:wl.H0].view(np.int16), device="cuda").view(torch.bfloat16),
+                         torch.as_tensor(v[:wl.H0].view(np.int16), device="cuda").view(torch.bfloat16))
+            self.hist.append((k, v))
+        shape = DecoderShape(L, wl.hidden, wl.q_heads, Hkv, wl.intermediate, wl.vocab, wl.recall_hidden, wl.eps,
+                             wl.rope_base)
+        self.model = ODADecoder(shape, wl.device_weights(), self.caches, wl.sinks, wl.window,
+                                local_only=local_only)
+        self.local_only = frozenset(local_only)
+        self.oracle = oracle.decoder.Decoder(
+            oracle.decoder.DecoderShape(L, wl.hidden, wl.q_heads, Hkv, wl.intermediate, wl.vocab, wl.recall_hidden,
+                                        eps=wl.eps, rope_base=wl.rope_base), wl.host_weights())
+
+    def run(self):
+        wl, rep, m = self.wl, Report(), self.model
+        h_prev = np.zeros(wl.hidden)
+        n_bad, n_all = 0, 0
+        for t in range(wl.steps):
+            n = wl.H0 + t + 1
+            tok = int(wl.tokens[t])
+            m.token.fill_(tok)
+            self.seq.fill_(n)
+            m.step(wl.theta)
+            torch.cuda.synchronize()
+            q_gpu = float(m.qscore[0].item())
+            g_gpu = bool(m.gate[0].item())
+
+            def decide(q):
+                if abs(q - wl.theta) < BAND:
+                    rep.decisions_in_band += 1
+                    return g_gpu
+                return oracle.recall.gate(q, wl.theta)
+
+            if self.local_only:
+                hs, g, q_ref, hL = self._oracle_step_local_only(tok, h_prev, n, decide)
+            else:
+                hs, g, q_ref, hL = self.oracle.oda_step(tok, h_prev, self.hist, n, wl.theta, decide=decide,
+                                                        sinks=wl.sinks, window=wl.window)
+            assert abs(q_gpu - q_ref) <= 1e-3 * max(1.0, abs(q_ref)), (t, q_gpu, q_ref)
+            assert g == g_gpu, (t, q_gpu, q_ref)
+            rep.decisions += 1
+            rep.recalls += int(g)
+            rep.add(m.h_local_final.cpu().numpy()[None], hL[None], "h_local t=%d" % t)
+            rep.add(m.h_prev.cpu().numpy()[None], hs[None], "h_selected t=%d" % t)
+            for l in range(wl.layers):  # committed candidates: bf16 of nearly equal values
+                k, v = ops.kv_read(self.caches[l], 0, n - 1, 1)
+                for got, ref in ((bf16_tensor_to_bits(k)[0], self.hist[l][0][n - 1]),
+                                 (bf16_tensor_to_bits(v)[0], self.hist[l][1][n - 1])):
+                    a, b = oracle.bf16_bits_to_f64(got), oracle.bf16_bits_to_f64(ref)
+                    assert np.all(np.abs(a - b) <= 2.0 ** -7 * np.maximum(np.abs(a), np.abs(b)) + 1e-30), (t, l)
+                    n_bad += int((got != ref).sum())
+                    n_all += got.size
+            h_prev = hs
+        rep.commit_mismatch_frac = n_bad / max(1, n_all)
+        assert rep.commit_mismatch_frac < 0.01, rep.commit_mismatch_frac
+        return rep
+
+    def _oracle_step_local_only(self, tok, h_prev, n, decide):
+        # per-layer access control in the recall pass (local-only layers keep the Local view)
+        dec, wl = self.oracle, self.wl
+        hL = dec.forward(tok, self.hist, n, False, sinks=wl.sinks, window=wl.window)
+        x = oracle.recall.concat_inputs(h_prev, dec.w["emb"][tok], hL)
+        q_t = oracle.recall.recall_score(x, dec.w["W1"], dec.w["b1"], dec.w["w2"], dec.w["b2"])
+        if not decide(q_t):
+            return hL, False, q_t, hL
+        scale = 1.0 / math.sqrt(128)
+        h = dec.w["emb"][tok].copy()
+        for l in range(wl.layers):
+            full = l not in self.local_only
+            h = dec.layer(l, h, self.hist[l][0], self.hist[l][1], n, full, scale, wl.sinks, wl.window)
+        return oracle.decoder.rms_norm(h, dec.w["g_final"], wl.eps), True, q_t, hL

@@ -90,3 +90,15 @@ def test_candidates_layer0_share_passes():
     k0, v0 = w.cand_kv(5, 0, 0, 0)
     k1, v1 = w.cand_kv(5, 0, 1, 0)
     assert np.array_equal(k0, k1) and np.array_equal(v0, v1)
+
+
+def test_decoder_workload_is_deterministic():
+    from synth.decoder import decoder_small
+    a, b = decoder_small(), decoder_small()
+    wa, wb = a.host_weights(), b.host_weights()
+    assert set(wa) == set(wb)
+    for k in wa:
+        assert np.array_equal(wa[k], wb[k]), k
+    assert wa["qkv.0"].shape == ((4 + 2 * 2) * 128, 512) and wa["qkv.0"].dtype == np.uint16
+    assert wa["W1"].dtype == np.float32 and wa["W1"].shape == (64, 3 * 512)
+    assert np.array_equal(a.tokens, b.tokens) and a.tokens.max() < a.vocab
