@@ -310,6 +310,86 @@ def da_tags_rate(device, reps=2):
             "us_per_step": round(best * 1e3 / wl.steps, 2)}
 
 
+def decoder_rates(device, contexts=(4096, 131072), steps=64, recalls=8):
+    """Whole-model decode (Qwen3-1.7B's dense shape, random weights): the ODA step
+    (Local pass through all 28 layers, recall head on its final hidden state, gated
+    recall pass, select) against always-Full decoding on the same kernels, at two
+    history lengths. The recall decisions follow a seeded schedule of `recalls` in
+    `steps` (the head's score is still computed every step), so both contexts see the
+    pages' 12.5 % rate. KV pools are filled with random bf16 (a random history)."""
+    import numpy as np
+    import torch
+    from sparse_kv_recall_amd import ops
+    from sparse_kv_recall_amd.model import DecoderShape, ODADecoder
+    from sparse_kv_recall_amd.stack import capture_graph
+    from synth import device as sdev
+    from synth.decoder import decoder_qwen3_1_7b
+    from synth.workloads import np_rng
+
+    out = {}
+    for H0 in contexts:
+        wl = decoder_qwen3_1_7b(H0, steps)
+        mb = wl.max_blocks
+        seq = torch.full((1,), H0, dtype=torch.int32, device=device)
+        bt = torch.arange(mb, dtype=torch.int32, device=device)[None]
+        caches = [ops.PagedKVCache(mb, 1, wl.q_heads, wl.kv_heads, mb, block_tables=bt, seq_lens=seq, device=device)
+                  for _ in range(wl.layers)]
+        for l, c in enumerate(caches):
+            sdev.fill_normal_(c.k_pool, wl.hist_key("k", l), 0)
+            sdev.fill_normal_(c.v_pool, wl.hist_key("v", l), 0)
+        shape = DecoderShape(wl.layers, wl.hidden, wl.q_heads, wl.kv_heads, wl.intermediate, wl.vocab,
+                             wl.recall_hidden)
+        model = ODADecoder(shape, wl.device_weights(device), caches, device=device)
+        tokens = torch.as_tensor(wl.tokens.astype(np.int64), device=device)
+        sched = -np.ones(steps, np.float32)
+        sched[np_rng(wl.wid, 99).choice(steps, size=recalls, replace=False)] = 1.0
+        sched = torch.as_tensor(sched, device=device)
+        t_idx = torch.zeros(1, dtype=torch.int64, device=device)
+        score = torch.zeros(1, dtype=torch.float32, device=device)
+
+        def feed():
+            model.token.copy_(torch.index_select(tokens, 0, t_idx))
+            score.copy_(torch.index_select(sched, 0, t_idx))
+            seq.add_(1)
+            t_idx.add_(1)
+
+        def oda_step():
+            feed()
+            model.local_pass()
+            model.recall_gate(0.0)
+            ops.oda_gate_scores(score, 0.0, out=model.gate)  # the schedule decides
+            model.recall_pass(gated=True)
+            ops.select(model.gate, model.final_full, model.h_local_final, model.h_prev)
+
+        def full_step():
+            feed()
+            model.always_full_step()
+
+        res = {}
+        for name, fn in (("oda", oda_step), ("always_full", full_step)):
+            graph = capture_graph(fn)
+            seq.fill_(H0)
+            t_idx.zero_()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(steps):
+                graph.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            res[name] = e0.elapsed_time(e1) / steps
+            del graph
+        out["ctx_%d" % H0] = {"oda_ms_per_step": round(res["oda"], 4), "oda_tok_s": round(1e3 / res["oda"], 2),
+                              "always_full_ms_per_step": round(res["always_full"], 4),
+                              "always_full_tok_s": round(1e3 / res["always_full"], 2),
+                              "oda_speedup": round(res["always_full"] / res["oda"], 3),
+                              "recall_steps": recalls, "steps": steps}
+        del model, caches
+        torch.cuda.empty_cache()
+    return dict(out, model="Qwen3-1.7B dense shape (28 layers, hidden 2048, 16/8 heads, MLP 6144), random bf16 "
+                           "weights, batch 1")
+
+
 def hybrid_rate(stack, feeder, wl, steps):
     """Decode rate of the same workload with per-layer access control: three of every
     four layers restricted to the Local range (their recall pass runs the Local view).
@@ -344,6 +424,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=16)
     ap.add_argument("--roofline-reps", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-model", action="store_true", help="skip the weight-bearing decode measurement")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the decode path here is built and measured on a single "
@@ -404,6 +485,11 @@ def main():
     log("hybrid access control: %s" % json.dumps(hybrid))
     da_tags = da_tags_rate(device)
     log("declaration-driven DA step: %s" % json.dumps(da_tags))
+    if not args.no_model:
+        whole_model = decoder_rates(device)
+        log("weight-bearing decode: %s" % json.dumps(whole_model))
+    else:
+        whole_model = None
     traffic = profiled_traffic(bytes_full)
     traffic = None if traffic is None else int(round(traffic))
     copy_calibration(device)
@@ -444,6 +530,7 @@ def main():
                                      attention_bytes_ratio=round(float(full_bytes / step_bytes), 3)),
         "hybrid_local_only": hybrid,
         "da_declared_step": da_tags,
+        "whole_model_decode": whole_model,
         "step_hbm_gbs": round(float(step_gbs), 1),
         "wall_s_timed": round(wall, 3),
     }
