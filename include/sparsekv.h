@@ -264,31 +264,33 @@ int da_declare(const int32_t* tokens, int32_t* state, const int32_t* segments,
 
 #define SK_PRO_NONE 0    /* x used as given, cols floats */
 #define SK_PRO_RMSNORM 1 /* x <- x / sqrt(mean(x^2) + eps) * gamma, cols floats */
-#define SK_PRO_SWIGLU 2  /* x holds [gate | up], 2*cols floats; x <- SiLU(gate) * up */
+#define SK_EPI_STORE 0   /* y[r] = a_r (+ residual[r]) */
+#define SK_EPI_SWIGLU 1  /* y[r] = SiLU(a_r) * a_{rows + r}: W holds 2*rows rows */
 
-/* y[r] = sum_c W[r][c] x'[c] (+ residual[r] when residual != NULL), x' from x by
- * the prologue, fp32 accumulation in a fixed order (deterministic). W: bf16
- * [rows][cols]; gamma: bf16 [cols] (SK_PRO_RMSNORM only). cols % 512 == 0 with
- * cols / 512 in {1, 2, 3, 4, 6, 8, 12, 16, 24, 32}, 1 <= rows; y may be
- * residual (in place) but not x. */
+/* a_r = sum_c W[r][c] x'[c], x' from x by the prologue, fp32 accumulation in a
+ * fixed order (deterministic); stored per the epilogue (SK_EPI_SWIGLU: gate rows
+ * 0..rows-1 then up rows rows..2rows-1 of W, no residual). W: bf16 [rows or
+ * 2*rows][cols]; gamma: bf16 [cols] (SK_PRO_RMSNORM only). cols % 512 == 0 with
+ * cols / 512 in {1, 2, 3, 4, 6, 8, 12, 16}, 1 <= rows; y may be residual (in
+ * place) but not x. */
 int sk_gemv(const uint16_t* W, int32_t rows, int32_t cols, const float* x, int32_t prologue,
-            const uint16_t* gamma, float eps, const float* residual, float* y,
+            const uint16_t* gamma, float eps, const float* residual, int32_t epilogue, float* y,
             const int32_t* sel, int32_t sel_value, hipStream_t stream);
 
 /* Attention inputs of one token: x = h / sqrt(mean(h^2) + eps) * g_attn;
- * [q; k; v] = W_qkv x with W_qkv bf16 [(Hq + 2 Hkv) * 128][hidden]; each q head
- * and each k head RMS-normalised over its 128 values with g_q / g_k (bf16
- * [128]); q and k rotated by RoPE at pos = seq_lens[0] - 1 (rotate-half: pair
- * (i, i + 64) turns by pos * rope_base^(-i/64), angles and their sines in
- * fp64). q_out: fp32 [Hq][128]; k_out, v_out: bf16 [Hkv][128], rounded to
- * nearest even -- the candidate the decode calls commit. hidden % 512 == 0,
- * 512 <= hidden <= 4096 (hidden / 512 in {1, 2, 3, 4, 6, 8}), 1 <= Hkv,
- * Hq % Hkv == 0. */
+ * [q; k; v] = W_qkv x with W_qkv bf16 [(Hq + 2 Hkv) * 128][hidden] (written to
+ * scratch, fp32 [(Hq + 2 Hkv) * 128], caller-owned); each q head and each k head
+ * RMS-normalised over its 128 values with g_q / g_k (bf16 [128]); q and k rotated
+ * by RoPE at pos = seq_lens[0] - 1 (rotate-half: pair (i, i + 64) turns by
+ * pos * rope_base^(-i/64), angles and their sines in fp64). q_out: fp32
+ * [Hq][128]; k_out, v_out: bf16 [Hkv][128], rounded to nearest even -- the
+ * candidate the decode calls commit. Two launches. hidden % 512 == 0 with
+ * hidden / 512 in {1, 2, 3, 4, 6, 8, 12, 16}, 1 <= Hkv, Hq % Hkv == 0. */
 int sk_qkv_rope(const uint16_t* W_qkv, const float* h, const uint16_t* g_attn,
                 const uint16_t* g_q, const uint16_t* g_k, int32_t hidden, int32_t q_heads,
                 int32_t kv_heads, float eps, float rope_base, const int32_t* seq_lens,
-                float* q_out, uint16_t* k_out, uint16_t* v_out, const int32_t* sel,
-                int32_t sel_value, hipStream_t stream);
+                float* scratch, float* q_out, uint16_t* k_out, uint16_t* v_out,
+                const int32_t* sel, int32_t sel_value, hipStream_t stream);
 
 /* out = x / sqrt(mean(x^2) + eps) * gamma over dim values (gamma bf16 [dim]);
  * 1 <= dim <= 16384. */

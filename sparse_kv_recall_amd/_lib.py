@@ -49,10 +49,10 @@ _SIGNATURES = {
     "da_keep_mask": (c_int32, [c_void_p, PagedKVStruct, c_int32, c_void_p, c_void_p]),
     "da_declare": (c_int32, [c_void_p, c_void_p, c_void_p, c_int32, c_void_p, DaTagsStruct, PagedKVStruct, c_int32,
                              c_void_p, c_void_p, c_void_p]),
-    "sk_gemv": (c_int32, [c_void_p, c_int32, c_int32, c_void_p, c_int32, c_void_p, c_float, c_void_p, c_void_p,
-                          c_void_p, c_int32, c_void_p]),
+    "sk_gemv": (c_int32, [c_void_p, c_int32, c_int32, c_void_p, c_int32, c_void_p, c_float, c_void_p, c_int32,
+                          c_void_p, c_void_p, c_int32, c_void_p]),
     "sk_qkv_rope": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32, c_float,
-                              c_float, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_void_p]),
+                              c_float, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_void_p]),
     "sk_rmsnorm": (c_int32, [c_void_p, c_void_p, c_int32, c_float, c_void_p, c_void_p, c_int32, c_void_p]),
     "sk_embed": (c_int32, [c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_void_p]),
     "sk_select": (c_int32, [c_void_p, c_int32, c_void_p, c_void_p, c_int32, c_void_p, c_void_p]),

@@ -10,12 +10,15 @@
 //
 // How (gfx950): batch-1 projections are GEMVs bound by reading the bf16 weights once,
 // so there is no MFMA here (a matrix core would see one useful column). Each wave owns
-// whole rows: its lanes issue all 16-byte weight loads of its rows first, then the
-// workgroup stages the transformed input vector in LDS (RMSNorm or SwiGLU prologue),
-// then every lane forms partial dot products that a DPP wave reduction sums in a fixed
-// order (deterministic). The residual add is fused into the store. The q/k/v kernel
-// gives one workgroup to each head, so the head's RMS norm and the rotary pairing
-// (i, i + 64) stay inside the workgroup; rotary angles are computed in fp64.
+// whole output rows and walks them with a two-deep register ring: the next row's 16-byte
+// weight loads are in flight while this row is reduced; loads past the last row go
+// through an empty buffer range (zeros, no memory access), so the loop has no branches.
+// The workgroup stages the input vector in LDS once (RMSNorm prologue, fp32), lanes
+// form partial dot products, and a DPP wave reduction sums them in a fixed order
+// (deterministic). Residual add and the SwiGLU product (gate and up rows paired in one
+// wave) are fused into the store. The q/k/v projection is one such GEMV followed by a
+// per-head kernel for the q/k RMS norm and the rotary pairs (i, i + 64), with rotary
+// angles computed in fp64.
 #include <math.h>
 
 #include "sk_internal.h"
@@ -23,8 +26,8 @@
 namespace sk {
 namespace {
 
-constexpr int kGemvWaves = 4;   // waves per GEMV workgroup
-constexpr int kQkvThreads = 1024;
+constexpr int kGemvWaves = 8;   // waves per GEMV workgroup
+constexpr int kGemvGrid = 512;  // GEMV workgroups at most (two per CU)
 
 __device__ inline float bf16f(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
 
@@ -87,115 +90,130 @@ __device__ inline void stage_input(const float* __restrict__ x, const uint16_t* 
     }
     const float r = 1.f / sqrtf(block_sum(ss, red) / float(cols) + eps);
     for (int i = threadIdx.x; i < cols; i += blockDim.x) xs[i] = x[i] * r * bf16f(gamma[i]);
-  } else if (PRO == SK_PRO_SWIGLU) {
-    for (int i = threadIdx.x; i < cols; i += blockDim.x) {
-      const float g = x[i];
-      xs[i] = g / (1.f + expf(-g)) * x[cols + i];
-    }
   } else {
     for (int i = threadIdx.x; i < cols; i += blockDim.x) xs[i] = x[i];
   }
   __syncthreads();
 }
 
-// RW rows per wave, J 16-byte chunks per lane per row (cols = 512 J).
-template <int J, int RW, int PRO>
+// A wave-uniform address in scalar registers (buffer resources must be uniform).
+__device__ inline const uint8_t* uniform_ptr(const uint8_t* p) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(a));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(a >> 32));
+  return reinterpret_cast<const uint8_t*>((uint64_t(hi) << 32) | lo);
+}
+
+constexpr int kBufferFlags = 0x00020000;  // raw buffer access, 32-bit data format (gfx9 word 3)
+constexpr int kNonTemporal = 2;
+
+// The lane's J 16-byte chunks of one weight row, through a buffer resource spanning the
+// row: when ok is false the range is empty and the loads return zeros without touching
+// memory, so fetches past the last row need no branch.
+template <int J>
+__device__ inline void load_row(const uint16_t* W, int row, int cols, bool ok, int lane, u32x4 (&w)[J]) {
+  const uint8_t* base = uniform_ptr(reinterpret_cast<const uint8_t*>(W) + size_t(row) * cols * 2);
+  const int bytes = __builtin_amdgcn_readfirstlane(ok ? cols * 2 : 0);
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), 0, bytes, kBufferFlags);
+#pragma unroll
+  for (int j = 0; j < J; ++j)
+    w[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, 16 * (lane + 64 * j), 0, kNonTemporal));
+}
+
+template <int J>
+__device__ inline float row_dot(const u32x4 (&w)[J], const float* xs, int lane) {
+  float acc = 0.f;
+#pragma unroll
+  for (int j = 0; j < J; ++j) acc += dot8(w[j], xs + 8 * (lane + 64 * j));
+  return wave_sum(acc);
+}
+
+// Persistent GEMV: every wave walks the output rows g, g + G, ... (G = waves in the
+// grid) with a two-deep register ring, so the next row's weights are in flight while
+// this row is reduced. EPI_SWIGLU pairs weight rows r (gate) and rows + r (up) in one
+// wave and stores SiLU(gate) * up.
+template <int J, int PRO, int EPI>
 __global__ __launch_bounds__(64 * kGemvWaves) void gemv_kernel(const uint16_t* __restrict__ W, int rows, int cols,
                                                                const float* __restrict__ x,
                                                                const uint16_t* __restrict__ gamma, float eps,
                                                                const float* residual, float* y, const int32_t* sel,
                                                                int sel_value) {
+  constexpr int NR = (EPI == SK_EPI_SWIGLU) ? 2 : 1;
+  constexpr bool kRing = NR * J <= 12;  // two row buffers fit the registers
   if (gated_off(sel, sel_value)) return;
   extern __shared__ float xs[];
   __shared__ float red[kGemvWaves];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int r0 = (blockIdx.x * kGemvWaves + wave) * RW;
-  u32x4 w[RW][J];
+  const int G = int(gridDim.x) * kGemvWaves;
+  int it = int(blockIdx.x) * kGemvWaves + wave;
+  u32x4 b0[NR][J], b1[NR][J];  // b1 is only used (and allocated) with the ring
+  auto fetch = [&](u32x4 (&b)[NR][J], int item) {
+    const bool ok = item < rows;
+    const int r = ok ? item : 0;
 #pragma unroll
-  for (int r = 0; r < RW; ++r) {
-    const u32x4* row = reinterpret_cast<const u32x4*>(W + size_t(min(r0 + r, rows - 1)) * cols);
-#pragma unroll
-    for (int j = 0; j < J; ++j) w[r][j] = __builtin_nontemporal_load(row + lane + 64 * j);
-  }
+    for (int k = 0; k < NR; ++k) load_row<J>(W, r + k * rows, cols, ok, lane, b[k]);
+  };
+  auto finish = [&](u32x4 (&b)[NR][J], int item) {
+    const float a0 = row_dot<J>(b[0], xs, lane);
+    float v;
+    if (EPI == SK_EPI_SWIGLU) {
+      const float a1 = row_dot<J>(b[NR - 1], xs, lane);
+      v = a0 / (1.f + expf(-a0)) * a1;
+    } else {
+      v = a0 + (residual ? residual[item] : 0.f);
+    }
+    if (lane == 0) y[item] = v;
+  };
+  fetch(b0, it);
   stage_input<PRO>(x, gamma, eps, cols, xs, red);
-#pragma unroll
-  for (int r = 0; r < RW; ++r) {
-    float acc = 0.f;
-#pragma unroll
-    for (int j = 0; j < J; ++j) acc += dot8(w[r][j], xs + 8 * (lane + 64 * j));
-    acc = wave_sum(acc);
-    if (lane == 0 && r0 + r < rows) y[r0 + r] = acc + (residual ? residual[r0 + r] : 0.f);
+  if constexpr (kRing) {
+    for (; it + G < rows; it += 2 * G) {
+      fetch(b1, it + G);
+      finish(b0, it);
+      fetch(b0, it + 2 * G);
+      finish(b1, it + G);
+    }
+    if (it < rows) finish(b0, it);
+  } else {  // wide rows: one row (pair) in flight per wave, the other waves overlap it
+    finish(b0, it);
+    for (it += G; it < rows; it += G) {
+      fetch(b0, it);
+      finish(b0, it);
+    }
   }
 }
 
-// One workgroup per head (q heads, then k heads, then v heads); 16 waves, 8 rows each,
-// RB rows in flight per wave at a time.
-template <int J>
-__global__ __launch_bounds__(kQkvThreads) void qkv_kernel(const uint16_t* __restrict__ W, const float* __restrict__ h,
-                                                          const uint16_t* __restrict__ g_attn,
-                                                          const uint16_t* __restrict__ g_q,
-                                                          const uint16_t* __restrict__ g_k, int hidden, int Hq,
-                                                          int Hkv, float eps, float rope_base,
-                                                          const int32_t* __restrict__ seq_lens, float* q_out,
-                                                          uint16_t* k_out, uint16_t* v_out, const int32_t* sel,
-                                                          int sel_value) {
-  constexpr int RB = (J <= 2) ? 8 : (J <= 4 ? 4 : (J <= 8 ? 2 : 1));
-  if (gated_off(sel, sel_value)) return;
-  extern __shared__ float xs[];
-  __shared__ float red[kQkvThreads / 64];
+// Per-head tail of the q/k/v projection: q and k heads RMS-normalised over their 128
+// values and rotated (RoPE, pairs (i, i + 64), angles in fp64); k and v rounded to bf16.
+__global__ __launch_bounds__(kHeadDim) void qk_finish_kernel(const float* __restrict__ raw,
+                                                            const uint16_t* __restrict__ g_q,
+                                                            const uint16_t* __restrict__ g_k, int Hq, int Hkv,
+                                                            float eps, float rope_base,
+                                                            const int32_t* __restrict__ seq_lens, float* q_out,
+                                                            uint16_t* k_out, uint16_t* v_out, const int32_t* sel,
+                                                            int sel_value) {
+  __shared__ float red[kHeadDim / 64];
   __shared__ float s_val[kHeadDim];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int head = blockIdx.x;
-  const uint16_t* Wh = W + size_t(head) * kHeadDim * hidden;
-  u32x4 w[RB][J];
-  auto load_rows = [&](int rb) {
-#pragma unroll
-    for (int r = 0; r < RB; ++r) {
-      const u32x4* row = reinterpret_cast<const u32x4*>(Wh + size_t(8 * wave + rb + r) * hidden);
-#pragma unroll
-      for (int j = 0; j < J; ++j) w[r][j] = __builtin_nontemporal_load(row + lane + 64 * j);
-    }
-  };
-  load_rows(0);
-  stage_input<SK_PRO_RMSNORM>(h, g_attn, eps, hidden, xs, red);
-  for (int rb = 0; rb < 8; rb += RB) {
-    if (rb > 0) load_rows(rb);
-#pragma unroll
-    for (int r = 0; r < RB; ++r) {
-      float acc = 0.f;
-#pragma unroll
-      for (int j = 0; j < J; ++j) acc += dot8(w[r][j], xs + 8 * (lane + 64 * j));
-      acc = wave_sum(acc);
-      if (lane == 0) s_val[8 * wave + rb + r] = acc;
-    }
-  }
-  __syncthreads();
-  const int t = threadIdx.x;
+  if (gated_off(sel, sel_value)) return;
+  const int head = blockIdx.x, t = threadIdx.x;
   const bool is_q = head < Hq, is_v = head >= Hq + Hkv;
-  float v = (t < kHeadDim) ? s_val[t] : 0.f;
-  // per-head RMS norm of q and k (sum over the 128 values, fixed order)
+  float v = raw[head * kHeadDim + t];
   const float ss = block_sum(v * v, red);
-  if (!is_v && t < kHeadDim) {
-    const uint16_t* g = is_q ? g_q : g_k;
-    v = v * (1.f / sqrtf(ss / float(kHeadDim) + eps)) * bf16f(g[t]);
+  if (!is_v) v = v * (1.f / sqrtf(ss / float(kHeadDim) + eps)) * bf16f((is_q ? g_q : g_k)[t]);
+  s_val[t] = v;
+  __syncthreads();
+  float o = v;
+  if (!is_v) {
+    const int i = t & 63;
+    const double ang = double(seq_lens[0] - 1) * pow(double(rope_base), -double(i) / 64.0);
+    const float c = float(cos(ang)), s = float(sin(ang));
+    o = (t < 64) ? v * c - s_val[t + 64] * s : v * c + s_val[t - 64] * s;
   }
-  __syncthreads();
-  if (t < kHeadDim) s_val[t] = v;
-  __syncthreads();
-  if (t < kHeadDim) {
-    float o = v;
-    if (!is_v) {
-      const int i = t & 63;
-      const double ang = double(seq_lens[0] - 1) * pow(double(rope_base), -double(i) / 64.0);
-      const float c = float(cos(ang)), s = float(sin(ang));
-      o = (t < 64) ? v * c - s_val[t + 64] * s : v * c + s_val[t - 64] * s;
-    }
-    if (is_q) {
-      q_out[head * kHeadDim + t] = o;
-    } else {
-      uint16_t* dst = is_v ? v_out + (head - Hq - Hkv) * kHeadDim : k_out + (head - Hq) * kHeadDim;
-      dst[t] = __builtin_bit_cast(uint16_t, __bf16(o));
-    }
+  if (is_q) {
+    q_out[head * kHeadDim + t] = o;
+  } else {
+    uint16_t* dst = is_v ? v_out + (head - Hq - Hkv) * kHeadDim : k_out + (head - Hq) * kHeadDim;
+    dst[t] = __builtin_bit_cast(uint16_t, __bf16(o));
   }
 }
 
@@ -228,35 +246,47 @@ __global__ void select_kernel(const int32_t* __restrict__ gate, int gate_value, 
   if (i < dim) out[i] = (gate[0] == gate_value) ? a[i] : b[i];
 }
 
-template <int J, int RW>
-int launch_gemv_j(const uint16_t* W, int rows, int cols, const float* x, int pro, const uint16_t* gamma, float eps,
-                  const float* residual, float* y, const int32_t* sel, int sel_value, hipStream_t stream) {
-  const int per_wg = kGemvWaves * RW;
-  const dim3 grid(unsigned((rows + per_wg - 1) / per_wg)), block(64 * kGemvWaves);
-  const size_t lds = size_t(cols) * 4;
-  if (pro == SK_PRO_RMSNORM)
-    hipLaunchKernelGGL((gemv_kernel<J, RW, SK_PRO_RMSNORM>), grid, block, lds, stream, W, rows, cols, x, gamma, eps,
-                       residual, y, sel, sel_value);
-  else if (pro == SK_PRO_SWIGLU)
-    hipLaunchKernelGGL((gemv_kernel<J, RW, SK_PRO_SWIGLU>), grid, block, lds, stream, W, rows, cols, x, gamma, eps,
-                       residual, y, sel, sel_value);
-  else
-    hipLaunchKernelGGL((gemv_kernel<J, RW, SK_PRO_NONE>), grid, block, lds, stream, W, rows, cols, x, gamma, eps,
-                       residual, y, sel, sel_value);
-  return launch_status(hipGetLastError());
-}
-
 template <int J>
-int launch_qkv_j(const uint16_t* W, const float* h, const uint16_t* g_attn, const uint16_t* g_q, const uint16_t* g_k,
-                 int hidden, int Hq, int Hkv, float eps, float rope_base, const int32_t* seq_lens, float* q_out,
-                 uint16_t* k_out, uint16_t* v_out, const int32_t* sel, int sel_value, hipStream_t stream) {
-  hipLaunchKernelGGL(qkv_kernel<J>, dim3(unsigned(Hq + 2 * Hkv)), dim3(kQkvThreads), size_t(hidden) * 4, stream, W, h,
-                     g_attn, g_q, g_k, hidden, Hq, Hkv, eps, rope_base, seq_lens, q_out, k_out, v_out, sel,
-                     sel_value);
+int launch_gemv_j(const uint16_t* W, int rows, int cols, const float* x, int pro, int epi, const uint16_t* gamma,
+                  float eps, const float* residual, float* y, const int32_t* sel, int sel_value, hipStream_t stream) {
+  const int waves = (rows + 1) / 2;  // about two output rows per wave
+  int wgs = (waves + kGemvWaves - 1) / kGemvWaves;
+  if (wgs > kGemvGrid) wgs = kGemvGrid;
+  const dim3 grid{unsigned(wgs)}, block{unsigned(64 * kGemvWaves)};
+  const size_t lds = size_t(cols) * 4;
+#define SK_GEMV(P, E)                                                                                             \
+  hipLaunchKernelGGL((gemv_kernel<J, P, E>), grid, block, lds, stream, W, rows, cols, x, gamma, eps, residual, y, \
+                     sel, sel_value)
+  if (pro == SK_PRO_RMSNORM) {
+    if (epi == SK_EPI_SWIGLU) SK_GEMV(SK_PRO_RMSNORM, SK_EPI_SWIGLU);
+    else SK_GEMV(SK_PRO_RMSNORM, SK_EPI_STORE);
+  } else {
+    if (epi == SK_EPI_SWIGLU) SK_GEMV(SK_PRO_NONE, SK_EPI_SWIGLU);
+    else SK_GEMV(SK_PRO_NONE, SK_EPI_STORE);
+  }
+#undef SK_GEMV
   return launch_status(hipGetLastError());
 }
 
-bool valid_width(int cols) { return cols >= 512 && cols <= 16384 && cols % 512 == 0; }
+int launch_gemv(const uint16_t* W, int rows, int cols, const float* x, int pro, int epi, const uint16_t* gamma,
+                float eps, const float* residual, float* y, const int32_t* sel, int sel_value, hipStream_t stream) {
+  switch (cols / 512) {
+#define SK_J(JJ) \
+  case JJ: return launch_gemv_j<JJ>(W, rows, cols, x, pro, epi, gamma, eps, residual, y, sel, sel_value, stream);
+    SK_J(1)
+    SK_J(2)
+    SK_J(3)
+    SK_J(4)
+    SK_J(6)
+    SK_J(8)
+    SK_J(12)
+    SK_J(16)
+#undef SK_J
+    default: return SK_E_SHAPE;
+  }
+}
+
+bool valid_width(int cols) { return cols >= 512 && cols <= 8192 && cols % 512 == 0; }
 
 }  // namespace
 }  // namespace sk
@@ -266,49 +296,34 @@ using namespace sk;
 extern "C" {
 
 int sk_gemv(const uint16_t* W, int32_t rows, int32_t cols, const float* x, int32_t prologue, const uint16_t* gamma,
-            float eps, const float* residual, float* y, const int32_t* sel, int32_t sel_value, hipStream_t stream) {
+            float eps, const float* residual, int32_t epilogue, float* y, const int32_t* sel, int32_t sel_value,
+            hipStream_t stream) {
   if (!W || !x || !y) return SK_E_NULL;
-  if (prologue < SK_PRO_NONE || prologue > SK_PRO_SWIGLU || rows < 1) return SK_E_RANGE;
+  if (prologue < SK_PRO_NONE || prologue > SK_PRO_RMSNORM || rows < 1) return SK_E_RANGE;
+  if (epilogue < SK_EPI_STORE || epilogue > SK_EPI_SWIGLU) return SK_E_RANGE;
+  if (epilogue == SK_EPI_SWIGLU && residual) return SK_E_RANGE;
   if (prologue == SK_PRO_RMSNORM && !gamma) return SK_E_NULL;
   if (!valid_width(cols)) return SK_E_SHAPE;
   if (x == y) return SK_E_RANGE;
-  switch (cols / 512) {
-    case 1: return launch_gemv_j<1, 2>(W, rows, cols, x, prologue, gamma, eps, residual, y, sel, sel_value, stream);
-    case 2: return launch_gemv_j<2, 2>(W, rows, cols, x, prologue, gamma, eps, residual, y, sel, sel_value, stream);
-    case 3: return launch_gemv_j<3, 2>(W, rows, cols, x, prologue, gamma, eps, residual, y, sel, sel_value, stream);
-    case 4: return launch_gemv_j<4, 2>(W, rows, cols, x, prologue, gamma, eps, residual, y, sel, sel_value, stream);
-    case 6: return launch_gemv_j<6, 2>(W, rows, cols, x, prologue, gamma, eps, residual, y, sel, sel_value, stream);
-    case 8: return launch_gemv_j<8, 2>(W, rows, cols, x, prologue, gamma, eps, residual, y, sel, sel_value, stream);
-    case 12: return launch_gemv_j<12, 1>(W, rows, cols, x, prologue, gamma, eps, residual, y, sel, sel_value, stream);
-    case 16: return launch_gemv_j<16, 1>(W, rows, cols, x, prologue, gamma, eps, residual, y, sel, sel_value, stream);
-    case 24: return launch_gemv_j<24, 1>(W, rows, cols, x, prologue, gamma, eps, residual, y, sel, sel_value, stream);
-    case 32: return launch_gemv_j<32, 1>(W, rows, cols, x, prologue, gamma, eps, residual, y, sel, sel_value, stream);
-    default: return SK_E_SHAPE;
-  }
+  return launch_gemv(W, rows, cols, x, prologue, epilogue, gamma, eps, residual, y, sel, sel_value, stream);
 }
 
 int sk_qkv_rope(const uint16_t* W_qkv, const float* h, const uint16_t* g_attn, const uint16_t* g_q,
                 const uint16_t* g_k, int32_t hidden, int32_t q_heads, int32_t kv_heads, float eps, float rope_base,
-                const int32_t* seq_lens, float* q_out, uint16_t* k_out, uint16_t* v_out, const int32_t* sel,
-                int32_t sel_value, hipStream_t stream) {
-  if (!W_qkv || !h || !g_attn || !g_q || !g_k || !seq_lens || !q_out || !k_out || !v_out) return SK_E_NULL;
+                const int32_t* seq_lens, float* scratch, float* q_out, uint16_t* k_out, uint16_t* v_out,
+                const int32_t* sel, int32_t sel_value, hipStream_t stream) {
+  if (!W_qkv || !h || !g_attn || !g_q || !g_k || !seq_lens || !scratch || !q_out || !k_out || !v_out)
+    return SK_E_NULL;
   if (kv_heads < 1 || q_heads < 1 || q_heads % kv_heads != 0) return SK_E_HEADS;
   if (q_heads + 2 * kv_heads > 65535 || !(rope_base > 0.f)) return SK_E_RANGE;
-  if (!valid_width(hidden) || hidden > 4096) return SK_E_SHAPE;
-  switch (hidden / 512) {
-#define SK_QKV(JJ) \
-  case JJ:         \
-    return launch_qkv_j<JJ>(W_qkv, h, g_attn, g_q, g_k, hidden, q_heads, kv_heads, eps, rope_base, seq_lens, q_out, \
-                            k_out, v_out, sel, sel_value, stream);
-    SK_QKV(1)
-    SK_QKV(2)
-    SK_QKV(3)
-    SK_QKV(4)
-    SK_QKV(6)
-    SK_QKV(8)
-#undef SK_QKV
-    default: return SK_E_SHAPE;
-  }
+  if (!valid_width(hidden)) return SK_E_SHAPE;
+  const int heads = q_heads + 2 * kv_heads;
+  int st = launch_gemv(W_qkv, heads * kHeadDim, hidden, h, SK_PRO_RMSNORM, SK_EPI_STORE, g_attn, eps, nullptr,
+                       scratch, sel, sel_value, stream);
+  if (st) return st;
+  hipLaunchKernelGGL(qk_finish_kernel, dim3(unsigned(heads)), dim3(kHeadDim), 0, stream, scratch, g_q, g_k, q_heads,
+                     kv_heads, eps, rope_base, seq_lens, q_out, k_out, v_out, sel, sel_value);
+  return launch_status(hipGetLastError());
 }
 
 int sk_rmsnorm(const float* x, const uint16_t* gamma, int32_t dim, float eps, float* out, const int32_t* sel,

@@ -10,10 +10,10 @@ ones committed. Here every launch of the recall pass carries the gate as its
 selector, so the step is one fixed sequence of launches (a HIP graph) with no host
 round trip ("Developer perspective").
 
-Layer (Qwen3-family, per launch): sk_qkv_rope (RMSNorm, q/k/v projection, per-head
-q/k norm, RoPE; the k/v candidate in bf16) -> oda_decode_local / oda_decode_full
-(attention with the candidate committed at n-1) -> sk_gemv W_o (+ residual) ->
-sk_gemv W_gate|up (RMSNorm prologue) -> sk_gemv W_down (SwiGLU prologue, + residual).
+Layer (Qwen3-family): sk_qkv_rope (RMSNorm, q/k/v projection, per-head q/k norm,
+RoPE; the k/v candidate in bf16) -> oda_decode_local / oda_decode_full (attention with
+the candidate committed at n-1) -> sk_gemv W_o (+ residual) -> sk_gemv W_gate|up
+(RMSNorm prologue, SwiGLU epilogue) -> sk_gemv W_down (+ residual).
 
 This module only sequences library calls; it computes nothing itself.
 """
@@ -62,7 +62,8 @@ class ODADecoder:
         self.k = torch.zeros((1, s.kv_heads, D), dtype=torch.bfloat16, device=dev)
         self.v = torch.zeros_like(self.k)
         self.attn = torch.zeros((1, s.q_heads, D), dtype=f32, device=dev)
-        self.gu = torch.zeros(2 * s.intermediate, dtype=f32, device=dev)
+        self.act = torch.zeros(s.intermediate, dtype=f32, device=dev)  # SiLU(gate) * up
+        self.qkv_raw = torch.zeros((s.q_heads + 2 * s.kv_heads) * D, dtype=f32, device=dev)
         self.qscore = torch.zeros(1, dtype=f32, device=dev)
         self.gate = torch.zeros(1, dtype=torch.int32, device=dev)
         self.ws = ops.workspace(1, s.q_heads, dev)
@@ -79,8 +80,8 @@ class ODADecoder:
     def _layer(self, l, h, full, sel):
         s, w = self.s, self.w
         ops.qkv_rope(w["qkv.%d" % l], h, w["g_attn.%d" % l], w["g_q.%d" % l], w["g_k.%d" % l], s.q_heads,
-                     s.kv_heads, self.seq_lens, self.q, self.k, self.v, eps=s.eps, rope_base=s.rope_base,
-                     sel=sel, sel_value=1)
+                     s.kv_heads, self.seq_lens, self.qkv_raw, self.q, self.k, self.v, eps=s.eps,
+                     rope_base=s.rope_base, sel=sel, sel_value=1)
         if full and l not in self.local_only:
             ops.oda_decode_full(self.q, self.caches[l], self.k, self.v, self.scale, sel=sel, sel_value=1,
                                 out=self.attn, ws=self.ws)
@@ -88,9 +89,9 @@ class ODADecoder:
             ops.oda_decode_local(self.q, self.caches[l], self.k, self.v, self.sinks, self.window, self.scale,
                                  sel=sel, sel_value=1, out=self.attn, ws=self.ws)
         ops.gemv(w["o.%d" % l], self.attn.view(-1), h, residual=h, sel=sel)
-        ops.gemv(w["gu.%d" % l], h, self.gu, prologue=ops.PRO_RMSNORM, gamma=w["g_mlp.%d" % l], eps=s.eps,
-                 sel=sel)
-        ops.gemv(w["down.%d" % l], self.gu, h, prologue=ops.PRO_SWIGLU, residual=h, sel=sel)
+        ops.gemv(w["gu.%d" % l], h, self.act, prologue=ops.PRO_RMSNORM, gamma=w["g_mlp.%d" % l], eps=s.eps,
+                 epilogue=ops.EPI_SWIGLU, sel=sel)
+        ops.gemv(w["down.%d" % l], self.act, h, residual=h, sel=sel)
 
     def local_pass(self):
         d = self.s.hidden

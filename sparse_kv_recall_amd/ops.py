@@ -247,7 +247,8 @@ def da_decode_blocks(q, kv, keep_mask, k_new=None, v_new=None, scale=None, sel=N
 
 # ---- dense layers of the weight-bearing decode step (batch 1)
 
-PRO_NONE, PRO_RMSNORM, PRO_SWIGLU = 0, 1, 2
+PRO_NONE, PRO_RMSNORM = 0, 1
+EPI_STORE, EPI_SWIGLU = 0, 1
 
 
 def _sel_args(sel, sel_value):
@@ -256,38 +257,43 @@ def _sel_args(sel, sel_value):
     return (0 if sel is None else sel.data_ptr()), int(sel_value)
 
 
-def gemv(W, x, y, prologue=PRO_NONE, gamma=None, eps=1e-6, residual=None, sel=None, sel_value=1):
-    """y[r] = W[r] . x' (+ residual[r]); W bf16 [rows][cols]; x' = x, RMSNorm(x) * gamma
-    (PRO_RMSNORM) or SiLU(x[:cols]) * x[cols:] (PRO_SWIGLU)."""
-    rows, cols = W.shape
+def gemv(W, x, y, prologue=PRO_NONE, gamma=None, eps=1e-6, residual=None, epilogue=EPI_STORE, sel=None,
+         sel_value=1):
+    """y[r] = W[r] . x' (+ residual[r]) with x' = x or RMSNorm(x) * gamma; with
+    EPI_SWIGLU, W holds 2*rows rows and y[r] = SiLU(W[r] . x') * (W[rows + r] . x')."""
+    wr, cols = W.shape
+    rows = wr // 2 if epilogue == EPI_SWIGLU else wr
     _check(W, torch.bfloat16, "W")
-    _check(x, torch.float32, "x", 2 * cols if prologue == PRO_SWIGLU else cols)
+    _check(x, torch.float32, "x", cols)
     _check(y, torch.float32, "y", rows)
     _check(gamma, torch.bfloat16, "gamma", cols)
     _check(residual, torch.float32, "residual", rows)
     s, sv = _sel_args(sel, sel_value)
     _lib.call("sk_gemv", W.data_ptr(), rows, cols, x.data_ptr(), int(prologue), _ptr(gamma), float(eps),
-              _ptr(residual), y.data_ptr(), s, sv, _stream(W.device))
+              _ptr(residual), int(epilogue), y.data_ptr(), s, sv, _stream(W.device))
     return y
 
 
-def qkv_rope(W_qkv, h, g_attn, g_q, g_k, q_heads, kv_heads, seq_lens, q_out, k_out, v_out, eps=1e-6,
+def qkv_rope(W_qkv, h, g_attn, g_q, g_k, q_heads, kv_heads, seq_lens, scratch, q_out, k_out, v_out, eps=1e-6,
              rope_base=1.0e6, sel=None, sel_value=1):
-    """Attention inputs of one token (RMSNorm, q/k/v projection, per-head q/k norm, RoPE
-    at position seq_lens[0] - 1); q_out fp32 [Hq*128], k_out / v_out bf16 [Hkv*128]."""
+    """Attention inputs of one token (RMSNorm, q/k/v projection into scratch, per-head q/k
+    norm, RoPE at position seq_lens[0] - 1); q_out fp32 [Hq*128], k_out / v_out bf16
+    [Hkv*128]; scratch fp32 [(Hq + 2 Hkv) * 128]."""
     hidden = h.numel()
-    _check(W_qkv, torch.bfloat16, "W_qkv", (q_heads + 2 * kv_heads) * HEAD_DIM * hidden)
+    heads = q_heads + 2 * kv_heads
+    _check(W_qkv, torch.bfloat16, "W_qkv", heads * HEAD_DIM * hidden)
     _check(h, torch.float32, "h")
     for t, n in ((g_attn, hidden), (g_q, HEAD_DIM), (g_k, HEAD_DIM)):
         _check(t, torch.bfloat16, "gamma", n)
     _check(seq_lens, torch.int32, "seq_lens", 1)
+    _check(scratch, torch.float32, "scratch", heads * HEAD_DIM)
     _check(q_out, torch.float32, "q_out", q_heads * HEAD_DIM)
     _check(k_out, torch.bfloat16, "k_out", kv_heads * HEAD_DIM)
     _check(v_out, torch.bfloat16, "v_out", kv_heads * HEAD_DIM)
     s, sv = _sel_args(sel, sel_value)
     _lib.call("sk_qkv_rope", W_qkv.data_ptr(), h.data_ptr(), g_attn.data_ptr(), g_q.data_ptr(), g_k.data_ptr(),
               hidden, int(q_heads), int(kv_heads), float(eps), float(rope_base), seq_lens.data_ptr(),
-              q_out.data_ptr(), k_out.data_ptr(), v_out.data_ptr(), s, sv, _stream(h.device))
+              scratch.data_ptr(), q_out.data_ptr(), k_out.data_ptr(), v_out.data_ptr(), s, sv, _stream(h.device))
 
 
 def rmsnorm(x, gamma, out, eps=1e-6, sel=None, sel_value=1):
