@@ -74,6 +74,21 @@ def test_other_entry_points_validation():
     assert L.da_declare(FAKE, FAKE, None, 0, FAKE, tags, kv(), 1024, FAKE, None, None) == SK_E_NULL
     assert L.da_decode_blocks(FAKE, kv(), None, None, None, FAKE, FAKE, FAKE, 0.1, None, 2, FAKE, FAKE,
                               1 << 30, None) == SK_E_NULL
+    # dense layers of the weight-bearing step
+    assert L.sk_gemv(None, 8, 512, FAKE, 0, None, 1e-6, None, 0, FAKE + 64, None, 0, None) == SK_E_NULL
+    assert L.sk_gemv(FAKE, 8, 500, FAKE, 0, None, 1e-6, None, 0, FAKE + 64, None, 0, None) == SK_E_SHAPE
+    assert L.sk_gemv(FAKE, 8, 5120, FAKE, 0, None, 1e-6, None, 0, FAKE + 64, None, 0, None) == SK_E_SHAPE
+    assert L.sk_gemv(FAKE, 8, 512, FAKE, 1, None, 1e-6, None, 0, FAKE + 64, None, 0, None) == SK_E_NULL
+    assert L.sk_gemv(FAKE, 8, 512, FAKE, 0, None, 1e-6, FAKE, 1, FAKE + 64, None, 0, None) == SK_E_RANGE
+    assert L.sk_gemv(FAKE, 8, 512, FAKE, 0, None, 1e-6, None, 0, FAKE, None, 0, None) == SK_E_RANGE   # y == x
+    assert L.sk_gemv(FAKE, 0, 512, FAKE, 0, None, 1e-6, None, 0, FAKE + 64, None, 0, None) == SK_E_RANGE
+    qa = [FAKE] * 5
+    assert L.sk_qkv_rope(*qa, 2048, 16, 6, 1e-6, 1e6, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None) == SK_E_HEADS
+    assert L.sk_qkv_rope(*qa, 2000, 16, 8, 1e-6, 1e6, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None) == SK_E_SHAPE
+    assert L.sk_qkv_rope(*qa, 2048, 16, 8, 1e-6, 1e6, FAKE, None, FAKE, FAKE, FAKE, None, 0, None) == SK_E_NULL
+    assert L.sk_rmsnorm(FAKE, FAKE, 0, 1e-6, FAKE, None, 0, None) == SK_E_RANGE
+    assert L.sk_embed(FAKE, 0, 8, FAKE, FAKE, None, None, 0, None) == SK_E_RANGE
+    assert L.sk_select(None, 1, FAKE, FAKE, 8, FAKE, None) == SK_E_NULL
     assert L.sk_kv_write(kv(), 1, 0, 1, FAKE, FAKE, None, None) == SK_E_RANGE       # request >= batch
     assert L.sk_kv_write(kv(), 0, 1599, 2, FAKE, FAKE, None, None) == SK_E_RANGE    # past max_blocks*16
     assert L.sk_kv_write(kv(), 0, 0, 1, None, FAKE, None, None) == SK_E_NULL
