@@ -89,11 +89,14 @@ def roofline_full(stack, feeder, reps):
 def roofline_blocks(stack, feeder, reps, seed=11):
     """Block-list (Declarative-Attention) decode over the same 36 pools at the current n,
     through a seeded permutation of the block table, keeping (a) every block and (b) a
-    seeded 12.5 % of the blocks plus the last one. Times the whole da_decode_blocks call
-    (gather + attention) with HIP events; returns achieved GB/s of algorithmic bytes."""
+    seeded 12.5 % of the blocks plus the last one. Three graphs, each timed with HIP
+    events per layer: da_decode_blocks in every layer (rewrite + attention), one
+    da_gather per step and da_decode_gathered per layer, and the decode kernel alone;
+    returns achieved GB/s of algorithmic bytes for each."""
     import numpy as np
     import torch
     from sparse_kv_recall_amd import ops
+    from sparse_kv_recall_amd.stack import capture_graph
     c0 = stack.caches[0]
     n = int(stack.seq_lens[0].item())
     nb = (n + 15) // 16
@@ -118,22 +121,40 @@ def roofline_blocks(stack, feeder, reps, seed=11):
         num = torch.zeros(1, dtype=torch.int32, device="cuda")
         positions = int(sum(min(16, n - 16 * int(b)) for b in kept))
 
-        def run():
+        def per_call():  # the rewrite repeated in every layer's call
             for l, v in enumerate(views):
                 ops.da_decode_blocks(feeder.q[l, 1], v, mt, scale=stack.scale, out=stack.out[l], gathered=gat,
                                      gathered_cnt=cnt, num_kept=num, ws=stack.ws)
-        run()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(reps):
-            run()
-        e1.record()
-        e1.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / (reps * len(views))
+
+        def per_step():  # one rewrite per step, one decode launch per layer
+            ops.da_gather(views[0], mt, gathered=gat, gathered_cnt=cnt, num_kept=num, ws=stack.ws)
+            for l, v in enumerate(views):
+                ops.da_decode_gathered(feeder.q[l, 1], v, gat, cnt, num, scale=stack.scale, out=stack.out[l],
+                                       ws=stack.ws)
+
+        def decode_only():  # the block-list decode kernel alone, list already gathered
+            for l, v in enumerate(views):
+                ops.da_decode_gathered(feeder.q[l, 1], v, gat, cnt, num, scale=stack.scale, out=stack.out[l],
+                                       ws=stack.ws)
+
         nbytes = positions * stack.Hkv * 128 * 4 + 2 * stack.Hq * 128 * 4
-        out[name] = {"kept_positions": positions, "us_per_call": round(us, 2),
-                     "achieved_GBs": round(nbytes / (us * 1e-6) / 1e9, 1),
-                     "frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+        res = {"kept_positions": positions}
+        for key, fn in (("gather_in_every_call", per_call), ("gather_once_per_step", per_step),
+                        ("decode_kernel", decode_only)):
+            graph = capture_graph(fn)
+            graph.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                graph.replay()
+            e1.record()
+            e1.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / (reps * len(views))
+            res[key] = {"us_per_layer": round(us, 2), "achieved_GBs": round(nbytes / (us * 1e-6) / 1e9, 1),
+                        "frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+            del graph
+        out[name] = res
     return out
 
 
@@ -524,8 +545,9 @@ def main():
                      "us_per_launch": round(full_ms * 1e3, 2), "algorithmic_bytes_per_launch": int(bytes_full),
                      "traffic_source": "profiles/decode_128k_hbm_counters.md (rocprofv3 FETCH_SIZE x2.0 + "
                                        "WRITE_SIZE x1.0, rescaled to this n); null if the kernel changed"},
-        "roofline_block_sparse": dict(blocks, kernel="da_decode_blocks (gather + decode_kernel<list>), permuted "
-                                      "block table, 36-layer rotation, n=%d" % n_now),
+        "roofline_block_sparse": dict(blocks, kernel="decode_kernel<list> over a permuted block table (36-layer "
+                                      "rotation, n=%d); also per layer with the rewrite (gather) in every call and "
+                                      "once per step" % n_now),
         "always_full_baseline": dict(full_only, speedup_of_oda=round(tok_s / full_only["tok_s"], 3),
                                      attention_bytes_ratio=round(float(full_bytes / step_bytes), 3)),
         "hybrid_local_only": hybrid,

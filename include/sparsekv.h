@@ -322,6 +322,24 @@ int da_decode_blocks(const float* q, sk_paged_kv kv, const void* k_new, const vo
                      int32_t* num_kept, float scale, const int32_t* sel, int32_t sel_value,
                      float* out, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* The two halves of da_decode_blocks, for callers that attend one rewritten
+ * block table from several layers ([DA] section 3: the engine rewrites the
+ * block table once per declaration; every attention layer of the step reads
+ * the same kept blocks). da_gather writes gathered / gathered_cnt / num_kept
+ * for every selected request exactly as da_decode_blocks does (one launch);
+ * da_decode_gathered attends the given list (entries in ascending logical
+ * order, as da_gather writes them) with the current token committed as in
+ * da_decode_blocks (one launch). A physical id outside [0, num_phys_blocks)
+ * sets SK_DEVERR_BLOCK_ID and attends nothing for that entry. */
+int da_gather(sk_paged_kv kv, const uint32_t* keep_mask, int32_t* gathered,
+              int32_t* gathered_cnt, int32_t* num_kept, const int32_t* sel, int32_t sel_value,
+              void* ws, hipStream_t stream);
+int da_decode_gathered(const float* q, sk_paged_kv kv, const void* k_new, const void* v_new,
+                       const int32_t* gathered, const int32_t* gathered_cnt,
+                       const int32_t* num_kept, float scale, const int32_t* sel,
+                       int32_t sel_value, float* out, void* ws, size_t ws_bytes,
+                       hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

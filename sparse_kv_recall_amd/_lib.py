@@ -56,6 +56,10 @@ _SIGNATURES = {
     "sk_rmsnorm": (c_int32, [c_void_p, c_void_p, c_int32, c_float, c_void_p, c_void_p, c_int32, c_void_p]),
     "sk_embed": (c_int32, [c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_void_p]),
     "sk_select": (c_int32, [c_void_p, c_int32, c_void_p, c_void_p, c_int32, c_void_p, c_void_p]),
+    "da_gather": (c_int32, [PagedKVStruct, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_void_p,
+                            c_void_p]),
+    "da_decode_gathered": (c_int32, [c_void_p, PagedKVStruct, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                     c_float, c_void_p, c_int32, c_void_p, c_void_p, c_size_t, c_void_p]),
     "da_decode_blocks": (c_int32, [c_void_p, PagedKVStruct, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                    c_void_p, c_float, c_void_p, c_int32, c_void_p, c_void_p, c_size_t, c_void_p]),
 }

@@ -826,4 +826,23 @@ int da_decode_blocks(const float* q, sk_paged_kv kv, const void* k_new, const vo
                               out, ws, ws_bytes, stream);
 }
 
+int da_gather(sk_paged_kv kv, const uint32_t* keep_mask, int32_t* gathered, int32_t* gathered_cnt, int32_t* num_kept,
+              const int32_t* sel, int32_t sel_value, void* ws, hipStream_t stream) {
+  int st = check_kv(kv);
+  if (st) return st;
+  if (!keep_mask || !gathered || !gathered_cnt || !num_kept) return SK_E_NULL;
+  hipLaunchKernelGGL(gather_kernel, dim3(unsigned((kv.max_blocks + 255) / 256), unsigned(kv.batch)), dim3(256), 0,
+                     stream, kv, keep_mask, sel, sel_value, gathered, gathered_cnt, num_kept,
+                     reinterpret_cast<int32_t*>(ws));
+  return launch_status(hipGetLastError());
+}
+
+int da_decode_gathered(const float* q, sk_paged_kv kv, const void* k_new, const void* v_new, const int32_t* gathered,
+                       const int32_t* gathered_cnt, const int32_t* num_kept, float scale, const int32_t* sel,
+                       int32_t sel_value, float* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!gathered || !gathered_cnt || !num_kept) return SK_E_NULL;
+  return launch_decode<kList>(q, kv, k_new, v_new, 0, 1, scale, sel, sel_value, gathered, gathered_cnt, num_kept,
+                              out, ws, ws_bytes, stream);
+}
+
 }  // extern "C"

@@ -245,6 +245,41 @@ def da_decode_blocks(q, kv, keep_mask, k_new=None, v_new=None, scale=None, sel=N
     return out, gathered, gathered_cnt, num_kept
 
 
+def da_gather(kv, keep_mask, gathered=None, gathered_cnt=None, num_kept=None, sel=None, sel_value=MODE_BLOCKS,
+              ws=None):
+    """The block-table rewrite of da_decode_blocks alone (once per step for all layers)."""
+    words = (kv.max_blocks + 31) // 32
+    _check(keep_mask, torch.int32, "keep_mask", kv.batch * words)
+    dev = keep_mask.device
+    if gathered is None:
+        gathered = torch.zeros((kv.batch, kv.max_blocks), dtype=torch.int32, device=dev)
+    if gathered_cnt is None:
+        gathered_cnt = torch.zeros((kv.batch, kv.max_blocks), dtype=torch.int32, device=dev)
+    if num_kept is None:
+        num_kept = torch.zeros(kv.batch, dtype=torch.int32, device=dev)
+    _check(gathered, torch.int32, "gathered", kv.batch * kv.max_blocks)
+    _check(gathered_cnt, torch.int32, "gathered_cnt", kv.batch * kv.max_blocks)
+    _check(num_kept, torch.int32, "num_kept", kv.batch)
+    _check(sel, torch.int32, "sel", kv.batch)
+    _lib.call("da_gather", kv.abi(), keep_mask.data_ptr(), gathered.data_ptr(), gathered_cnt.data_ptr(),
+              num_kept.data_ptr(), _ptr(sel), int(sel_value), _ptr(ws), _stream(dev))
+    return gathered, gathered_cnt, num_kept
+
+
+def da_decode_gathered(q, kv, gathered, gathered_cnt, num_kept, k_new=None, v_new=None, scale=None, sel=None,
+                       sel_value=MODE_BLOCKS, out=None, ws=None):
+    """Attention over a gathered block list (da_gather's output), one launch."""
+    out, ws = _decode_common(q, kv, k_new, v_new, sel, out, ws)
+    _check(gathered, torch.int32, "gathered", kv.batch * kv.max_blocks)
+    _check(gathered_cnt, torch.int32, "gathered_cnt", kv.batch * kv.max_blocks)
+    _check(num_kept, torch.int32, "num_kept", kv.batch)
+    scale = 1.0 / math.sqrt(HEAD_DIM) if scale is None else float(scale)
+    _lib.call("da_decode_gathered", q.data_ptr(), kv.abi(), _ptr(k_new), _ptr(v_new), gathered.data_ptr(),
+              gathered_cnt.data_ptr(), num_kept.data_ptr(), scale, _ptr(sel), int(sel_value), out.data_ptr(),
+              ws.data_ptr(), ws.numel(), _stream(q.device))
+    return out
+
+
 # ---- dense layers of the weight-bearing decode step (batch 1)
 
 PRO_NONE, PRO_RMSNORM = 0, 1

@@ -74,6 +74,9 @@ def test_other_entry_points_validation():
     assert L.da_declare(FAKE, FAKE, None, 0, FAKE, tags, kv(), 1024, FAKE, None, None) == SK_E_NULL
     assert L.da_decode_blocks(FAKE, kv(), None, None, None, FAKE, FAKE, FAKE, 0.1, None, 2, FAKE, FAKE,
                               1 << 30, None) == SK_E_NULL
+    assert L.da_gather(kv(), None, FAKE, FAKE, FAKE, None, 2, None, None) == SK_E_NULL
+    assert L.da_decode_gathered(FAKE, kv(), None, None, None, FAKE, FAKE, 0.1, None, 2, FAKE, FAKE, 1 << 30,
+                                None) == SK_E_NULL
     # dense layers of the weight-bearing step
     assert L.sk_gemv(None, 8, 512, FAKE, 0, None, 1e-6, None, 0, FAKE + 64, None, 0, None) == SK_E_NULL
     assert L.sk_gemv(FAKE, 8, 500, FAKE, 0, None, 1e-6, None, 0, FAKE + 64, None, 0, None) == SK_E_SHAPE

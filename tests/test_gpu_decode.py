@@ -230,6 +230,49 @@ def test_blocks_all_kept_equals_full_and_commit_when_unkept():
         assert np.array_equal(bf16_tensor_to_bits(vr)[0], vn[b])
 
 
+def test_gather_once_decode_per_layer():
+    # one block-table rewrite serves several layers: da_gather + da_decode_gathered give
+    # exactly what da_decode_blocks gives for each layer's query
+    from sparse_kv_recall_amd import ops
+    Hq, Hkv = 32, 8
+    g = np.random.default_rng(41)
+    ns = [5000, 700, 16]
+    hc = HostCache(Hq, Hkv, ns, seed=42)
+    kept = [sorted(set(g.choice((n + 15) // 16, size=max(1, (n + 15) // 64), replace=False).tolist())) for n in ns]
+    mask = torch.as_tensor(_mask_words(kept, hc.max_blocks).view(np.int32), device="cuda")
+    gat, cnt, num = ops.da_gather(hc.kv, mask)
+    for layer in range(3):
+        q = _q(Hq, len(ns), seed=50 + layer)
+        qt = torch.as_tensor(q, device="cuda")
+        o1 = ops.da_decode_gathered(qt, hc.kv, gat, cnt, num)
+        o2, g2, c2, n2 = ops.da_decode_blocks(qt, hc.kv, mask)
+        assert torch.equal(o1, o2) and torch.equal(gat, g2) and torch.equal(cnt, c2) and torch.equal(num, n2)
+        for b, n in enumerate(ns):
+            ref = attention.attend(q[b], hc.k[b], hc.v[b], keysets.block_keys(n, kept[b]), SCALE)
+            check_close(o1.cpu().numpy()[b], ref, abs_tol=1e-5, row_rel_tol=1e-4)
+
+
+def test_gathered_list_with_bad_block_id():
+    # a caller-built list naming a block outside the pool: error bit, that entry attends nothing
+    from sparse_kv_recall_amd import ops
+    Hq, Hkv = 8, 2
+    ns = [300]
+    hc = HostCache(Hq, Hkv, ns, seed=43)
+    mb = hc.max_blocks
+    gat = torch.zeros((1, mb), dtype=torch.int32, device="cuda")
+    cnt = torch.zeros_like(gat)
+    blocks = [0, 3, 7]
+    gat[0, :3] = torch.as_tensor([int(hc.bt[0][0]), 10 ** 6, int(hc.bt[0][7])], dtype=torch.int32)
+    cnt[0, :3] = torch.as_tensor([16, 16, 16], dtype=torch.int32)
+    num = torch.full((1,), 3, dtype=torch.int32, device="cuda")
+    q = _q(Hq, 1, seed=13)
+    ws = ops.workspace(1, Hq)
+    out = ops.da_decode_gathered(torch.as_tensor(q, device="cuda"), hc.kv, gat, cnt, num, ws=ws)
+    assert ops.workspace_error(ws) & 1  # SK_DEVERR_BLOCK_ID
+    ref = attention.attend(q[0], hc.k[0], hc.v[0], keysets.block_keys(300, [blocks[0], blocks[2]]), SCALE)
+    check_close(out.cpu().numpy()[0], ref, abs_tol=1e-5, row_rel_tol=1e-4)
+
+
 def test_keep_mask_modes():
     from sparse_kv_recall_amd import ops
     Hq, Hkv = 8, 2
