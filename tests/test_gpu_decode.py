@@ -273,6 +273,58 @@ def test_gathered_list_with_bad_block_id():
     check_close(out.cpu().numpy()[0], ref, abs_tol=1e-5, row_rel_tol=1e-4)
 
 
+def test_large_batch_all_views_with_selector():
+    # batches above 64 take the workgroup (LDS) planning path: Full, Local and block
+    # lists with a per-request selector and fused commits, 100 ragged requests
+    from sparse_kv_recall_amd import ops
+    Hq, Hkv = 8, 2
+    g = np.random.default_rng(61)
+    B = 100
+    ns = [int(x) for x in g.integers(1, 2600, size=B)]
+    ns[:4] = [1, 16, 17, 2500]
+    hc = HostCache(Hq, Hkv, ns, seed=62)
+    q = _q(Hq, B, seed=63)
+    qt = torch.as_tensor(q, device="cuda")
+    view = g.integers(0, 3, size=B).astype(np.int32)  # 0 local, 1 full, 2 blocks
+    kept = []
+    for n in ns:
+        nb = (n + 15) // 16
+        kept.append(sorted(set(g.choice(nb, size=max(1, nb // 3), replace=False).tolist()) | {nb - 1}))
+    mask = torch.as_tensor(_mask_words(kept, hc.max_blocks).view(np.int32), device="cuda")
+    kn = rand_bits(rng.mix_key(905, 1), B, Hkv)
+    vn = rand_bits(rng.mix_key(905, 2), B, Hkv)
+    kt, vt = bits_to_bf16_tensor(kn), bits_to_bf16_tensor(vn)
+    sel = torch.as_tensor(view, device="cuda")
+    out = torch.full((B, Hq, 128), 7.0, device="cuda")
+    ops.oda_decode_local(qt, hc.kv, kt, vt, sinks=4, window=64, sel=sel, sel_value=0, out=out)
+    ops.oda_decode_full(qt, hc.kv, kt, vt, sel=sel, sel_value=1, out=out)
+    ops.da_decode_blocks(qt, hc.kv, mask, kt, vt, sel=sel, sel_value=2, out=out)
+    got = out.cpu().numpy()
+    for b, n in enumerate(ns):
+        k, v = hc.k[b].copy(), hc.v[b].copy()
+        oracle.oda.commit(k, v, n, kn[b], vn[b])
+        keys = (keysets.local_keys(n, 4, 64), keysets.full_keys(n), keysets.block_keys(n, kept[b]))[view[b]]
+        ref = attention.attend(q[b], k, v, keys, SCALE)
+        check_close(got[b], ref, abs_tol=1e-5, row_rel_tol=1e-4, what="b=%d n=%d view=%d" % (b, n, view[b]))
+        kr, vr = ops.kv_read(hc.kv, b, n - 1, 1)
+        assert np.array_equal(bf16_tensor_to_bits(kr)[0], kn[b]) and np.array_equal(bf16_tensor_to_bits(vr)[0], vn[b])
+
+
+def test_maximum_batch():
+    # 1024 requests (the library's maximum batch), short ragged histories
+    from sparse_kv_recall_amd import ops
+    Hq, Hkv = 8, 2
+    g = np.random.default_rng(64)
+    B = 1024
+    ns = [int(x) for x in g.integers(1, 48, size=B)]
+    hc = HostCache(Hq, Hkv, ns, seed=65, poison=False)
+    q = _q(Hq, B, seed=66)
+    out = ops.oda_decode_full(torch.as_tensor(q, device="cuda"), hc.kv).cpu().numpy()
+    for b in range(0, B, 7):
+        ref = attention.attend(q[b], hc.k[b], hc.v[b], keysets.full_keys(ns[b]), SCALE)
+        check_close(out[b], ref, abs_tol=1e-5, row_rel_tol=1e-4, what="b=%d" % b)
+
+
 def test_keep_mask_modes():
     from sparse_kv_recall_amd import ops
     Hq, Hkv = 8, 2
