@@ -11,7 +11,8 @@
 // The head here is a two-layer MLP, q = <w2, GELU(W1 x + b1)> + b2 (exact-erf GELU).
 // It is a GEMV: each wave keeps one row of W1 (in_dim fp32) in registers and dots it
 // with every request's x; no matrix cores are used. Per-workgroup partial sums are
-// added in a fixed order by the last workgroup (atomic ticket), so q is deterministic.
+// published with device-coherent stores and added in a fixed order by the last
+// workgroup (atomic ticket), so q is deterministic.
 #include <math.h>
 
 #include "sk_internal.h"
@@ -22,6 +23,7 @@ namespace {
 constexpr int kRecallMaxBatch = 64;
 constexpr int kRecallMaxIn = 65536;
 constexpr int kRecallWaves = 4;  // one W1 row per wave
+constexpr int kRecallMaxParts = 8192;  // workgroups x batch partial sums the last workgroup stages
 
 __device__ inline float gelu_erf(float a) { return 0.5f * a * (1.0f + erff(a * 0.70710678118654752f)); }
 
@@ -35,6 +37,7 @@ __global__ __launch_bounds__(256) void recall_kernel(const float* __restrict__ x
                                                      int32_t* __restrict__ gate_out, float* partials,
                                                      uint32_t* ticket) {
   __shared__ float s_c[kRecallWaves][kRecallMaxBatch];
+  __shared__ float s_part[kRecallMaxParts];
   __shared__ int s_last;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int row = blockIdx.x * kRecallWaves + wave;
@@ -72,21 +75,27 @@ __global__ __launch_bounds__(256) void recall_kernel(const float* __restrict__ x
     if (lane == 0) s_c[wave][b] = (row < hidden) ? w2[row] * gelu_erf(dot + b1[row]) : 0.f;
   }
   __syncthreads();
+  // Workgroup sums are published with device-coherent stores; once they have completed,
+  // one thread takes the ticket. The last workgroup loads every workgroup's sums in one
+  // round of device-coherent loads into LDS and adds them in workgroup order.
   for (int b = tid; b < B; b += blockDim.x) {
     float s = 0.f;
 #pragma unroll
     for (int i = 0; i < kRecallWaves; ++i) s += s_c[i][b];
-    partials[size_t(blockIdx.x) * B + b] = s;
+    __hip_atomic_store(&partials[size_t(blockIdx.x) * B + b], s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  __threadfence();
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's stores have completed
   __syncthreads();
   if (tid == 0) s_last = (atomicAdd(ticket, 1u) == gridDim.x - 1);
   __syncthreads();
   if (!s_last) return;
-  __threadfence();
+  const int total = int(gridDim.x) * B;
+  for (int e = tid; e < total; e += blockDim.x)
+    s_part[e] = __hip_atomic_load(&partials[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
   for (int b = tid; b < B; b += blockDim.x) {
     float s = 0.f;
-    for (unsigned i = 0; i < gridDim.x; ++i) s += partials[size_t(i) * B + b];
+    for (unsigned i = 0; i < gridDim.x; ++i) s += s_part[i * B + b];
     float q = s + b2[0];
     q_out[b] = q;
     gate_out[b] = (q > theta) ? 1 : 0;
@@ -213,7 +222,9 @@ int oda_recall_score(const float* x, const float* W1, const float* b1, const flo
   if (!x || !W1 || !b1 || !w2 || !b2 || !q_out || !gate_out || !ws) return SK_E_NULL;
   if (batch < 1 || batch > kRecallMaxBatch || in_dim < 4 || in_dim > kRecallMaxIn || (in_dim % 4) || hidden < 1)
     return SK_E_RANGE;
-  size_t need = kPartialsOffset + size_t((hidden + kRecallWaves - 1) / kRecallWaves) * batch * 4;
+  const size_t parts = size_t((hidden + kRecallWaves - 1) / kRecallWaves) * batch;
+  if (parts > size_t(kRecallMaxParts)) return SK_E_RANGE;
+  size_t need = kPartialsOffset + parts * 4;
   if (ws_bytes < need) return SK_E_WORKSPACE;
   int chunks = (in_dim / 4 + 63) / 64;  // float4 per lane
   if (chunks <= 8) return launch_recall<8>(x, W1, b1, w2, b2, batch, in_dim, hidden, theta, q_out, gate_out, ws, stream);

@@ -345,7 +345,7 @@ def test_keep_mask_modes():
 def test_recall_head_small():
     from sparse_kv_recall_amd import ops
     g = np.random.default_rng(3)
-    for B, din, hid in ((1, 6144, 512), (3, 100, 7), (5, 2048, 33)):
+    for B, din, hid in ((1, 6144, 512), (3, 100, 7), (5, 2048, 33), (64, 512, 128), (2, 20000, 40)):
         x = g.standard_normal((B, din)).astype(np.float32)
         W1 = (g.standard_normal((hid, din)) * 0.02).astype(np.float32)
         b1 = (g.standard_normal(hid) * 0.1).astype(np.float32)
@@ -354,6 +354,8 @@ def test_recall_head_small():
         dev = lambda a: torch.as_tensor(a, device="cuda")
         qo, go = ops.oda_recall_score(dev(x), dev(W1), dev(b1), dev(w2), dev(b2), theta=0.0)
         qo, go = qo.cpu().numpy(), go.cpu().numpy()
+        q2, _ = ops.oda_recall_score(dev(x), dev(W1), dev(b1), dev(w2), dev(b2), theta=0.0)
+        assert np.array_equal(q2.cpu().numpy(), qo)  # fixed reduction order
         for b in range(B):
             ref = oracle.recall.recall_score(x[b], W1, b1, w2, b2)
             assert abs(qo[b] - ref) <= 1e-5 * max(1.0, abs(ref)), (qo[b], ref)
