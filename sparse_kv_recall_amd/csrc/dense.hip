@@ -205,8 +205,13 @@ __global__ __launch_bounds__(kHeadDim) void qk_finish_kernel(const float* __rest
   float o = v;
   if (!is_v) {
     const int i = t & 63;
-    const double ang = double(seq_lens[0] - 1) * pow(double(rope_base), -double(i) / 64.0);
-    const float c = float(cos(ang)), s = float(sin(ang));
+    // angle in fp64, reduced to [-pi, pi] before the sine and cosine (|angle| < 2^31
+    // rad, so the reduction error stays far below fp32 resolution)
+    const double ang = double(seq_lens[0] - 1) * exp2(-double(i) / 64.0 * log2(double(rope_base)));
+    const double red = ang - 6.283185307179586 * rint(ang * 0.15915494309189535);
+    double sd, cd;
+    sincos(red, &sd, &cd);
+    const float c = float(cd), s = float(sd);
     o = (t < 64) ? v * c - s_val[t + 64] * s : v * c + s_val[t - 64] * s;
   }
   if (is_q) {
