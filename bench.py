@@ -86,6 +86,62 @@ def roofline_full(stack, feeder, reps):
     return e0.elapsed_time(e1) / (reps * stack.layers)
 
 
+def view_sweep(device, Hq=32, Hkv=8, reps=5, min_bytes=1 << 30):
+    """Full and Local views over context lengths at batch 1 and over batch sizes at 32K
+    positions per request (identity block tables, every request of equal length, 32 q /
+    8 KV heads). Each configuration rotates over enough layer pools that one graph replay
+    streams at least 1 GiB, so the pools are not cache resident; per launch time from HIP
+    events around the replays, and the fraction of 8 TB/s that the algorithmic bytes
+    (visible positions x 4096 B + q and out) give."""
+    import torch
+    from sparse_kv_recall_amd import ops
+    from sparse_kv_recall_amd.stack import capture_graph
+    from synth import device as sdev, rng
+
+    def one(view, B, n):
+        mb = (n + 15) // 16
+        keys = n if view == "full" else min(n, 2052)
+        layers = max(2, -(-min_bytes // (B * keys * Hkv * 512)))
+        bt = torch.arange(B * mb, dtype=torch.int32, device=device).view(B, mb)
+        sl = torch.full((B,), n, dtype=torch.int32, device=device)
+        caches = [ops.PagedKVCache(B * mb, B, Hq, Hkv, mb, block_tables=bt, seq_lens=sl, device=device)
+                  for _ in range(layers)]
+        for i, c in enumerate(caches):
+            sdev.fill_normal_(c.k_pool, rng.mix_key(5, 1, i), 0)
+            sdev.fill_normal_(c.v_pool, rng.mix_key(5, 2, i), 0)
+        q = torch.randn(layers, B, Hq, 128, device=device)
+        out = torch.zeros(layers, B, Hq, 128, device=device)
+        ws = ops.workspace(B, Hq, device)
+        if view == "full":
+            fn = lambda: [ops.oda_decode_full(q[l], caches[l], out=out[l], ws=ws) for l in range(layers)]
+        else:
+            fn = lambda: [ops.oda_decode_local(q[l], caches[l], out=out[l], ws=ws) for l in range(layers)]
+        g = capture_graph(fn)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        e1.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / (reps * layers)
+        nbytes = B * (keys * Hkv * 512 + 2 * Hq * 512)
+        del g, caches
+        torch.cuda.empty_cache()
+        return {"view": view, "batch": B, "n": n, "us_per_launch": round(us, 2),
+                "frac_of_peak": round(nbytes / (us * 1e-6) / (HBM_PEAK_GBS * 1e9), 3)}
+
+    cases = [("full", 1, n) for n in (4096, 16384, 32768, 65536, 131072, 262144)]
+    cases += [("full", B, 32768) for B in (2, 4, 8, 12, 16, 24, 32)]
+    cases += [("local", B, 32768) for B in (1, 8, 32, 64)]
+    res = []
+    for view, B, n in cases:
+        res.append(one(view, B, n))
+        log("sweep: %s" % json.dumps(res[-1]))
+    return res
+
+
 def roofline_blocks(stack, feeder, reps, seed=11):
     """Block-list (Declarative-Attention) decode over the same 36 pools at the current n,
     through a seeded permutation of the block table, keeping (a) every block and (b) a
@@ -446,6 +502,8 @@ def main():
     ap.add_argument("--roofline-reps", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-model", action="store_true", help="skip the weight-bearing decode measurement")
+    ap.add_argument("--sweep", action="store_true",
+                    help="also sweep the Full and Local views over context lengths and batch sizes")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the decode path here is built and measured on a single "
@@ -511,6 +569,7 @@ def main():
         log("weight-bearing decode: %s" % json.dumps(whole_model))
     else:
         whole_model = None
+    sweep = view_sweep(device) if args.sweep else None
     traffic = profiled_traffic(bytes_full)
     traffic = None if traffic is None else int(round(traffic))
     copy_calibration(device)
@@ -556,6 +615,8 @@ def main():
         "step_hbm_gbs": round(float(step_gbs), 1),
         "wall_s_timed": round(wall, 3),
     }
+    if sweep is not None:
+        res["view_sweep"] = sweep
     if not args.no_cpu_baseline:
         log("timing the fp64 oracle on the host (bounded sample)")
         del stack

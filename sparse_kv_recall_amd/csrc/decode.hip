@@ -157,6 +157,71 @@ __device__ inline float wave_sum(float v) {
   return (lane_value(v, 0) + lane_value(v, 16)) + (lane_value(v, 32) + lane_value(v, 48));
 }
 
+// Integer wave reductions and an inclusive prefix sum for the plan, all in registers
+// (DPP). Scan: shift right by 1, 2, 4, 8 within each row of 16 (lanes shifted in from
+// outside the row read 0), then add the last lane of row 0 to row 1 and of row 2 to
+// row 3 (row broadcast 15), then lane 31 to rows 2 and 3 (row broadcast 31).
+template <int CTRL, int ROWS = 0xF>
+__device__ inline int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROWS, 0xF, false);
+}
+__device__ inline int wave_sum_i(int v) {
+  v += dpp_i<kDppSwap1>(v);
+  v += dpp_i<kDppSwap2>(v);
+  v += dpp_i<kDppRor4>(v);
+  v += dpp_i<kDppRor8>(v);
+  return (__builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16)) +
+         (__builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48));
+}
+__device__ inline int wave_max_i(int v) {
+  v = max(v, dpp_i<kDppSwap1>(v));
+  v = max(v, dpp_i<kDppSwap2>(v));
+  v = max(v, dpp_i<kDppRor4>(v));
+  v = max(v, dpp_i<kDppRor8>(v));
+  return max(max(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+             max(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
+}
+constexpr int kDppShr1 = 0x111, kDppShr2 = 0x112, kDppShr4 = 0x114, kDppShr8 = 0x118;
+constexpr int kDppBcast15 = 0x142, kDppBcast31 = 0x143;
+__device__ inline int wave_inclusive_scan(int v) {
+  v += dpp_i<kDppShr1>(v);
+  v += dpp_i<kDppShr2>(v);
+  v += dpp_i<kDppShr4>(v);
+  v += dpp_i<kDppShr8>(v);
+  v += dpp_i<kDppBcast15, 0xA>(v);
+  v += dpp_i<kDppBcast31, 0xC>(v);
+  return v;
+}
+
+// Max and sum over the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48) in
+// registers, with gfx950's permlane swaps: the 16-lane swap trades the first operand's
+// odd rows with the second operand's even rows, the 32-lane swap its upper half with
+// the second operand's lower half; with the same value in both operands the two results
+// hold a lane's value and its partner's. The copy goes through an empty asm statement so
+// that the compiler sees two distinct operands: given one value twice it folds the
+// swap's second result into the first, which the hardware does not do.
+template <bool HALF>
+__device__ inline void partner(float v, float& a, float& b) {
+  unsigned x = __builtin_bit_cast(unsigned, v), y = x;
+  asm volatile("" : "+v"(y));
+  const auto r = HALF ? __builtin_amdgcn_permlane32_swap(x, y, false, false)
+                      : __builtin_amdgcn_permlane16_swap(x, y, false, false);
+  a = __builtin_bit_cast(float, unsigned(r[0]));
+  b = __builtin_bit_cast(float, unsigned(r[1]));
+}
+__device__ inline float rows_max(float v) {
+  float a, b;
+  partner<false>(v, a, b);
+  partner<true>(fmaxf(a, b), a, b);
+  return fmaxf(a, b);
+}
+__device__ inline float rows_sum(float v) {
+  float a, b;
+  partner<false>(v, a, b);
+  partner<true>(a + b, a, b);
+  return a + b;
+}
+
 // s_waitcnt vmcnt(0): all of this wave's stores have completed (gfx9 counts stores in vmcnt).
 __device__ inline void wait_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
@@ -347,25 +412,32 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
       if (valid) tiles = request_tiles<MODE>(P, lane, n);
       if (blockIdx.x == 0 && wave == 0 && (!valid || tiles == 0)) bad_request(lane, n, valid);
     }
-    int sum = tiles, act = tiles > 0, mx = tiles;
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      sum += __shfl_xor(sum, off);
-      act += __shfl_xor(act, off);
-      mx = max(mx, __shfl_xor(mx, off));
-    }
+    const int sum = wave_sum_i(tiles), act = wave_sum_i(tiles > 0), mx = wave_max_i(tiles);
     T = split_size(sum, act, mx);
-    const int items = ((tiles + T - 1) / T) * Hkv;
-    int x = items;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int y = __shfl_up(x, off);
-      if (lane >= off) x += y;
+    int splits = (tiles + T - 1) / T;  // this request's splits per KV head
+    int x = wave_inclusive_scan(splits);
+    // The budget above reserves one split per active request for rounding. With a few
+    // long requests of similar length that reserve is mostly unused and can leave a
+    // large part of the grid idle (16 requests of 2K tiles: half of it); then take the
+    // smallest tiles per split, from total / slots up, whose splits fit the slots.
+    const int slots = int(gridDim.x) / Hkv;
+    if (4 * __builtin_amdgcn_readlane(x, 63) < 3 * slots) {
+      auto count = [&](int t) { return wave_sum_i((tiles + t - 1) / t); };
+      int t = (sum + slots - 1) / slots;
+      const int t_cap = (mx + kMaxSplits - 1) / kMaxSplits;
+      if (t < t_cap) t = t_cap;
+      if (t < kMinTilesPerSplit) t = kMinTilesPerSplit;
+      for (int k = 0; k < 4 && t < T && count(t) > slots; ++k) t += (t >> 3) + 1;
+      if (t < T && count(t) <= slots) {
+        T = t;
+        splits = (tiles + T - 1) / T;
+        x = wave_inclusive_scan(splits);
+      }
     }
     w_tiles = tiles;
     w_len = (lane < B) ? P.kv.seq_lens[lane] : 0;
-    w_start = x - items;
-    total_items = __shfl(x, 63);
+    w_start = (x - splits) * Hkv;
+    total_items = __builtin_amdgcn_readlane(x, 63) * Hkv;
   } else {
     __syncthreads();
     int my_sum = 0, my_active = 0, my_max = 0;
@@ -395,14 +467,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
       for (int base = 0; base < B; base += 64) {
         const int b = base + lane;
         const int items = (b < B) ? ((s_tiles[b] + T - 1) / T) * Hkv : 0;
-        int x = items;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-          const int y = __shfl_up(x, off);
-          if (lane >= off) x += y;
-        }
+        const int x = wave_inclusive_scan(items);
         if (b < B) s_start[b] = carry + x - items;
-        carry += __shfl(x, 63);
+        carry += __builtin_amdgcn_readlane(x, 63);
       }
       if (lane == 0) s_start[B] = carry;
     }
@@ -410,11 +477,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
     total_items = s_start[B];
   }
 
-  // XCD-aware order: consecutive items (the splits of one (request, KV head)) go to
-  // workgroups that the dispatcher places on the same XCD (round-robin over 8 XCDs),
-  // so the merge reads partials written through the same L2.
-  const int per_xcd = int(gridDim.x) / 8;
-  const int item_first = (per_xcd > 0) ? int(blockIdx.x % 8) * per_xcd + int(blockIdx.x / 8) : int(blockIdx.x);
+  // Items in workgroup order. The dispatcher deals workgroups round-robin over the 8
+  // XCDs, so a launch with fewer items than workgroups still spreads over all of them;
+  // partials and tickets go through device-coherent stores and loads, so the XCD that
+  // merges a (request, KV head) does not need to be the one that wrote its partials.
+  const int item_first = int(blockIdx.x);
 
   const int ncol = lane & 15, grp = lane >> 4;
   const uint8_t* kpool = reinterpret_cast<const uint8_t*>(P.kv.k_pool);
@@ -535,8 +602,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
         sv[jj] = (t >= lo && t < hi) ? s[jj] : -INFINITY;
       }
       float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = rows_max(mx);
       const float m_new = fmaxf(m_run, mx);
       const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
@@ -599,8 +665,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
     }
 
     // ---- combine the waves of this workgroup
-    l_run += __shfl_xor(l_run, 16);
-    l_run += __shfl_xor(l_run, 32);
+    l_run = rows_sum(l_run);
     if (ncol < G) {
 #pragma unroll
       for (int dc = 0; dc < 8; ++dc)
@@ -722,8 +787,7 @@ __global__ __launch_bounds__(256) void gather_kernel(sk_paged_kv kv, const uint3
   if (wave == 0) {  // kept blocks before this workgroup's range (all full words)
     int c = 0;
     for (int w = lane; w < base / 32; w += 64) c += __popc(mrow[w]);
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) c += __shfl_xor(c, off);
+    c = wave_sum_i(c);
     if (lane == 0) s_prefix = c;
   }
   const int blk = base + tid;
