@@ -86,7 +86,7 @@ def roofline_full(stack, feeder, reps):
     return e0.elapsed_time(e1) / (reps * stack.layers)
 
 
-def view_sweep(device, Hq=32, Hkv=8, reps=5, min_bytes=1 << 30):
+def view_sweep(device, Hq=32, Hkv=8, reps=10, min_bytes=1 << 30):
     """Full and Local views over context lengths at batch 1 and over batch sizes at 32K
     positions per request (identity block tables, every request of equal length, 32 q /
     8 KV heads). Each configuration rotates over enough layer pools that one graph replay
@@ -117,7 +117,8 @@ def view_sweep(device, Hq=32, Hkv=8, reps=5, min_bytes=1 << 30):
         else:
             fn = lambda: [ops.oda_decode_local(q[l], caches[l], out=out[l], ws=ws) for l in range(layers)]
         g = capture_graph(fn)
-        g.replay()
+        for _ in range(2):
+            g.replay()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
@@ -569,7 +570,6 @@ def main():
         log("weight-bearing decode: %s" % json.dumps(whole_model))
     else:
         whole_model = None
-    sweep = view_sweep(device) if args.sweep else None
     traffic = profiled_traffic(bytes_full)
     traffic = None if traffic is None else int(round(traffic))
     copy_calibration(device)
@@ -615,12 +615,12 @@ def main():
         "step_hbm_gbs": round(float(step_gbs), 1),
         "wall_s_timed": round(wall, 3),
     }
-    if sweep is not None:
-        res["view_sweep"] = sweep
+    del graph, feeder, stack
+    torch.cuda.empty_cache()
+    if args.sweep:  # after the metric stack is freed: fresh pools, as in a process of their own
+        res["view_sweep"] = view_sweep(device)
     if not args.no_cpu_baseline:
         log("timing the fp64 oracle on the host (bounded sample)")
-        del stack
-        torch.cuda.empty_cache()
         res["cpu_baseline"] = cpu_baseline(wl, recalls / args.steps)
     print(json.dumps(res), flush=True)
 
