@@ -143,6 +143,51 @@ def view_sweep(device, Hq=32, Hkv=8, reps=10, min_bytes=1 << 30):
     return res
 
 
+def stream_peak(device, gib=4, reps=5):
+    """Measured streaming-read bandwidth: sk_stream_read over a 4 GiB buffer (16-byte
+    non-temporal loads, 1 KiB contiguous per wave instruction, as the decode kernels
+    issue them), median of `reps` launches timed with HIP events. The reference for the
+    fraction of what this GPU streams in practice, beside the 8 TB/s of the data sheet."""
+    import torch
+    from sparse_kv_recall_amd import ops
+    data = torch.ones(gib << 28, dtype=torch.int32, device=device)
+    sink = ops.stream_read(data)
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        ops.stream_read(data, sink)
+        e1.record()
+        e1.synchronize()
+        times.append(e0.elapsed_time(e1))
+    ms = sorted(times)[len(times) // 2]
+    nbytes = data.numel() * 4
+    del data
+    torch.cuda.empty_cache()
+    return nbytes / (ms * 1e-3) / 1e9
+
+
+def gated_off_launch(stack, feeder, reps=20):
+    """Per-launch time of the recall pass's Full launches when the gate is 0, so that every
+    workgroup leaves at once: the per-node cost that the step graph pays 36 times on
+    every non-recall step (HIP graphs have no conditional node that could skip them)."""
+    import torch
+    from sparse_kv_recall_amd.stack import capture_graph
+    q, k, v = feeder.q, feeder.k, feeder.v
+    g = capture_graph(lambda: stack.full_pass(q[:, 1, :], k[:, 1, :], v[:, 1, :], gated=True))
+    stack.gate.zero_()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    e1.synchronize()
+    return e0.elapsed_time(e1) / (reps * stack.layers)
+
+
 def roofline_blocks(stack, feeder, reps, seed=11):
     """Block-list (Declarative-Attention) decode over the same 36 pools at the current n,
     through a seeded permutation of the block table, keeping (a) every block and (b) a
@@ -522,6 +567,8 @@ def main():
     if args.steps < 1 or args.steps > wl.steps:
         print("--steps must be in 1..%d (the workload's decode steps)" % wl.steps, file=sys.stderr)
         sys.exit(2)
+    stream_gbs = stream_peak(device)  # before the stack is staged: a fresh allocation
+    log("streaming-read reference: %.0f GB/s" % stream_gbs)
     log("staging %d layers x %d positions of bf16 KV" % (wl.layers, int(wl.H0[0])))
     t0 = time.time()
     stack = build_stack(wl, device)
@@ -557,6 +604,8 @@ def main():
     bytes_full = n_now * wl.Hkv * 128 * 2 * 2 + 2 * wl.Hq * 128 * 4 + 2 * wl.Hkv * 128 * 2
     achieved = bytes_full / (full_ms * 1e-3) / 1e9
     log("Full-view kernel at n=%d: %.1f us per launch, %.0f GB/s" % (n_now, full_ms * 1e3, achieved))
+    gated_off_ms = gated_off_launch(stack, feeder)
+    log("gated-off Full launch: %.2f us" % (gated_off_ms * 1e3))
     blocks = roofline_blocks(stack, feeder, args.roofline_reps)
     log("block-list view: %s" % json.dumps(blocks))
     full_only = always_full_rate(stack, feeder, wl, min(64, args.steps))
@@ -600,6 +649,8 @@ def main():
                    "global_batch": 1, "seq_len": int(ns[-1]), "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "stream_peak_gbs": round(stream_gbs, 1),
+                     "frac_of_stream_peak": round(achieved / stream_gbs, 4),
                      "kernel": "decode_kernel<full> (oda_decode_full), n=%d, 36-layer rotation" % n_now,
                      "us_per_launch": round(full_ms * 1e3, 2), "algorithmic_bytes_per_launch": int(bytes_full),
                      "traffic_source": "profiles/decode_128k_hbm_counters.md (rocprofv3 FETCH_SIZE x2.0 + "
@@ -609,6 +660,11 @@ def main():
                                       "once per step" % n_now),
         "always_full_baseline": dict(full_only, speedup_of_oda=round(tok_s / full_only["tok_s"], 3),
                                      attention_bytes_ratio=round(float(full_bytes / step_bytes), 3)),
+        "dispatch": {"graph_launches_per_step": 2 + 2 * wl.layers,
+                     "gated_off_full_launch_us": round(gated_off_ms * 1e3, 2),
+                     "gated_off_us_per_nonrecall_step": round(gated_off_ms * 1e3 * wl.layers, 1),
+                     "note": "one feed, 36 Local, the gate and 36 gated Full launches per step; on a "
+                             "non-recall step the Full launches exit at once but each still costs a graph node"},
         "hybrid_local_only": hybrid,
         "da_declared_step": da_tags,
         "whole_model_decode": whole_model,

@@ -341,6 +341,19 @@ int da_decode_gathered(const float* q, sk_paged_kv kv, const void* k_new, const 
                        int32_t sel_value, float* out, void* ws, size_t ws_bytes,
                        hipStream_t stream);
 
+/* ---- measurement helper (not part of the method) ---- */
+
+/* Bandwidth reference for the decode rooflines: one launch of SK_STREAM_READ_GRID
+ * workgroups (one per CU) reads `bytes` of device memory at `data` once, each
+ * workgroup its own contiguous range (16-byte non-temporal loads, 1 KiB contiguous per
+ * wave instruction, four loads per lane in flight), and writes one XOR checksum per
+ * workgroup to sink[0 .. SK_STREAM_READ_GRID-1] (device uint32, caller-owned; the XOR
+ * of all of them equals the XOR of all 32-bit words read). bytes must be a multiple of
+ * 16 and data 16-byte aligned (SK_E_RANGE); NULL sink, or NULL data with bytes > 0,
+ * gives SK_E_NULL. Asynchronous on `stream`. */
+#define SK_STREAM_READ_GRID 256
+int sk_stream_read(const void* data, uint64_t bytes, uint32_t* sink, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

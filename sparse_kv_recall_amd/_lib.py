@@ -15,6 +15,7 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "sparsekv.h")
 
 c_void_p, c_int32, c_int64, c_float, c_size_t = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
                                                  ctypes.c_float, ctypes.c_size_t)
+c_uint64 = ctypes.c_uint64
 
 
 class PagedKVStruct(ctypes.Structure):
@@ -56,6 +57,7 @@ _SIGNATURES = {
     "sk_rmsnorm": (c_int32, [c_void_p, c_void_p, c_int32, c_float, c_void_p, c_void_p, c_int32, c_void_p]),
     "sk_embed": (c_int32, [c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_void_p]),
     "sk_select": (c_int32, [c_void_p, c_int32, c_void_p, c_void_p, c_int32, c_void_p, c_void_p]),
+    "sk_stream_read": (c_int32, [c_void_p, c_uint64, c_void_p, c_void_p]),
     "da_gather": (c_int32, [PagedKVStruct, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_void_p,
                             c_void_p]),
     "da_decode_gathered": (c_int32, [c_void_p, PagedKVStruct, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,

@@ -353,6 +353,22 @@ def embed(table, token, out, out2=None, sel=None, sel_value=1):
     return out
 
 
+STREAM_READ_GRID = 256  # workgroups (and checksum words) of sk_stream_read
+
+
+def stream_read(data, sink=None):
+    """Bandwidth reference: reads every byte of the contiguous device tensor `data` once;
+    returns the int32 [STREAM_READ_GRID] per-workgroup XOR checksums (sk_stream_read)."""
+    if not data.is_contiguous():
+        raise ValueError("data must be contiguous")
+    if sink is None:
+        sink = torch.empty(STREAM_READ_GRID, dtype=torch.int32, device=data.device)
+    _check(sink, torch.int32, "sink", STREAM_READ_GRID)
+    nbytes = data.numel() * data.element_size()
+    _lib.call("sk_stream_read", data.data_ptr(), nbytes, sink.data_ptr(), _stream(data.device))
+    return sink
+
+
 def select(gate, a, b, out, gate_value=1):
     _check(gate, torch.int32, "gate", 1)
     for t, n in ((a, "a"), (b, "b"), (out, "out")):

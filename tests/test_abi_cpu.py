@@ -92,6 +92,10 @@ def test_other_entry_points_validation():
     assert L.sk_rmsnorm(FAKE, FAKE, 0, 1e-6, FAKE, None, 0, None) == SK_E_RANGE
     assert L.sk_embed(FAKE, 0, 8, FAKE, FAKE, None, None, 0, None) == SK_E_RANGE
     assert L.sk_select(None, 1, FAKE, FAKE, 8, FAKE, None) == SK_E_NULL
+    assert L.sk_stream_read(FAKE, 64, None, None) == SK_E_NULL
+    assert L.sk_stream_read(None, 64, FAKE, None) == SK_E_NULL
+    assert L.sk_stream_read(FAKE, 24, FAKE, None) == SK_E_RANGE        # not a multiple of 16
+    assert L.sk_stream_read(FAKE + 8, 64, FAKE, None) == SK_E_RANGE    # data not 16-byte aligned
     assert L.sk_kv_write(kv(), 1, 0, 1, FAKE, FAKE, None, None) == SK_E_RANGE       # request >= batch
     assert L.sk_kv_write(kv(), 0, 1599, 2, FAKE, FAKE, None, None) == SK_E_RANGE    # past max_blocks*16
     assert L.sk_kv_write(kv(), 0, 0, 1, None, FAKE, None, None) == SK_E_NULL
