@@ -382,6 +382,177 @@ def always_full_rate(stack, feeder, wl, steps):
     return {"steps": steps, "tok_s": round(steps * wl.batch / (ms / 1e3), 2), "ms_per_step": round(ms / steps, 4)}
 
 
+def _stage_history(cache, wl, unit, H0, request, device):
+    """Seeded bf16 history of one request (positions 0 .. H0-1), written into its pages."""
+    import torch
+    from sparse_kv_recall_amd import ops
+    from synth import device as sdev
+    from synth.workloads import C_KHIST, C_VHIST
+    stage_k = torch.empty((H0, wl.Hkv, 128), dtype=torch.bfloat16, device=device)
+    stage_v = torch.empty_like(stage_k)
+    sdev.fill_normal_(stage_k, wl.key(C_KHIST, unit), 0)
+    sdev.fill_normal_(stage_v, wl.key(C_VHIST, unit), 0)
+    ops.kv_write(cache, request, 0, stage_k, stage_v)
+
+
+def _time_replays(graph, steps, reset, reps):
+    """Best of `reps` passes of `steps` graph replays (reset() before each), in ms."""
+    import torch
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    best = None
+    for _ in range(reps):
+        reset()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(steps):
+            graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        best = ms if best is None else min(best, ms)
+    return best
+
+
+def other_workloads(device, reps=2):
+    """Throughput of the other seeded workloads, each step one HIP graph replay, all
+    steps from step 0 (best of `reps` passes; inputs resident before timing):
+    * oda_stack16k: 28 layers, 16 q / 8 KV heads, 16K history, the fp32 recall head
+      deciding on the device -- tokens/s, the recall steps it chose, and the Full view
+      over all 28 layers at the final n (1.9 GB per rotation, more than the MALL holds);
+    * da_32k: declared mode -> keep mask -> gathered list -> attention over the kept
+      blocks, 32K context, permuted pool -- microseconds per step for each mode (events
+      around every replay of one pass);
+    * ragged32: 32 requests of 4K-128K, each step Full or the request's fallback (Local
+      or its keep-list) -- tokens/s and GB/s of the attended positions (4096 B each)."""
+    import numpy as np
+    import torch
+    from sparse_kv_recall_amd import ops
+    from sparse_kv_recall_amd.stack import DAStep, ODAStack, RaggedBatch, capture_graph
+    from synth import device as sdev
+    from synth import workloads
+
+    res = {}
+    # ---- 16K stack with the recall head
+    wl = workloads.oda_stack16k()
+    H0 = int(wl.H0[0])
+    seq = torch.zeros(1, dtype=torch.int32, device=device)
+    stack = ODAStack(wl.layers, 1, wl.Hq, wl.Hkv, wl.num_phys_blocks, wl.max_blocks,
+                     torch.as_tensor(wl.block_tables, device=device), seq, sinks=wl.sinks, window=wl.window,
+                     device=device)
+    for l in range(wl.layers):
+        _stage_history(stack.caches[l], wl, l, H0, 0, device)
+    feeder = sdev.Feeder(wl, seq, device=device, with_x=True)
+    W = tuple(torch.as_tensor(a, device=device) for a in wl.recall_weights())
+
+    def step16k():
+        feeder.step()
+        stack.local_pass(feeder.q[:, 0], feeder.k[:, 0], feeder.v[:, 0])
+        stack.gate_from_recall_head(feeder.x, *W, theta=wl.theta)
+        stack.full_pass(feeder.q[:, 1], feeder.k[:, 1], feeder.v[:, 1], gated=True)
+
+    graph = capture_graph(step16k)
+    feeder.set_step(0)
+    recalls = 0
+    for _ in range(wl.steps):  # untimed pass: the head's decisions
+        graph.replay()
+        recalls += int(stack.gate[0].item())
+    ms = _time_replays(graph, wl.steps, lambda: feeder.set_step(0), reps)
+    n_end = int(seq[0].item())
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    stack.full_pass(feeder.q[:, 1], feeder.k[:, 1], feeder.v[:, 1], gated=False)
+    e0.record()
+    for _ in range(3):
+        stack.full_pass(feeder.q[:, 1], feeder.k[:, 1], feeder.v[:, 1], gated=False)
+    e1.record()
+    e1.synchronize()
+    full_us = e0.elapsed_time(e1) * 1e3 / (3 * wl.layers)
+    full_bytes = n_end * wl.Hkv * 512 + 2 * wl.Hq * 512 + wl.Hkv * 512
+    res["oda_stack16k"] = {"steps": wl.steps, "recall_steps": recalls, "tok_s": round(wl.steps / (ms / 1e3), 1),
+                           "ms_per_step": round(ms / wl.steps, 4), "full_view_us": round(full_us, 2),
+                           "full_view_frac_of_peak": round(full_bytes / (full_us * 1e-6) / (HBM_PEAK_GBS * 1e9), 3),
+                           "full_view_n": n_end}
+    del graph, stack, feeder
+    torch.cuda.empty_cache()
+
+    # ---- 32K DA workload, per declared mode
+    wl = workloads.da_32k()
+    H0 = int(wl.H0[0])
+    seq = torch.zeros(1, dtype=torch.int32, device=device)
+    cache = ops.PagedKVCache(wl.num_phys_blocks, 1, wl.Hq, wl.Hkv, wl.max_blocks,
+                             block_tables=torch.as_tensor(wl.block_tables, device=device), seq_lens=seq,
+                             device=device)
+    _stage_history(cache, wl, 0, H0, 0, device)
+    da = DAStep(cache, wl.da_local_tokens, device=device)
+    feeder = sdev.Feeder(wl, seq, device=device, with_decl=True)
+
+    def step_da():
+        feeder.step()
+        da.step(feeder.q[0, 0], feeder.k[0, 0], feeder.v[0, 0], feeder.decl)
+
+    graph = capture_graph(step_da)
+    ms = _time_replays(graph, wl.steps, lambda: feeder.set_step(0), reps)
+    feeder.set_step(0)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(wl.steps)]
+    for a, b in ev:
+        a.record()
+        graph.replay()
+        b.record()
+    torch.cuda.synchronize()
+    per = np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
+    modes = wl.decl[:, 0, 0]
+    res["da_32k"] = {"steps": wl.steps, "us_per_step": round(ms * 1e3 / wl.steps, 2),
+                     "us_per_step_by_mode": {name: round(float(np.median(per[modes == m])), 2)
+                                             for m, name in ((0, "global"), (1, "focus"), (2, "local"))}}
+    del graph, cache, da, feeder
+    torch.cuda.empty_cache()
+
+    # ---- ragged batch of 32
+    wl = workloads.ragged32()
+    seq = torch.zeros(wl.batch, dtype=torch.int32, device=device)
+    cache = ops.PagedKVCache(wl.num_phys_blocks, wl.batch, wl.Hq, wl.Hkv, wl.max_blocks,
+                             block_tables=torch.as_tensor(wl.block_tables, device=device), seq_lens=seq,
+                             device=device)
+    for r in range(wl.batch):
+        _stage_history(cache, wl, r, int(wl.H0[r]), r, device)
+    rb = RaggedBatch(cache, torch.as_tensor(wl.fallback, device=device),
+                     torch.as_tensor(wl.keep_mask.view(np.int32), device=device), sinks=wl.sinks,
+                     window=wl.window, device=device)
+    feeder = sdev.Feeder(wl, seq, device=device, with_scores=True)
+
+    def step_ragged():
+        feeder.step()
+        rb.step(feeder.q[0, 0], feeder.k[0, 0], feeder.v[0, 0], feeder.scores, wl.theta)
+
+    graph = capture_graph(step_ragged)
+    ms = _time_replays(graph, wl.steps, lambda: feeder.set_step(0), reps)
+    # attended positions per step and request: n (Full), min(n, sinks + window) (Local), or
+    # the positions of the kept blocks below n (keep-list)
+    scores = wl.scores_all()
+    bits = np.unpackbits(wl.keep_mask.view(np.uint8), axis=1, bitorder="little")
+    positions, recalls = 0, 0
+    for t in range(wl.steps):
+        for r in range(wl.batch):
+            n = int(wl.H0[r]) + t + 1
+            if scores[t, r] > wl.theta:
+                positions += n
+                recalls += 1
+            elif wl.fallback[r] == ops.MODE_LOCAL:
+                positions += min(n, wl.sinks + wl.window)
+            else:
+                nb = (n + 15) // 16
+                kept = np.nonzero(bits[r, :nb])[0]
+                positions += int(np.minimum(16, n - 16 * kept).sum())
+    nbytes = positions * wl.Hkv * 512
+    res["ragged32"] = {"steps": wl.steps, "batch": wl.batch, "full_request_steps": recalls,
+                       "tok_s": round(wl.steps * wl.batch / (ms / 1e3), 1), "ms_per_step": round(ms / wl.steps, 4),
+                       "attention_GBs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                       "frac_of_peak": round(nbytes / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9), 3)}
+    del graph, cache, rb, feeder
+    torch.cuda.empty_cache()
+    return res
+
+
 def da_tags_rate(device, reps=2):
     """Declaration-driven DA decode at 32K (the ``da_tags_32k`` workload): per step the
     input token advances the device parser (declaration + keep mask), then the kept
@@ -548,6 +719,8 @@ def main():
     ap.add_argument("--roofline-reps", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-model", action="store_true", help="skip the weight-bearing decode measurement")
+    ap.add_argument("--no-other", action="store_true",
+                    help="skip the throughput of the 16K stack, the 32K DA workload and the ragged batch")
     ap.add_argument("--sweep", action="store_true",
                     help="also sweep the Full and Local views over context lengths and batch sizes")
     args = ap.parse_args()
@@ -673,6 +846,9 @@ def main():
     }
     del graph, feeder, stack
     torch.cuda.empty_cache()
+    if not args.no_other:
+        res["other_workloads"] = other_workloads(device)
+        log("other workloads: %s" % json.dumps(res["other_workloads"]))
     if args.sweep:  # after the metric stack is freed: fresh pools, as in a process of their own
         res["view_sweep"] = view_sweep(device)
     if not args.no_cpu_baseline:
