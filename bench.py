@@ -421,7 +421,8 @@ def other_workloads(device, reps=2):
       over all 28 layers at the final n (1.9 GB per rotation, more than the MALL holds);
     * da_32k: declared mode -> keep mask -> gathered list -> attention over the kept
       blocks, 32K context, permuted pool -- microseconds per step for each mode (events
-      around every replay of one pass);
+      around every replay of one pass), and the same with the block-table rewrite done
+      inside the decode kernel (da_decode_declared);
     * ragged32: 32 requests of 4K-128K, each step Full or the request's fallback (Local
       or its keep-list) -- tokens/s and GB/s of the attended positions (4096 B each)."""
     import numpy as np
@@ -482,29 +483,32 @@ def other_workloads(device, reps=2):
                              block_tables=torch.as_tensor(wl.block_tables, device=device), seq_lens=seq,
                              device=device)
     _stage_history(cache, wl, 0, H0, 0, device)
-    da = DAStep(cache, wl.da_local_tokens, device=device)
     feeder = sdev.Feeder(wl, seq, device=device, with_decl=True)
-
-    def step_da():
-        feeder.step()
-        da.step(feeder.q[0, 0], feeder.k[0, 0], feeder.v[0, 0], feeder.decl)
-
-    graph = capture_graph(step_da)
-    ms = _time_replays(graph, wl.steps, lambda: feeder.set_step(0), reps)
-    feeder.set_step(0)
-    torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(wl.steps)]
-    for a, b in ev:
-        a.record()
-        graph.replay()
-        b.record()
-    torch.cuda.synchronize()
-    per = np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
     modes = wl.decl[:, 0, 0]
-    res["da_32k"] = {"steps": wl.steps, "us_per_step": round(ms * 1e3 / wl.steps, 2),
-                     "us_per_step_by_mode": {name: round(float(np.median(per[modes == m])), 2)
-                                             for m, name in ((0, "global"), (1, "focus"), (2, "local"))}}
-    del graph, cache, da, feeder
+    res["da_32k"] = {"steps": wl.steps}
+    for suffix, in_kernel in (("", False), ("_rewrite_in_kernel", True)):
+        da = DAStep(cache, wl.da_local_tokens, device=device, in_kernel_rewrite=in_kernel)
+
+        def step_da():
+            feeder.step()
+            da.step(feeder.q[0, 0], feeder.k[0, 0], feeder.v[0, 0], feeder.decl)
+
+        graph = capture_graph(step_da)
+        ms = _time_replays(graph, wl.steps, lambda: feeder.set_step(0), reps)
+        feeder.set_step(0)
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(wl.steps)]
+        for a, b in ev:
+            a.record()
+            graph.replay()
+            b.record()
+        torch.cuda.synchronize()
+        per = np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
+        res["da_32k"]["us_per_step" + suffix] = round(ms * 1e3 / wl.steps, 2)
+        res["da_32k"]["us_per_step_by_mode" + suffix] = {
+            name: round(float(np.median(per[modes == m])), 2) for m, name in ((0, "global"), (1, "focus"), (2, "local"))}
+        del graph, da
+    del cache, feeder
     torch.cuda.empty_cache()
 
     # ---- ragged batch of 32
@@ -556,7 +560,9 @@ def other_workloads(device, reps=2):
 def da_tags_rate(device, reps=2):
     """Declaration-driven DA decode at 32K (the ``da_tags_32k`` workload): per step the
     input token advances the device parser (declaration + keep mask), then the kept
-    blocks are gathered and attended. Returns the average step time over the 512 steps."""
+    blocks are gathered and attended; and the same with the parser writing only the
+    declaration and the decode kernel deriving the kept blocks from it. Returns the
+    average step time over the 512 steps of each."""
     import torch
     from sparse_kv_recall_amd import ops
     from sparse_kv_recall_amd.stack import DATagStep, capture_graph
@@ -574,34 +580,29 @@ def da_tags_rate(device, reps=2):
     sdev.fill_normal_(stage_k, wl.key(C_KHIST, 0), 0)
     sdev.fill_normal_(stage_v, wl.key(C_VHIST, 0), 0)
     ops.kv_write(cache, 0, 0, stage_k, stage_v)
-    da = DATagStep(cache, wl.da_tags, torch.as_tensor(wl.output_begin, device=device),
-                   segments=torch.as_tensor(wl.segments, device=device), local_tokens=wl.da_local_tokens)
     feeder = sdev.Feeder(wl, seq, device=device, with_tokens=True)
+    res = {"workload": "da_tags_32k: 1 layer, 32 q / 8 kv heads, context 32768 + 512 steps, declarations "
+                       "parsed on the device from a seeded token stream", "steps": wl.steps}
+    for key, in_kernel in (("us_per_step", False), ("us_per_step_rewrite_in_kernel", True)):
+        da = DATagStep(cache, wl.da_tags, torch.as_tensor(wl.output_begin, device=device),
+                       segments=torch.as_tensor(wl.segments, device=device), local_tokens=wl.da_local_tokens,
+                       in_kernel_rewrite=in_kernel)
 
-    def step():
-        feeder.step()
-        da.step(feeder.q[0, 0], feeder.k[0, 0], feeder.v[0, 0], feeder.tokens)
+        def step():
+            feeder.step()
+            da.step(feeder.q[0, 0], feeder.k[0, 0], feeder.v[0, 0], feeder.tokens)
 
-    graph = capture_graph(step)
-    graph.replay()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    best = None
-    for _ in range(reps):
-        feeder.set_step(0)
-        da.state.zero_()
+        graph = capture_graph(step)
+        graph.replay()
         torch.cuda.synchronize()
-        e0.record()
-        for _ in range(wl.steps):
-            graph.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1)
-        best = ms if best is None else min(best, ms)
-    del graph
-    return {"workload": "da_tags_32k: 1 layer, 32 q / 8 kv heads, context 32768 + 512 steps, declarations "
-                        "parsed on the device from a seeded token stream", "steps": wl.steps,
-            "us_per_step": round(best * 1e3 / wl.steps, 2)}
+
+        def reset():
+            feeder.set_step(0)
+            da.state.zero_()
+
+        res[key] = round(_time_replays(graph, wl.steps, reset, reps) * 1e3 / wl.steps, 2)
+        del graph
+    return res
 
 
 def decoder_rates(device, contexts=(4096, 131072), steps=64, recalls=8):

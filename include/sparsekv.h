@@ -243,9 +243,10 @@ typedef struct sk_da_tags {
  * Then decl[b] = {mode, focus_begin_block, focus_end_block, output_begin[b]}
  * (the row da_keep_mask reads; output_begin: int32 [batch], the first logical
  * block of the model's own output) and keep_mask row b is written exactly as
- * da_keep_mask writes it. One workgroup per request; segments may be NULL
- * when num_segments == 0. Host-checked: pointers, num_segments >= 0,
- * local_tokens >= 0, the paged-KV description. */
+ * da_keep_mask writes it; keep_mask may be NULL when only the declaration is
+ * wanted (da_decode_declared reads it directly). One workgroup per request;
+ * segments may be NULL when num_segments == 0. Host-checked: pointers,
+ * num_segments >= 0, local_tokens >= 0, the paged-KV description. */
 int da_declare(const int32_t* tokens, int32_t* state, const int32_t* segments,
                int32_t num_segments, const int32_t* output_begin, sk_da_tags tags,
                sk_paged_kv kv, int32_t local_tokens, int32_t* decl,
@@ -338,6 +339,21 @@ int da_gather(sk_paged_kv kv, const uint32_t* keep_mask, int32_t* gathered,
 int da_decode_gathered(const float* q, sk_paged_kv kv, const void* k_new, const void* v_new,
                        const int32_t* gathered, const int32_t* gathered_cnt,
                        const int32_t* num_kept, float scale, const int32_t* sel,
+                       int32_t sel_value, float* out, void* ws, size_t ws_bytes,
+                       hipStream_t stream);
+
+/* Attention over the blocks a declared mode keeps ([DA] sections 1 and 3), with the
+ * block-table rewrite done inside the decode kernel instead of through a keep mask and
+ * a gathered list: decl and local_tokens as in da_keep_mask; the request attends exactly
+ * the positions of the kept blocks, in ascending logical order, and commits k_new /
+ * v_new (when given) as da_decode_blocks does. Outputs, commits and device error bits
+ * are those of da_keep_mask followed by da_decode_blocks (the same tiles in the same
+ * order, so bit for bit), in one launch and without the mask and list buffers. A mode
+ * other than SK_DA_GLOBAL / SK_DA_FOCUS / SK_DA_LOCAL keeps nothing (SK_DEVERR_EMPTY,
+ * zero row). NULL decl gives SK_E_NULL, local_tokens < 0 SK_E_RANGE; other arguments as
+ * oda_decode_local. */
+int da_decode_declared(const float* q, sk_paged_kv kv, const void* k_new, const void* v_new,
+                       const int32_t* decl, int32_t local_tokens, float scale, const int32_t* sel,
                        int32_t sel_value, float* out, void* ws, size_t ws_bytes,
                        hipStream_t stream);
 

@@ -58,6 +58,8 @@ _SIGNATURES = {
     "sk_embed": (c_int32, [c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_void_p]),
     "sk_select": (c_int32, [c_void_p, c_int32, c_void_p, c_void_p, c_int32, c_void_p, c_void_p]),
     "sk_stream_read": (c_int32, [c_void_p, c_uint64, c_void_p, c_void_p]),
+    "da_decode_declared": (c_int32, [c_void_p, PagedKVStruct, c_void_p, c_void_p, c_void_p, c_int32, c_float,
+                                     c_void_p, c_int32, c_void_p, c_void_p, c_size_t, c_void_p]),
     "da_gather": (c_int32, [PagedKVStruct, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_void_p,
                             c_void_p]),
     "da_decode_gathered": (c_int32, [c_void_p, PagedKVStruct, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,

@@ -5,8 +5,9 @@
 //   o_h = sum_{j in S} softmax_j(scale * <q_h, k_{g,j}>) v_{g,j}
 // with S the Full view [0, n), the Local view [0, min(s,n)) u [max(.., n-w), n)
 // (On-Demand Attention summary page, "Approach"; "Main results" for the window that
-// counts the current token) or the kept blocks of a Declarative-Attention keep-list
-// (DA review page, section 3: block-granular mask by block-table rewrite).
+// counts the current token), the kept blocks of a Declarative-Attention keep-list
+// (DA review page, section 3: block-granular mask by block-table rewrite), or the kept
+// blocks of a declared DA mode, derived in the kernel from the declaration.
 //
 // How (gfx950):
 //  * Work item = (request, KV head, split of consecutive tiles); a tile is one
@@ -21,7 +22,7 @@
 //    split into bf16 hi + lo parts, so the products keep ~16 mantissa bits; the
 //    accumulation is fp32. All query heads of a KV head share one read of K and V.
 //  * Online softmax in base 2 (q pre-scaled by scale*log2 e), max reduced across the
-//    four lane groups with shuffles; waves combine through LDS; splits are merged by
+//    four 16-lane rows with permlane swaps; waves combine through LDS; splits are merged by
 //    the last workgroup to finish (atomic ticket per (request, KV head)) in registers,
 //    in a fixed split order, so results are deterministic.
 #include <math.h>
@@ -33,7 +34,7 @@
 namespace sk {
 namespace {
 
-enum { kFull = 0, kLocal = 1, kList = 2 };
+enum { kFull = 0, kLocal = 1, kList = 2, kDecl = 3 };
 constexpr int kThreads = 64 * kWavesPerWG;
 constexpr int kMinTilesPerSplit = 8;                   // small launches: many short splits
 constexpr int kMaxSplits = 256;                     // splits per (request, KV head)
@@ -58,6 +59,8 @@ struct DecodeParams {
   int sinks;
   int window;
   float qscale;
+  const int32_t* decl;  // declared view: {mode, focus_begin, focus_end, output_begin} per request
+  int local_tokens;
 };
 
 struct Tile {
@@ -69,6 +72,54 @@ __device__ inline bool request_active(const DecodeParams& P, int b) {
   return !HAS_SEL || P.sel[b] == P.sel_value;
 }
 
+// Kept blocks of a declared mode ([DA] sections 1 and 3) as at most two ascending,
+// disjoint runs of logical blocks, [s0, s0 + l0) then [s1, s1 + l1), the same set (in the
+// same order) as the keep mask of the declaration compacted into a list: global keeps every
+// block below ceil(n/16); focus keeps [focus_begin, focus_end) and every block from
+// output_begin on, both cut there; local keeps the blocks overlapping the last local_tokens
+// positions; any other mode keeps nothing. n must be valid (1 .. max_blocks*16).
+struct Runs {
+  int s0, l0, s1, l1;
+};
+__device__ inline Runs declared_runs(const DecodeParams& P, int b, int n) {
+  const int nb = (n + kBlock - 1) / kBlock;
+  const int32_t* d = P.decl + 4 * int64_t(b);
+  const int mode = d[0];
+  int s0 = 0, e0 = 0, s1 = 0, e1 = 0;
+  if (mode == SK_DA_GLOBAL) {
+    e0 = nb;
+  } else if (mode == SK_DA_LOCAL) {
+    s0 = (n > P.local_tokens ? n - P.local_tokens : 0) / kBlock;
+    e0 = nb;
+  } else if (mode == SK_DA_FOCUS) {
+    s0 = min(max(d[1], 0), nb);
+    e0 = min(max(d[2], s0), nb);
+    s1 = min(max(d[3], 0), nb);
+    e1 = nb;
+  }
+  if (e0 <= s0) {  // first run empty: the second (possibly empty) one alone
+    s0 = s1;
+    e0 = e1;
+    s1 = e1 = 0;
+  }
+  if (e1 <= s1) {
+    s1 = e1 = 0;
+  } else {
+    if (s1 < s0) {  // ascending order
+      const int ts = s0, te = e0;
+      s0 = s1;
+      e0 = e1;
+      s1 = ts;
+      e1 = te;
+    }
+    if (s1 <= e0) {  // overlapping or adjacent: one run
+      e0 = max(e0, e1);
+      s1 = e1 = 0;
+    }
+  }
+  return Runs{s0, e0 - s0, s1, e1 - s1};
+}
+
 template <int MODE>
 __device__ inline int request_tiles(const DecodeParams& P, int b, int n) {
   if (MODE == kFull) return (n + kBlock - 1) / kBlock;
@@ -78,6 +129,10 @@ __device__ inline int request_tiles(const DecodeParams& P, int b, int n) {
     int st = (s_end + kBlock - 1) / kBlock;
     int wt = (a < n) ? ((n - 1) / kBlock - a / kBlock + 1) : 0;
     return st + wt;
+  }
+  if (MODE == kDecl) {
+    const Runs r = declared_runs(P, b, n);
+    return r.l0 + r.l1;
   }
   int k = P.list_num[b];
   return min(max(k, 0), P.kv.max_blocks);
@@ -106,6 +161,12 @@ __device__ inline Tile tile_at(const DecodeParams& P, int b, int n, int i) {
       t.lo = (j == 0) ? (a % kBlock) : 0;
       t.hi = min(kBlock, n - kBlock * lb);
     }
+    t.phys = bt[lb];
+  } else if (MODE == kDecl) {
+    const Runs r = declared_runs(P, b, n);
+    const int lb = (i < r.l0) ? r.s0 + i : r.s1 + (i - r.l0);
+    t.lo = 0;
+    t.hi = min(kBlock, n - kBlock * lb);
     t.phys = bt[lb];
   } else {
     int64_t o = int64_t(b) * P.kv.max_blocks + i;
@@ -404,7 +465,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
   int w_tiles = 0, w_start = 0, w_len = 0;  // small batches: lane b holds request b's tiles,
                                              // first item and sequence length
   if (B <= 64) {
-    // every wave plans on its own with shuffles; no workgroup barrier
+    // every wave plans on its own with register reductions; no workgroup barrier
     int tiles = 0;
     if (lane < B && request_active<HAS_SEL>(P, lane)) {
       const int n = P.kv.seq_lens[lane];
@@ -524,8 +585,14 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
     int commit_tile = -1;
     const int tl = (n - 1) % kBlock;
     if (P.k_new) {
-      if (MODE != kList) {
+      if (MODE == kFull || MODE == kLocal) {
         commit_tile = tiles_b - 1;
+      } else if (MODE == kDecl) {
+        // the current token's block is attended when it is the last kept block
+        const Runs r = declared_runs(P, b, n);
+        const int last_blk = (r.l1 > 0) ? r.s1 + r.l1 - 1 : r.s0 + r.l0 - 1;
+        if (last_blk == (n - 1) / kBlock) commit_tile = tiles_b - 1;
+        else if (split == 0 && wave == 0) commit_token_lanes(P, b, g, n, lane);
       } else {
         int last_phys = P.kv.block_tables[int64_t(b) * maxb + (n - 1) / kBlock];
         if (P.list_phys[int64_t(b) * maxb + tiles_b - 1] == last_phys) commit_tile = tiles_b - 1;
@@ -809,7 +876,8 @@ __global__ __launch_bounds__(256) void gather_kernel(sk_paged_kv kv, const uint3
 template <int MODE>
 int launch_decode(const float* q, sk_paged_kv kv, const void* k_new, const void* v_new, int sinks, int window,
                   float scale, const int32_t* sel, int sel_value, const int32_t* lp, const int32_t* lc,
-                  const int32_t* ln, float* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+                  const int32_t* ln, float* out, void* ws, size_t ws_bytes, hipStream_t stream,
+                  const int32_t* decl = nullptr, int local_tokens = 0) {
   int st = check_kv(kv);
   if (st) return st;
   if (!q || !out || !ws) return SK_E_NULL;
@@ -832,6 +900,8 @@ int launch_decode(const float* q, sk_paged_kv kv, const void* k_new, const void*
   P.sinks = sinks;
   P.window = window;
   P.qscale = scale * kLog2e;
+  P.decl = decl;
+  P.local_tokens = local_tokens;
   const int G = kv.num_q_heads / kv.num_kv_heads;
   // Grid: one workgroup per CU at most, fewer for small launches (an upper bound of the
   // work items from max_blocks), rounded to a multiple of the 8 XCDs.
@@ -899,6 +969,15 @@ int da_gather(sk_paged_kv kv, const uint32_t* keep_mask, int32_t* gathered, int3
                      stream, kv, keep_mask, sel, sel_value, gathered, gathered_cnt, num_kept,
                      reinterpret_cast<int32_t*>(ws));
   return launch_status(hipGetLastError());
+}
+
+int da_decode_declared(const float* q, sk_paged_kv kv, const void* k_new, const void* v_new, const int32_t* decl,
+                       int32_t local_tokens, float scale, const int32_t* sel, int32_t sel_value, float* out,
+                       void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!decl) return SK_E_NULL;
+  if (local_tokens < 0) return SK_E_RANGE;
+  return launch_decode<kDecl>(q, kv, k_new, v_new, 0, 1, scale, sel, sel_value, nullptr, nullptr, nullptr, out, ws,
+                              ws_bytes, stream, decl, local_tokens);
 }
 
 int da_decode_gathered(const float* q, sk_paged_kv kv, const void* k_new, const void* v_new, const int32_t* gathered,

@@ -193,8 +193,9 @@ __global__ __launch_bounds__(256) void declare_kernel(const int32_t* __restrict_
   const int n = kv.seq_lens[b];
   const int first_local = (n > local_tokens ? n - local_tokens : 0) / kBlock;
   const int nb = visible_blocks(kv, n);
-  for (int w = threadIdx.x; w < words_row; w += blockDim.x)
-    mask[int64_t(b) * words_row + w] = keep_word(s_decl[0], s_decl[1], s_decl[2], s_decl[3], first_local, nb, w);
+  if (mask)
+    for (int w = threadIdx.x; w < words_row; w += blockDim.x)
+      mask[int64_t(b) * words_row + w] = keep_word(s_decl[0], s_decl[1], s_decl[2], s_decl[3], first_local, nb, w);
 }
 
 template <int CHUNKS>
@@ -258,7 +259,7 @@ int da_declare(const int32_t* tokens, int32_t* state, const int32_t* segments, i
                uint32_t* keep_mask, hipStream_t stream) {
   int st = check_kv(kv);
   if (st) return st;
-  if (!tokens || !state || !output_begin || !decl || !keep_mask) return SK_E_NULL;
+  if (!tokens || !state || !output_begin || !decl) return SK_E_NULL;
   if (num_segments < 0 || local_tokens < 0) return SK_E_RANGE;
   if (num_segments > 0 && !segments) return SK_E_NULL;
   hipLaunchKernelGGL(declare_kernel, dim3(unsigned(kv.batch)), dim3(256), 0, stream, tokens, state, segments,

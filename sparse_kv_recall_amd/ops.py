@@ -194,11 +194,13 @@ def da_keep_mask(decl, kv, local_tokens=1024, mask=None):
     return mask
 
 
-def da_declare(tokens, state, output_begin, kv, tags, segments=None, local_tokens=1024, decl=None, mask=None):
+def da_declare(tokens, state, output_begin, kv, tags, segments=None, local_tokens=1024, decl=None, mask=None,
+               with_mask=True):
     """Advance each request's declaration parser by this step's token and write the
-    step's declaration and keep mask. tokens: int32 [B]; state: int32 [B][4]
+    step's declaration and (with_mask) keep mask. tokens: int32 [B]; state: int32 [B][4]
     (persistent, start {DA_GLOBAL, 0, 0, 0}); output_begin: int32 [B]; tags:
-    (global, focus, local, segment_base) token ids; segments: int32 [B][S][2] or None."""
+    (global, focus, local, segment_base) token ids; segments: int32 [B][S][2] or None.
+    Returns (decl, mask), mask None without with_mask."""
     B = kv.batch
     words = (kv.max_blocks + 31) // 32
     _check(tokens, torch.int32, "tokens", B)
@@ -213,12 +215,14 @@ def da_declare(tokens, state, output_begin, kv, tags, segments=None, local_token
     if decl is None:
         decl = torch.empty((B, 4), dtype=torch.int32, device=tokens.device)
     _check(decl, torch.int32, "decl", B * 4)
-    if mask is None:
+    if not with_mask:
+        mask = None
+    elif mask is None:
         mask = torch.empty((B, words), dtype=torch.int32, device=tokens.device)
     _check(mask, torch.int32, "mask", B * words)
     t = _lib.DaTagsStruct(*(int(x) for x in tags))
     _lib.call("da_declare", tokens.data_ptr(), state.data_ptr(), 0 if segments is None else segments.data_ptr(),
-              nseg, output_begin.data_ptr(), t, kv.abi(), int(local_tokens), decl.data_ptr(), mask.data_ptr(),
+              nseg, output_begin.data_ptr(), t, kv.abi(), int(local_tokens), decl.data_ptr(), _ptr(mask),
               _stream(tokens.device))
     return decl, mask
 
@@ -277,6 +281,19 @@ def da_decode_gathered(q, kv, gathered, gathered_cnt, num_kept, k_new=None, v_ne
     _lib.call("da_decode_gathered", q.data_ptr(), kv.abi(), _ptr(k_new), _ptr(v_new), gathered.data_ptr(),
               gathered_cnt.data_ptr(), num_kept.data_ptr(), scale, _ptr(sel), int(sel_value), out.data_ptr(),
               ws.data_ptr(), ws.numel(), _stream(q.device))
+    return out
+
+
+def da_decode_declared(q, kv, decl, local_tokens=1024, k_new=None, v_new=None, scale=None, sel=None,
+                       sel_value=MODE_BLOCKS, out=None, ws=None):
+    """Attention over the blocks a declared mode keeps (decl int32 [B][4] as for
+    da_keep_mask), the block-table rewrite done in the kernel: one launch."""
+    out, ws = _decode_common(q, kv, k_new, v_new, sel, out, ws)
+    _check(decl, torch.int32, "decl", 4 * kv.batch)
+    scale = 1.0 / math.sqrt(HEAD_DIM) if scale is None else float(scale)
+    _lib.call("da_decode_declared", q.data_ptr(), kv.abi(), _ptr(k_new), _ptr(v_new), decl.data_ptr(),
+              int(local_tokens), scale, _ptr(sel), int(sel_value), out.data_ptr(), ws.data_ptr(), ws.numel(),
+              _stream(q.device))
     return out
 
 

@@ -104,10 +104,14 @@ class RaggedBatch:
 
 
 class DAStep:
-    """One attention layer driven by Declarative-Attention declarations."""
+    """One attention layer driven by Declarative-Attention declarations. By default the
+    declaration becomes a keep mask, the mask a gathered list (the rewritten block table)
+    and the list is attended; with in_kernel_rewrite the decode kernel derives the kept
+    blocks from the declaration itself (da_decode_declared: same result, one launch)."""
 
-    def __init__(self, cache, local_tokens=1024, scale=None, device="cuda"):
+    def __init__(self, cache, local_tokens=1024, scale=None, device="cuda", in_kernel_rewrite=False):
         self.cache = cache
+        self.in_kernel_rewrite = in_kernel_rewrite
         self.local_tokens = local_tokens
         self.scale = 1.0 / math.sqrt(ops.HEAD_DIM) if scale is None else scale
         B, mb = cache.batch, cache.max_blocks
@@ -119,6 +123,10 @@ class DAStep:
         self.num_kept = torch.zeros(B, dtype=torch.int32, device=device)
 
     def step(self, q, k, v, decl):
+        if self.in_kernel_rewrite:
+            ops.da_decode_declared(q, self.cache, decl, self.local_tokens, k, v, self.scale, out=self.out,
+                                   ws=self.ws)
+            return
         ops.da_keep_mask(decl, self.cache, self.local_tokens, mask=self.mask)
         ops.da_decode_blocks(q, self.cache, self.mask, k, v, self.scale, out=self.out, gathered=self.gathered,
                              gathered_cnt=self.gathered_cnt, num_kept=self.num_kept, ws=self.ws)
@@ -129,8 +137,9 @@ class DATagStep(DAStep):
     the input token advances the per-request parser (mode tags, named segments), which
     writes the step's declaration and keep mask, then the kept blocks are attended."""
 
-    def __init__(self, cache, tags, output_begin, segments=None, local_tokens=1024, scale=None, device="cuda"):
-        super().__init__(cache, local_tokens, scale, device)
+    def __init__(self, cache, tags, output_begin, segments=None, local_tokens=1024, scale=None, device="cuda",
+                 in_kernel_rewrite=False):
+        super().__init__(cache, local_tokens, scale, device, in_kernel_rewrite)
         B = cache.batch
         self.tags = tuple(int(x) for x in tags)
         self.output_begin = output_begin
@@ -140,7 +149,12 @@ class DATagStep(DAStep):
 
     def step(self, q, k, v, tokens):
         ops.da_declare(tokens, self.state, self.output_begin, self.cache, self.tags, segments=self.segments,
-                       local_tokens=self.local_tokens, decl=self.decl, mask=self.mask)
+                       local_tokens=self.local_tokens, decl=self.decl, mask=self.mask,
+                       with_mask=not self.in_kernel_rewrite)
+        if self.in_kernel_rewrite:
+            ops.da_decode_declared(q, self.cache, self.decl, self.local_tokens, k, v, self.scale, out=self.out,
+                                   ws=self.ws)
+            return
         ops.da_decode_blocks(q, self.cache, self.mask, k, v, self.scale, out=self.out, gathered=self.gathered,
                              gathered_cnt=self.gathered_cnt, num_kept=self.num_kept, ws=self.ws)
 

@@ -172,9 +172,10 @@ class DaRun:
     """Declarative-Attention workload: per step a declared mode -> keep mask -> gathered
     block list -> attention over the kept blocks (with the current token committed)."""
 
-    def __init__(self, wl, steps=None, use_graph=True):
+    def __init__(self, wl, steps=None, use_graph=True, in_kernel_rewrite=False):
         self.wl = wl
         self.steps = wl.steps if steps is None else steps
+        self.in_kernel_rewrite = in_kernel_rewrite
         H0 = int(wl.H0[0])
         bt = torch.as_tensor(wl.block_tables, device="cuda")
         seq = torch.zeros(1, dtype=torch.int32, device="cuda")
@@ -183,7 +184,7 @@ class DaRun:
         self.cache.k_pool.view(torch.int16).fill_(0x7FC0)  # unwritten slots are NaN
         self.cache.v_pool.view(torch.int16).fill_(0x7FC0)
         _fill_history(self.cache, wl, 0, H0)
-        self.da = DAStep(self.cache, wl.da_local_tokens)
+        self.da = DAStep(self.cache, wl.da_local_tokens, in_kernel_rewrite=in_kernel_rewrite)
         self.feeder = sdev.Feeder(wl, seq, with_decl=True)
         self.mirror = _mirror(wl, 0, H0, self.steps)
         self.graph = capture_graph(self._step) if use_graph else None
@@ -205,11 +206,12 @@ class DaRun:
             mode, f0, f1, ob = (int(x) for x in wl.decl[t, 0])
             assert ob == pb
             kept = gather.da_mode_blocks(mode, n, f0, f1, ob, local_tokens=wl.da_local_tokens)
-            phys, cnt = gather.gather_blocks(wl.block_tables[0], kept, n)
-            num = int(self.da.num_kept[0].item())
-            assert num == len(phys), t
-            assert np.array_equal(self.da.gathered[0, :num].cpu().numpy(), phys), t
-            assert np.array_equal(self.da.gathered_cnt[0, :num].cpu().numpy(), cnt), t
+            if not self.in_kernel_rewrite:  # the rewritten block table is materialised
+                phys, cnt = gather.gather_blocks(wl.block_tables[0], kept, n)
+                num = int(self.da.num_kept[0].item())
+                assert num == len(phys), t
+                assert np.array_equal(self.da.gathered[0, :num].cpu().numpy(), phys), t
+                assert np.array_equal(self.da.gathered_cnt[0, :num].cpu().numpy(), cnt), t
             q = wl.cand_q(t, 0, 0, 0)
             kN, vN = wl.cand_kv(t, 0, 0, 0)
             if check_steps is None or t in check_steps:
@@ -229,10 +231,11 @@ class DaTagsRun:
     advances the device parser (checked against the oracle parser: state and
     declaration bit for bit), then keep mask -> gathered list -> attention."""
 
-    def __init__(self, wl, steps=None, use_graph=True):
+    def __init__(self, wl, steps=None, use_graph=True, in_kernel_rewrite=False):
         from sparse_kv_recall_amd.stack import DATagStep
         self.wl = wl
         self.steps = wl.steps if steps is None else steps
+        self.in_kernel_rewrite = in_kernel_rewrite
         H0 = int(wl.H0[0])
         bt = torch.as_tensor(wl.block_tables, device="cuda")
         seq = torch.zeros(1, dtype=torch.int32, device="cuda")
@@ -242,7 +245,8 @@ class DaTagsRun:
         self.cache.v_pool.view(torch.int16).fill_(0x7FC0)
         _fill_history(self.cache, wl, 0, H0)
         self.da = DATagStep(self.cache, wl.da_tags, torch.as_tensor(wl.output_begin, device="cuda"),
-                            segments=torch.as_tensor(wl.segments, device="cuda"), local_tokens=wl.da_local_tokens)
+                            segments=torch.as_tensor(wl.segments, device="cuda"), local_tokens=wl.da_local_tokens,
+                            in_kernel_rewrite=in_kernel_rewrite)
         self.feeder = sdev.Feeder(wl, seq, with_tokens=True)
         self.mirror = _mirror(wl, 0, H0, self.steps)
         self.graph = capture_graph(self._step) if use_graph else None
@@ -266,13 +270,14 @@ class DaTagsRun:
             assert tuple(int(x) for x in self.da.decl[0].cpu()) == rows[t], t
             mode, fb, fe, ob = rows[t]
             kept = gather.da_mode_blocks(mode, n, fb, fe, ob, local_tokens=wl.da_local_tokens)
-            words = self.da.mask[0].cpu().numpy().view(np.uint32)
-            assert gather.mask_to_blocks(words, n) == kept, t
-            phys, cnt = gather.gather_blocks(wl.block_tables[0], kept, n)
-            num = int(self.da.num_kept[0].item())
-            assert num == len(phys), t
-            assert np.array_equal(self.da.gathered[0, :num].cpu().numpy(), phys), t
-            assert np.array_equal(self.da.gathered_cnt[0, :num].cpu().numpy(), cnt), t
+            if not self.in_kernel_rewrite:  # keep mask and rewritten block table are materialised
+                words = self.da.mask[0].cpu().numpy().view(np.uint32)
+                assert gather.mask_to_blocks(words, n) == kept, t
+                phys, cnt = gather.gather_blocks(wl.block_tables[0], kept, n)
+                num = int(self.da.num_kept[0].item())
+                assert num == len(phys), t
+                assert np.array_equal(self.da.gathered[0, :num].cpu().numpy(), phys), t
+                assert np.array_equal(self.da.gathered_cnt[0, :num].cpu().numpy(), cnt), t
             q = wl.cand_q(t, 0, 0, 0)
             kN, vN = wl.cand_kv(t, 0, 0, 0)
             if check_steps is None or t in check_steps:

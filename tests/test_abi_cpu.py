@@ -71,7 +71,8 @@ def test_other_entry_points_validation():
     assert L.da_declare(FAKE, FAKE, None, 2, FAKE, tags, kv(), 1024, FAKE, FAKE, None) == SK_E_NULL
     assert L.da_declare(FAKE, FAKE, FAKE, -1, FAKE, tags, kv(), 1024, FAKE, FAKE, None) == SK_E_RANGE
     assert L.da_declare(FAKE, FAKE, None, 0, FAKE, tags, kv(), -1, FAKE, FAKE, None) == SK_E_RANGE
-    assert L.da_declare(FAKE, FAKE, None, 0, FAKE, tags, kv(), 1024, FAKE, None, None) == SK_E_NULL
+    assert L.da_declare(FAKE, FAKE, None, 0, FAKE, tags, kv(), 1024, None, None, None) == SK_E_NULL  # decl
+    # (keep_mask may be NULL: only the declaration is written)
     assert L.da_decode_blocks(FAKE, kv(), None, None, None, FAKE, FAKE, FAKE, 0.1, None, 2, FAKE, FAKE,
                               1 << 30, None) == SK_E_NULL
     assert L.da_gather(kv(), None, FAKE, FAKE, FAKE, None, 2, None, None) == SK_E_NULL
@@ -92,6 +93,10 @@ def test_other_entry_points_validation():
     assert L.sk_rmsnorm(FAKE, FAKE, 0, 1e-6, FAKE, None, 0, None) == SK_E_RANGE
     assert L.sk_embed(FAKE, 0, 8, FAKE, FAKE, None, None, 0, None) == SK_E_RANGE
     assert L.sk_select(None, 1, FAKE, FAKE, 8, FAKE, None) == SK_E_NULL
+    assert L.da_decode_declared(FAKE, kv(), None, None, None, 1024, 0.1, None, 0, FAKE, FAKE, 1 << 20,
+                                None) == SK_E_NULL
+    assert L.da_decode_declared(FAKE, kv(), None, None, FAKE, -1, 0.1, None, 0, FAKE, FAKE, 1 << 20,
+                                None) == SK_E_RANGE
     assert L.sk_stream_read(FAKE, 64, None, None) == SK_E_NULL
     assert L.sk_stream_read(None, 64, FAKE, None) == SK_E_NULL
     assert L.sk_stream_read(FAKE, 24, FAKE, None) == SK_E_RANGE        # not a multiple of 16

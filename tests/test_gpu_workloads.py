@@ -46,12 +46,14 @@ def test_oda_stack128k_metric_workload():
           "max-abs %.2e, row-rel %.2e" % (sorted(sample), rep.max_abs, rep.max_row_rel))
 
 
-def test_da_32k_every_step():
+@pytest.mark.parametrize("in_kernel_rewrite", [False, True])
+def test_da_32k_every_step(in_kernel_rewrite):
     from tests.harness import DaRun
     wl = workloads.da_32k()
-    rep = DaRun(wl).run()
+    rep = DaRun(wl, in_kernel_rewrite=in_kernel_rewrite).run()
     assert rep.checked_outputs == 512
-    print("da_32k: max-abs %.2e, row-rel %.2e" % (rep.max_abs, rep.max_row_rel))
+    print("da_32k (rewrite in kernel: %s): max-abs %.2e, row-rel %.2e" % (in_kernel_rewrite, rep.max_abs,
+                                                                         rep.max_row_rel))
 
 
 @pytest.mark.slow
@@ -87,10 +89,11 @@ def test_all_layers_local_only_equals_local():
     print("all local-only: recalls %d/24, max-abs %.2e" % (rep.recalls, rep.max_abs))
 
 
-def test_da_tag_stream_every_step():
+@pytest.mark.parametrize("in_kernel_rewrite", [False, True])
+def test_da_tag_stream_every_step(in_kernel_rewrite):
     # declarations parsed on the device from a token stream (mode tags, named segments)
     from tests.harness import DaTagsRun
     wl = workloads.da_tags_32k()
-    rep = DaTagsRun(wl).run()
+    rep = DaTagsRun(wl, in_kernel_rewrite=in_kernel_rewrite).run()
     assert rep.checked_outputs == 512 and rep.recalls > 0
     print("da_tags_32k: focus steps %d/512, max-abs %.2e, row-rel %.2e" % (rep.recalls, rep.max_abs, rep.max_row_rel))
