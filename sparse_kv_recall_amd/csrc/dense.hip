@@ -198,22 +198,25 @@ __global__ __launch_bounds__(kHeadDim) void qk_finish_kernel(const float* __rest
   const int head = blockIdx.x, t = threadIdx.x;
   const bool is_q = head < Hq, is_v = head >= Hq + Hkv;
   float v = raw[head * kHeadDim + t];
+  // rotary angle of pair t % 64 at position n - 1, in fp64 and reduced to [-pi, pi]
+  // before the sine and cosine (|angle| < 2^31 rad, so the reduction error stays far
+  // below fp32 resolution); computed while the projection row is still loading
+  float c = 1.f, s = 0.f;
+  if (!is_v) {
+    const int i = t & 63;
+    const double ang = double(seq_lens[0] - 1) * exp2(-double(i) / 64.0 * log2(double(rope_base)));
+    const double red = ang - 6.283185307179586 * rint(ang * 0.15915494309189535);
+    double sd, cd;
+    sincos(red, &sd, &cd);
+    c = float(cd);
+    s = float(sd);
+  }
   const float ss = block_sum(v * v, red);
   if (!is_v) v = v * (1.f / sqrtf(ss / float(kHeadDim) + eps)) * bf16f((is_q ? g_q : g_k)[t]);
   s_val[t] = v;
   __syncthreads();
   float o = v;
-  if (!is_v) {
-    const int i = t & 63;
-    // angle in fp64, reduced to [-pi, pi] before the sine and cosine (|angle| < 2^31
-    // rad, so the reduction error stays far below fp32 resolution)
-    const double ang = double(seq_lens[0] - 1) * exp2(-double(i) / 64.0 * log2(double(rope_base)));
-    const double red = ang - 6.283185307179586 * rint(ang * 0.15915494309189535);
-    double sd, cd;
-    sincos(red, &sd, &cd);
-    const float c = float(cd), s = float(sd);
-    o = (t < 64) ? v * c - s_val[t + 64] * s : v * c + s_val[t - 64] * s;
-  }
+  if (!is_v) o = (t < 64) ? v * c - s_val[t + 64] * s : v * c + s_val[t - 64] * s;
   if (is_q) {
     q_out[head * kHeadDim + t] = o;
   } else {
@@ -254,7 +257,7 @@ __global__ void select_kernel(const int32_t* __restrict__ gate, int gate_value, 
 template <int J>
 int launch_gemv_j(const uint16_t* W, int rows, int cols, const float* x, int pro, int epi, const uint16_t* gamma,
                   float eps, const float* residual, float* y, const int32_t* sel, int sel_value, hipStream_t stream) {
-  const int waves = (rows + 1) / 2;  // about two output rows per wave
+  const int waves = rows;  // one output row (pair) per wave while the grid allows
   int wgs = (waves + kGemvWaves - 1) / kGemvWaves;
   if (wgs > kGemvGrid) wgs = kGemvGrid;
   const dim3 grid{unsigned(wgs)}, block{unsigned(64 * kGemvWaves)};
