@@ -384,7 +384,7 @@ def test_commit_holds_selected_candidate():
 
 
 def test_recall_pass_access_control():
-    # NEXT-1 (per-layer access control): a local-only layer's recall pass reads the
+    # Per-layer access control: a local-only layer's recall pass reads the
     # sinks and the window only -- perturbing any other position leaves its output
     # unchanged, perturbing a position inside changes it -- while an unrestricted
     # layer's recall pass reads everything. Both commit the recall candidate.
@@ -420,7 +420,7 @@ def test_recall_pass_access_control():
 
 
 def test_all_layers_local_only_equals_local():
-    # NEXT-1 test from the scope table: with every layer local-only, an ODA step
+    # With every layer local-only, an ODA step
     # that recalls gives the Local result and commits the same candidate, layer by
     # layer, when the recall pass sees the candidates the Local pass saw (as it does
     # in a model, where every earlier layer then computes the same thing).
@@ -466,7 +466,7 @@ def test_cost_counters():
     assert cost.attention_flops(10, 32, 128) == 4 * 32 * 128 * 10
 
 
-# ---------------------------------------------------------------- whole-model accounting (NEXT-4)
+# ---------------------------------------------------------------- whole-model accounting
 
 # Qwen3-1.7B's dense sizes: 28 layers, hidden 2048, 16 q / 8 kv heads of 128 (the pages'
 # workload shape), gated MLP of 6144 and a 151936-token vocabulary with tied embeddings
@@ -546,7 +546,7 @@ def test_whole_model_bytes_bound_the_page_speedup():
     assert 149.52 / 75.54 < bound < 1 / float(cost.oda_over_full(ns, flags))
 
 
-# ---------------------------------------------------------------- DA declarations (NEXT-3)
+# ---------------------------------------------------------------- DA declarations
 
 from oracle import declare  # noqa: E402
 
@@ -613,7 +613,7 @@ def test_declaration_rows_give_the_declared_blocks():
     assert gather.da_mode_blocks(*rows[-1][:1], 800, *rows[-1][1:]) == [0] + list(range(40, 50))
 
 
-# ---------------------------------------------------------------- weight-bearing decoder (NEXT-2)
+# ---------------------------------------------------------------- weight-bearing decoder
 
 from oracle import decoder  # noqa: E402
 from oracle.bf16 import f64_to_bf16_bits  # noqa: E402
