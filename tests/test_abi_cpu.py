@@ -125,3 +125,59 @@ def test_workspace_size_monotone_and_status_strings():
     assert L.sk_workspace_bytes(32, 32) >= L.sk_workspace_bytes(1, 32)
     for code in (0, -1, -2, -3, -4, -5, -1001, 7):
         assert isinstance(L.sk_status_str(code), bytes) and L.sk_status_str(code)
+
+
+def _header_prototypes():
+    """name -> list of parameter type strings, parsed from include/sparsekv.h."""
+    import re
+    text = open(_lib.HEADER).read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"#.*", " ", text)
+    protos = {}
+    for m in re.finditer(r"([A-Za-z_][\w\s\*]*?)\b(\w+)\s*\(([^)]*)\)\s*;", text):
+        name, params = m.group(2), m.group(3)
+        parts = [p.strip() for p in params.split(",") if p.strip()]
+        if parts == ["void"]:
+            parts = []
+        protos[name] = [re.sub(r"\s*\b\w+$", "", p) if not p.endswith("*") else p for p in parts]
+    return protos
+
+
+def _kind_of_c(t):
+    t = " ".join(t.replace("const ", "").split())
+    if "*" in t or t == "hipStream_t":
+        return "ptr"
+    return {"int32_t": "i32", "int": "i32", "float": "f32", "size_t": "u64", "uint64_t": "u64",
+            "sk_paged_kv": "sk_paged_kv", "sk_da_tags": "sk_da_tags"}[t]
+
+
+def _kind_of_ctypes(t):
+    if t in (ctypes.c_void_p, ctypes.c_char_p):
+        return "ptr"
+    if t is _lib.PagedKVStruct:
+        return "sk_paged_kv"
+    if t is _lib.DaTagsStruct:
+        return "sk_da_tags"
+    if t is ctypes.c_int32:
+        return "i32"
+    if t is ctypes.c_float:
+        return "f32"
+    if t in (ctypes.c_size_t, ctypes.c_uint64):
+        return "u64"
+    raise AssertionError(t)
+
+
+def test_binding_signatures_match_the_header():
+    """Every ctypes signature has the header's parameter count and kinds, in order."""
+    protos = _header_prototypes()
+    assert set(protos) == set(_lib._SIGNATURES), set(protos) ^ set(_lib._SIGNATURES)
+    for name, (_, args) in _lib._SIGNATURES.items():
+        want = [_kind_of_c(t) for t in protos[name]]
+        got = [_kind_of_ctypes(t) for t in args]
+        assert got == want, (name, got, want)
+
+
+def test_struct_layouts_match_the_header():
+    assert ctypes.sizeof(_lib.PagedKVStruct) == 2 * 8 + 2 * 8 + 6 * 4 + 8  # 4 pointers, 6 int32, int64
+    assert _lib.PagedKVStruct.num_phys_blocks.offset == 56
+    assert ctypes.sizeof(_lib.DaTagsStruct) == 16
