@@ -120,8 +120,9 @@ __device__ inline Runs declared_runs(const DecodeParams& P, int b, int n) {
   return Runs{s0, e0 - s0, s1, e1 - s1};
 }
 
+// listed: the request's entry of list_num (block-list view only)
 template <int MODE>
-__device__ inline int request_tiles(const DecodeParams& P, int b, int n) {
+__device__ inline int request_tiles(const DecodeParams& P, int b, int n, int listed) {
   if (MODE == kFull) return (n + kBlock - 1) / kBlock;
   if (MODE == kLocal) {
     int s_end = min(P.sinks, n);
@@ -134,8 +135,8 @@ __device__ inline int request_tiles(const DecodeParams& P, int b, int n) {
     const Runs r = declared_runs(P, b, n);
     return r.l0 + r.l1;
   }
-  int k = P.list_num[b];
-  return min(max(k, 0), P.kv.max_blocks);
+  (void)b;
+  return min(max(listed, 0), P.kv.max_blocks);
 }
 
 template <int MODE>
@@ -435,9 +436,18 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
   // Gated launches: when no request is selected there is nothing to do (not even the
   // invalid-request handling, which only concerns selected requests), so every
   // workgroup leaves before touching the plan.
-  if (HAS_SEL && B <= 64) {
-    const bool any = (lane < B) && P.sel[lane] == P.sel_value;
-    if (__builtin_amdgcn_readfirstlane(__ballot(any) != 0) == 0) return;
+  // Small batches: lane b loads request b's length, selector and list length once, in one
+  // round of loads (lanes past the batch read request 0 and ignore it).
+  int l_len = 0, l_listed = 0;
+  bool l_sel = true;
+  if (B <= 64) {
+    const int bl = (lane < B) ? lane : 0;
+    l_len = P.kv.seq_lens[bl];
+    if (MODE == kList) l_listed = P.list_num[bl];
+    if (HAS_SEL) {
+      l_sel = (lane < B) && P.sel[bl] == P.sel_value;
+      if (__builtin_amdgcn_readfirstlane(__ballot(l_sel) != 0) == 0) return;
+    }
   }
 
   // ---- plan: tiles per request, tiles per split, first work item of each request --
@@ -467,10 +477,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
   if (B <= 64) {
     // every wave plans on its own with register reductions; no workgroup barrier
     int tiles = 0;
-    if (lane < B && request_active<HAS_SEL>(P, lane)) {
-      const int n = P.kv.seq_lens[lane];
+    if (lane < B && l_sel) {
+      const int n = l_len;
       const bool valid = n >= 1 && n <= maxb * kBlock;
-      if (valid) tiles = request_tiles<MODE>(P, lane, n);
+      if (valid) tiles = request_tiles<MODE>(P, lane, n, l_listed);
       if (blockIdx.x == 0 && wave == 0 && (!valid || tiles == 0)) bad_request(lane, n, valid);
     }
     const int sum = wave_sum_i(tiles), act = wave_sum_i(tiles > 0), mx = wave_max_i(tiles);
@@ -496,7 +506,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
       }
     }
     w_tiles = tiles;
-    w_len = (lane < B) ? P.kv.seq_lens[lane] : 0;
+    w_len = (lane < B) ? l_len : 0;
     w_start = (x - splits) * Hkv;
     total_items = __builtin_amdgcn_readlane(x, 63) * Hkv;
   } else {
@@ -507,7 +517,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
       if (request_active<HAS_SEL>(P, b)) {
         const int n = P.kv.seq_lens[b];
         const bool valid = n >= 1 && n <= maxb * kBlock;
-        if (valid) tiles = request_tiles<MODE>(P, b, n);
+        if (valid) tiles = request_tiles<MODE>(P, b, n, MODE == kList ? P.list_num[b] : 0);
         if (blockIdx.x == 0 && (!valid || tiles == 0)) bad_request(b, n, valid);
       }
       s_tiles[b] = tiles;
@@ -574,12 +584,17 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
     const int t_begin = split * T, t_end = min(t_begin + T, tiles_b);
 
     // q rows of the G heads of KV head g for the operand staging below, requested first so
-    // that their latency overlaps the descriptor loads. Lanes past the G heads read head 0
+    // that their latency overlaps the descriptor loads. Waves 0-3 load them (wave c the
+    // dims of chunk c) and stage both bf16 parts; waves 4-7 request nothing here, so the
+    // workgroup's first round of loads stays small. Lanes past the G heads read head 0
     // (and stage zeros).
-    const int qc = tid >> 7, qpart = (tid >> 6) & 1, qcol = lane & 15, qgrp = lane >> 4;
+    const int qc = wave & 3, qcol = lane & 15, qgrp = lane >> 4;
     const float* qrow = P.q + (int64_t(b) * Hq + g * G + (qcol < G ? qcol : 0)) * kHeadDim + 8 * (4 * qc + qgrp);
-    const f32x4 qa0 = *reinterpret_cast<const f32x4*>(qrow);
-    const f32x4 qa1 = *reinterpret_cast<const f32x4*>(qrow + 4);
+    f32x4 qa0 = {0.f, 0.f, 0.f, 0.f}, qa1 = {0.f, 0.f, 0.f, 0.f};
+    if (wave < 4) {
+      qa0 = *reinterpret_cast<const f32x4*>(qrow);
+      qa1 = *reinterpret_cast<const f32x4*>(qrow + 4);
+    }
 
     // which tile receives the current token (-1: none attended here)
     int commit_tile = -1;
@@ -608,12 +623,13 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
     const bool split_commits = commit_tile >= t_begin && commit_tile < t_end;
     const bool own_commit = split_commits && (commit_tile - t_begin) % W == wave;
     const int loop_tiles = my_tiles - (own_commit ? 1 : 0);
-    // the current token's K and V words (staged in LDS below); without a commit here the
-    // load reads q instead and is discarded, so no branch separates it from its use
-    const uint32_t* tok = reinterpret_cast<const uint32_t*>(P.q);
-    if (split_commits)
-      tok = reinterpret_cast<const uint32_t*>(((tid & 64) ? P.v_new : P.k_new) + (int64_t(b) * Hkv + g) * kHeadDim);
-    const uint32_t tok_word = tok[lane];
+    // the current token's K (wave 0) and V (wave 1) words, staged in LDS below when this
+    // split receives the token; the uniform branch sits before a full wait (the descriptor
+    // loads below are waited for before the first tile is requested), so it costs no
+    // wait-count precision
+    uint32_t tok_word = 0u;
+    if (split_commits && wave < 2)
+      tok_word = reinterpret_cast<const uint32_t*>((wave ? P.v_new : P.k_new) + (int64_t(b) * Hkv + g) * kHeadDim)[lane];
 
     // descriptors (physical block, valid range) of this wave's first 64 tiles, lane r for
     // tile r
@@ -629,22 +645,25 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
 
     // q -> MFMA B operands (hi and lo bf16 parts), staged in LDS: entry (c, part, lane) holds
     // dims 8*(4c + lane/16) .. +7 of head lane%16. The wave's first tile is requested
-    // before the q rows are used, so its latency overlaps the staging. Straight-line code
-    // (no branch between loads and use): a wave without loop tiles requests its first
-    // descriptor (block 0 of the pool when it has none) and never uses it.
+    // before the q rows are used, so its latency overlaps the staging. A wave without loop
+    // tiles requests its first descriptor (block 0 of the pool when it has none) and never
+    // uses it, so the request needs no branch.
     u32x4 k0[4], v0[4], k1[4], v1[4];
     load_tile(kpool, vpool, __builtin_amdgcn_readfirstlane(dphys), g, Hkv, lane, k0, v0);
     if (split_commits && tid < 128) s_new[tid] = tok_word;
-    {
+    if (wave < 4) {
       const float x[8] = {qa0.x, qa0.y, qa0.z, qa0.w, qa1.x, qa1.y, qa1.z, qa1.w};
-      bf16x8 o;
+      bf16x8 oh, ol;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const float v = x[i] * P.qscale;
         const __bf16 hi = __bf16(v);
-        o[i] = qpart ? __bf16(v - bf16_to_f32(hi)) : hi;
+        oh[i] = hi;
+        ol[i] = __bf16(v - bf16_to_f32(hi));
       }
-      s_q[tid] = (qcol < G) ? __builtin_bit_cast(u32x4, o) : u32x4{0u, 0u, 0u, 0u};
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      s_q[qc * 128 + lane] = (qcol < G) ? __builtin_bit_cast(u32x4, oh) : z;
+      s_q[qc * 128 + 64 + lane] = (qcol < G) ? __builtin_bit_cast(u32x4, ol) : z;
     }
     __syncthreads();
 
