@@ -108,3 +108,36 @@ def test_declared_with_selector_skips_requests():
                                      local_tokens=1024)
         ref = attention.attend(q[b], hc.k[b], hc.v[b], keysets.block_keys(ns[b], kept), SCALE)
         check_close(got[b], ref, abs_tol=1e-5, row_rel_tol=1e-4)
+
+
+def test_declared_large_batch_matches_list_path():
+    """Batches above 64 take the workgroup (LDS) planning path: 100 ragged requests with
+    seeded declarations of every mode, bit for bit against mask + list, with commits."""
+    from sparse_kv_recall_amd import ops
+    Hq, Hkv = 8, 2
+    g = np.random.default_rng(73)
+    B = 100
+    ns = [int(x) for x in g.integers(1, 3000, size=B)]
+    ns[:3] = [1, 16, 2999]
+    decl = np.zeros((B, 4), np.int32)
+    for b, n in enumerate(ns):
+        nb = (n + 15) // 16
+        mode = int(g.integers(0, 3))
+        fb = int(g.integers(-2, nb + 2))
+        decl[b] = (mode, fb, fb + int(g.integers(0, 40)), int(g.integers(0, nb + 3)))
+    hc_d = HostCache(Hq, Hkv, ns, seed=74)
+    hc_l = HostCache(Hq, Hkv, ns, seed=74)
+    q = torch.as_tensor(rand_f32(rng.mix_key(974), (B, Hq, 128), 1.0), device="cuda")
+    kn = bits_to_bf16_tensor(rand_bits(rng.mix_key(975, 1), B, Hkv))
+    vn = bits_to_bf16_tensor(rand_bits(rng.mix_key(975, 2), B, Hkv))
+    dt = torch.as_tensor(decl, device="cuda")
+    out_d = ops.da_decode_declared(q, hc_d.kv, dt, local_tokens=300, k_new=kn, v_new=vn)
+    mask = ops.da_keep_mask(dt, hc_l.kv, local_tokens=300)
+    out_l, _, _, _ = ops.da_decode_blocks(q, hc_l.kv, mask, k_new=kn, v_new=vn)
+    torch.cuda.synchronize()
+    assert np.array_equal(out_d.cpu().numpy().view(np.uint32), out_l.cpu().numpy().view(np.uint32))
+    for b, n in enumerate(ns):
+        kd, vd = ops.kv_read(hc_d.kv, b, 0, n)
+        kl, vl = ops.kv_read(hc_l.kv, b, 0, n)
+        assert np.array_equal(bf16_tensor_to_bits(kd), bf16_tensor_to_bits(kl)), b
+        assert np.array_equal(bf16_tensor_to_bits(vd), bf16_tensor_to_bits(vl)), b
