@@ -489,16 +489,21 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
     int x = wave_inclusive_scan(splits);
     // The budget above reserves one split per active request for rounding. With a few
     // long requests of similar length that reserve is mostly unused and can leave a
-    // large part of the grid idle (16 requests of 2K tiles: half of it); then take the
-    // smallest tiles per split, from total / slots up, whose splits fit the slots.
+    // large part of the grid idle (16 requests of 2K tiles: half of it); with requests of
+    // very different lengths the longest ones' splits set the launch time while the short
+    // ones' single splits finish early. In both cases take the smallest tiles per split,
+    // from total / slots up, whose splits fit the slots. (Not for one request or equal
+    // lengths that already fill most of the grid: equal splits that start at aligned
+    // offsets and move in lockstep measured slower there.)
     const int slots = int(gridDim.x) / Hkv;
-    if (4 * __builtin_amdgcn_readlane(x, 63) < 3 * slots) {
+    const int used = __builtin_amdgcn_readlane(x, 63);
+    if (4 * used < 3 * slots || (used < slots && mx * act > 2 * sum)) {
       auto count = [&](int t) { return wave_sum_i((tiles + t - 1) / t); };
       int t = (sum + slots - 1) / slots;
       const int t_cap = (mx + kMaxSplits - 1) / kMaxSplits;
       if (t < t_cap) t = t_cap;
       if (t < kMinTilesPerSplit) t = kMinTilesPerSplit;
-      for (int k = 0; k < 4 && t < T && count(t) > slots; ++k) t += (t >> 3) + 1;
+      for (int k = 0; k < 8 && t < T && count(t) > slots; ++k) t += (t >> 3) + 1;
       if (t < T && count(t) <= slots) {
         T = t;
         splits = (tiles + T - 1) / T;
