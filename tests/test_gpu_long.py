@@ -1,0 +1,65 @@
+"""GPU parity of the decode kernel in the regimes only long contexts reach: waves with more
+than 64 tiles of one split (the descriptor chunks after the first: c0 > 0), and (request,
+KV head) pairs with more than 48 splits (the split merge in several rounds). The host
+arithmetic of each case's plan is stated next to it; outputs are checked against the fp64
+oracle, and the all-blocks list view bit for bit against the Full view (same tiles, same
+splits)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import attention, keysets
+from synth import rng
+from tests.helpers import (SCALE, HostCache, bf16_tensor_to_bits, bits_to_bf16_tensor, check_close, rand_bits,
+                           rand_f32, requires_gpu)
+
+pytestmark = [pytest.mark.gpu, requires_gpu]
+
+
+def test_full_long_context_descriptor_chunks_and_blocks_view():
+    # n = 300017: 18752 tiles per KV head; grid 256, 32 slots per head, one reserved for
+    # rounding -> 605 tiles per split (31 splits), about 76 tiles per wave: two descriptor
+    # chunks. The commit lands in the last split's last chunk.
+    from sparse_kv_recall_amd import ops
+    Hq, Hkv, n = 8, 8, 300017
+    hc = HostCache(Hq, Hkv, [n], seed=80, poison=False)
+    q = rand_f32(rng.mix_key(980), (1, Hq, 128), 1.0)
+    qt = torch.as_tensor(q, device="cuda")
+    nb = (n + 15) // 16
+    words = np.zeros((1, (hc.max_blocks + 31) // 32), np.uint32)
+    for blk in range(nb):
+        words[0, blk // 32] |= np.uint32(1 << (blk % 32))
+    mask = torch.as_tensor(words.view(np.int32), device="cuda")
+    out_b, _, _, num = ops.da_decode_blocks(qt, hc.kv, mask)
+    out_f0 = ops.oda_decode_full(qt, hc.kv)
+    torch.cuda.synchronize()
+    assert int(num[0].item()) == nb
+    assert np.array_equal(out_b.cpu().numpy().view(np.uint32), out_f0.cpu().numpy().view(np.uint32))
+    kn = rand_bits(rng.mix_key(981, 1), 1, Hkv)
+    vn = rand_bits(rng.mix_key(981, 2), 1, Hkv)
+    out = ops.oda_decode_full(qt, hc.kv, bits_to_bf16_tensor(kn), bits_to_bf16_tensor(vn)).cpu().numpy()
+    k, v = hc.k[0].copy(), hc.v[0].copy()
+    oracle.oda.commit(k, v, n, kn[0], vn[0])
+    ref = attention.attend(q[0], k, v, keysets.full_keys(n), SCALE)
+    check_close(out[0], ref, abs_tol=1e-5, row_rel_tol=1e-4, what="full n=%d" % n)
+    kr, vr = ops.kv_read(hc.kv, 0, n - 1, 1)
+    assert np.array_equal(bf16_tensor_to_bits(kr)[0], kn[0]) and np.array_equal(bf16_tensor_to_bits(vr)[0], vn[0])
+    # before the commit the Full view attended the old slot n - 1
+    ref0 = attention.attend(q[0], hc.k[0], hc.v[0], keysets.full_keys(n), SCALE)
+    check_close(out_f0.cpu().numpy()[0], ref0, abs_tol=1e-5, row_rel_tol=1e-4, what="full n=%d (no commit)" % n)
+
+
+@pytest.mark.parametrize("n", [70001, 4096 * 16 * 4 + 3])
+def test_full_many_splits_merge_in_rounds(n):
+    # one KV head: 256 slots, 255 after the rounding reserve. n = 70001: 4376 tiles -> 18
+    # tiles per split, 244 splits; n = 262147: 16385 tiles -> 65 tiles per split, 253 splits
+    # (and 9 tiles per wave). Both merge in 6 rounds of up to 48 splits.
+    from sparse_kv_recall_amd import ops
+    Hq, Hkv = 4, 1
+    hc = HostCache(Hq, Hkv, [n], seed=82, poison=True)
+    q = rand_f32(rng.mix_key(982, n), (1, Hq, 128), 1.0)
+    out = ops.oda_decode_full(torch.as_tensor(q, device="cuda"), hc.kv).cpu().numpy()
+    ref = attention.attend(q[0], hc.k[0], hc.v[0], keysets.full_keys(n), SCALE)
+    check_close(out[0], ref, abs_tol=1e-5, row_rel_tol=1e-4, what="full Hkv=1 n=%d" % n)
