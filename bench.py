@@ -133,12 +133,53 @@ def view_sweep(device, Hq=32, Hkv=8, reps=10, min_bytes=1 << 30):
         return {"view": view, "batch": B, "n": n, "us_per_launch": round(us, 2),
                 "frac_of_peak": round(nbytes / (us * 1e-6) / (HBM_PEAK_GBS * 1e9), 3)}
 
+    def ragged_full(B, lo=4096, hi=131072):
+        # a large batch of ragged lengths (log-uniform in [lo, hi], seeded), each request's
+        # pages contiguous in one pool; one Full launch per replay (the pool exceeds 1 GiB)
+        import math
+        import numpy as np
+        g = np.random.default_rng(np.random.SeedSequence([9, 7, B]))
+        ns = np.floor(np.exp(g.uniform(math.log(lo), math.log(hi), size=B))).astype(np.int64)
+        nbs = (ns + 15) // 16
+        mb, total = int(nbs.max()), int(nbs.sum())
+        bt = np.zeros((B, mb), np.int32)
+        off = 0
+        for b in range(B):
+            bt[b, :nbs[b]] = np.arange(off, off + nbs[b])
+            off += int(nbs[b])
+        cache = ops.PagedKVCache(total, B, Hq, Hkv, mb, block_tables=torch.as_tensor(bt, device=device),
+                                 seq_lens=torch.as_tensor(ns.astype(np.int32), device=device), device=device)
+        sdev.fill_normal_(cache.k_pool, rng.mix_key(5, 1, 99), 0)
+        sdev.fill_normal_(cache.v_pool, rng.mix_key(5, 2, 99), 0)
+        q = torch.randn(B, Hq, 128, device=device)
+        out = torch.zeros(B, Hq, 128, device=device)
+        ws = ops.workspace(B, Hq, device)
+        g2 = capture_graph(lambda: ops.oda_decode_full(q, cache, out=out, ws=ws))
+        for _ in range(2):
+            g2.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps // 2):
+            g2.replay()
+        e1.record()
+        e1.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / (reps // 2)
+        nbytes = int(ns.sum()) * Hkv * 512 + B * 2 * Hq * 512
+        del g2, cache
+        torch.cuda.empty_cache()
+        return {"view": "full", "batch": B, "n": "ragged %d-%d (log-uniform)" % (lo, hi), "us_per_launch": round(us, 2),
+                "frac_of_peak": round(nbytes / (us * 1e-6) / (HBM_PEAK_GBS * 1e9), 3)}
+
     cases = [("full", 1, n) for n in (4096, 16384, 32768, 65536, 131072, 262144)]
     cases += [("full", B, 32768) for B in (2, 4, 8, 12, 16, 24, 32)]
     cases += [("local", B, 32768) for B in (1, 8, 32, 64)]
     res = []
     for view, B, n in cases:
         res.append(one(view, B, n))
+        log("sweep: %s" % json.dumps(res[-1]))
+    for B in (96, 128):
+        res.append(ragged_full(B))
         log("sweep: %s" % json.dumps(res[-1]))
     return res
 
