@@ -209,6 +209,44 @@ def stream_peak(device, gib=4, reps=5):
     return nbytes / (ms * 1e-3) / 1e9
 
 
+def stream_floor(device, sizes, launches=36, reps=3):
+    """Size-matched streaming reference: sk_stream_read launched `launches` times in one
+    HIP graph, each launch over its own slice of the given size (as the decode launches
+    rotate over 36 layers' pools, so no slice is still in the last-level cache). Per
+    size, the time of one launch that does nothing but stream that many bytes, launch
+    and ramp included: the floor for a decode launch that reads the same bytes."""
+    import torch
+    from sparse_kv_recall_amd import ops
+    from sparse_kv_recall_amd.stack import capture_graph
+    out = {}
+    for name, nbytes in sizes:
+        per = (int(nbytes) + 4095) // 4096 * 4096
+        data = torch.ones(launches * per // 4, dtype=torch.int32, device=device)
+        sink = torch.empty(ops.STREAM_READ_GRID, dtype=torch.int32, device=device)
+        slices = [data[i * per // 4:(i + 1) * per // 4] for i in range(launches)]
+
+        def run():
+            for sl in slices:
+                ops.stream_read(sl, sink)
+
+        graph = capture_graph(run)
+        graph.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            graph.replay()
+        e1.record()
+        e1.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / (reps * launches)
+        gbs = per / (us * 1e-6) / 1e9
+        out[name] = {"bytes": per, "us_per_launch": round(us, 2), "achieved_GBs": round(gbs, 1),
+                     "frac": round(gbs / HBM_PEAK_GBS, 4)}
+        del graph, slices, data
+        torch.cuda.empty_cache()
+    return out
+
+
 def gated_off_launch(stack, feeder, reps=20):
     """Per-launch time of the recall pass's Full launches when the gate is 0, so that every
     workgroup leaves at once: the per-node cost that the step graph pays 36 times on
@@ -823,6 +861,10 @@ def main():
     log("gated-off Full launch: %.2f us" % (gated_off_ms * 1e3))
     blocks = roofline_blocks(stack, feeder, args.roofline_reps)
     log("block-list view: %s" % json.dumps(blocks))
+    floor = stream_floor(device, [("local_2052_positions", min(n_now, wl.sinks + wl.window) * wl.Hkv * 512),
+                                  ("keep_12.5pct_positions", blocks["keep_12.5pct"]["kept_positions"] * wl.Hkv * 512),
+                                  ("full_n", n_now * wl.Hkv * 512)])
+    log("size-matched streaming reference: %s" % json.dumps(floor))
     full_only = always_full_rate(stack, feeder, wl, min(64, args.steps))
     log("always-Full baseline: %s" % json.dumps(full_only))
     hybrid = hybrid_rate(stack, feeder, wl, min(256, args.steps))
@@ -873,6 +915,9 @@ def main():
         "roofline_block_sparse": dict(blocks, kernel="decode_kernel<list> over a permuted block table (36-layer "
                                       "rotation, n=%d); also per layer with the rewrite (gather) in every call and "
                                       "once per step" % n_now),
+        "stream_floor": dict(floor, note="sk_stream_read alone, 36 launches over distinct slices in one graph, "
+                                         "at the K/V bytes of the Local view, the 12.5 % block list and the Full "
+                                         "view: what a launch that only streams those bytes costs"),
         "always_full_baseline": dict(full_only, speedup_of_oda=round(tok_s / full_only["tok_s"], 3),
                                      attention_bytes_ratio=round(float(full_bytes / step_bytes), 3)),
         "dispatch": {"graph_launches_per_step": 2 + 2 * wl.layers,
