@@ -284,6 +284,33 @@ __device__ inline float rows_sum(float v) {
   return a + b;
 }
 
+// One round of the split merge over nb <= NB consecutive splits, for one output element
+// per lane (all lanes of the wave on one head): lane u loads the (m, l) of split u of the
+// round (ml: the first split's m of this head; its l follows G floats later), every lane
+// loads its element's accumulator of each split (acc: the first split's, splits `stride`
+// floats apart), all in one round of independent loads. NB is the load count per lane:
+// rounds are sized to the splits they hold, so that few splits issue few loads.
+template <int NB>
+__device__ inline void merge_round(const float* ml, const float* acc, uint32_t stride, int nb, int G, int lane,
+                                   float& M, float& L, float& A) {
+  const uint32_t mine = uint32_t(min(lane, nb - 1)) * stride;
+  const float mv = fetch_published(ml + mine);
+  const float lv = fetch_published(ml + mine + G);
+  float as[NB];
+#pragma unroll
+  for (int u = 0; u < NB; ++u) as[u] = fetch_published(acc + uint32_t(min(u, nb - 1)) * stride);
+  const float Mn = fmaxf(M, wave_max((lane < nb) ? mv : -INFINITY));
+  const float Mu = (Mn == -INFINITY) ? 0.f : Mn;
+  const float r = __builtin_amdgcn_exp2f(M - Mu);
+  const float e = (lane < nb) ? __builtin_amdgcn_exp2f(mv - Mu) : 0.f;
+  L = L * r + wave_sum(e * lv);
+  A *= r;
+  // weights past the round are zero and their (repeated) accumulators finite
+#pragma unroll
+  for (int u = 0; u < NB; ++u) A += lane_value(e, u) * as[u];
+  M = Mn;
+}
+
 // s_waitcnt vmcnt(0): all of this wave's stores have completed (gfx9 counts stores in vmcnt).
 __device__ inline void wait_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
@@ -820,24 +847,14 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
           float M = -INFINITY, L = 0.f, A = 0.f;
           for (int s0 = 0; s0 < S; s0 += kMergeBatch) {
             const int nb = min(kMergeBatch, S - s0);
-            const uint32_t ml = uint32_t(s0 + min(lane, nb - 1)) * stride + G * kHeadDim + h;
-            const float mv = fetch_published(base + ml);
-            const float lv = fetch_published(base + ml + G);
-            float as[kMergeBatch];
-#pragma unroll
-            for (int u = 0; u < kMergeBatch; ++u)
-              as[u] = fetch_published(base + (uint32_t(s0 + min(u, nb - 1)) * stride + uint32_t(idx)));
-            const float Mn = fmaxf(M, wave_max((lane < nb) ? mv : -INFINITY));
-            const float Mu = (Mn == -INFINITY) ? 0.f : Mn;
-            const float r = __builtin_amdgcn_exp2f(M - Mu);
-            const float e = (lane < nb) ? __builtin_amdgcn_exp2f(mv - Mu) : 0.f;
-            L = L * r + wave_sum(e * lv);
-            A *= r;
-            // weights past the batch are zero and their (repeated) accumulators finite
-#pragma unroll
-            for (int u = 0; u < kMergeBatch; ++u)
-              A += lane_value(e, u) * as[u];
-            M = Mn;
+            const uint32_t ml = uint32_t(s0) * stride + G * kHeadDim + h;
+            const float* acc0 = base + (uint32_t(s0) * stride + uint32_t(idx));
+            if (nb <= 16)
+              merge_round<16>(base + ml, acc0, stride, nb, G, lane, M, L, A);
+            else if (nb <= 32)
+              merge_round<32>(base + ml, acc0, stride, nb, G, lane, M, L, A);
+            else
+              merge_round<kMergeBatch>(base + ml, acc0, stride, nb, G, lane, M, L, A);
           }
           P.out[(int64_t(b) * Hq + g * G + h) * kHeadDim + (idx & (kHeadDim - 1))] = (L > 0.f) ? A / L : 0.f;
         }
