@@ -51,11 +51,13 @@ def test_full_long_context_descriptor_chunks_and_blocks_view():
     check_close(out_f0.cpu().numpy()[0], ref0, abs_tol=1e-5, row_rel_tol=1e-4, what="full n=%d (no commit)" % n)
 
 
-@pytest.mark.parametrize("n", [70001, 4096 * 16 * 4 + 3])
+@pytest.mark.parametrize("n", [9337, 70001, 4096 * 16 * 4 + 3])
 def test_full_many_splits_merge_in_rounds(n):
-    # one KV head: 256 slots, 255 after the rounding reserve. n = 70001: 4376 tiles -> 18
-    # tiles per split, 244 splits; n = 262147: 16385 tiles -> 65 tiles per split, 253 splits
-    # (and 9 tiles per wave). Both merge in 6 rounds of up to 48 splits.
+    # one KV head: 256 slots, 255 after the rounding reserve. n = 9337: 584 tiles -> 8 tiles
+    # per split (the minimum), 73 splits, merged in a round of 48 and one of 25 (the 32-load
+    # round). n = 70001: 4376 tiles -> 18 tiles per split, 244 splits; n = 262147: 16385
+    # tiles -> 65 tiles per split, 253 splits (and 9 tiles per wave). Both merge in 6 rounds
+    # of up to 48 splits, the last of 4 and 13 splits (16-load rounds).
     from sparse_kv_recall_amd import ops
     Hq, Hkv = 4, 1
     hc = HostCache(Hq, Hkv, [n], seed=82, poison=True)
