@@ -385,13 +385,15 @@ def copy_calibration(device):
     return a.numel() * 2
 
 
-def cpu_baseline(wl, recall_rate, budget_s=20.0):
-    """The fp64 oracle, as it stands, on a bounded sample of the same workload: Local
-    layer-steps and one Full layer-step at step 0 (n = 131073), timed on the host cores.
-    Input generation is not timed. Tokens/s = 1 / (L * t_local + rate * L * t_full)."""
+def cpu_baseline(wl, recall_rate, budget_s=20.0, local_s=2.0):
+    """The fp64 oracle, as it stands, on a bounded sample of the same workload at step 0
+    (n = 131073), timed on the host cores: Local layer-steps (four layers' sinks and
+    windows, each step with another step's candidates) for about `local_s` seconds, then
+    Full layer-steps over one layer's whole history (each with another step's candidates)
+    until about `budget_s` seconds of oracle time in all. Input generation is not timed.
+    Tokens/s = 1 / (L * t_local + rate * L * t_full) with the mean times per layer-step."""
     import numpy as np
     import oracle
-    from synth.workloads import C_KHIST, C_VHIST  # noqa: F401
     try:
         from threadpoolctl import threadpool_info
         threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
@@ -400,37 +402,47 @@ def cpu_baseline(wl, recall_rate, budget_s=20.0):
     H0 = int(wl.H0[0])
     n = H0 + 1
     scale = 1.0 / math.sqrt(128.0)
-    t_local, n_local = 0.0, 0
-    layer_full = 1
-    # Local sample: the positions the Local view reads, per layer
-    for l in range(4):
+    locals_ = []
+    for l in range(4):  # the positions the Local view reads, per layer
         k = np.zeros((n, wl.Hkv, 128), np.uint16)
         v = np.zeros((n, wl.Hkv, 128), np.uint16)
         k[:4] = wl.hist_bits("k", l, 0, 4)
         v[:4] = wl.hist_bits("v", l, 0, 4)
         k[n - 2048:n - 1] = wl.hist_bits("k", l, n - 2048, 2047)
         v[n - 2048:n - 1] = wl.hist_bits("v", l, n - 2048, 2047)
-        q = wl.cand_q(0, l, 0, 0)
-        kn, vn = wl.cand_kv(0, l, 0, 0)
+        locals_.append((l, k, v))
+    t_local, n_local = 0.0, 0
+    while (t_local < local_s or n_local < 4) and n_local < 4096:
+        l, k, v = locals_[n_local % 4]
+        step = n_local // 4
+        q = wl.cand_q(step, l, 0, 0)
+        kn, vn = wl.cand_kv(step, l, 0, 0)
         t0 = time.perf_counter()
         oracle.oda.local_pass(q, kn, vn, k, v, n, scale)
         t_local += time.perf_counter() - t0
         n_local += 1
-    t_local /= n_local
+    del locals_
+    layer_full = 1
     k = np.empty((n, wl.Hkv, 128), np.uint16)
     v = np.empty((n, wl.Hkv, 128), np.uint16)
     k[:H0] = wl.hist_bits("k", layer_full, 0, H0)
     v[:H0] = wl.hist_bits("v", layer_full, 0, H0)
-    q = wl.cand_q(0, layer_full, 1, 0)
-    kn, vn = wl.cand_kv(0, layer_full, 1, 0)
-    t0 = time.perf_counter()
-    oracle.oda.full_pass(q, kn, vn, k, v, n, scale)
-    t_full = time.perf_counter() - t0
-    step_s = wl.layers * t_local + recall_rate * wl.layers * t_full
+    t_full, n_full = 0.0, 0
+    while (t_local + t_full < budget_s or n_full < 1) and n_full < 256:
+        q = wl.cand_q(n_full, layer_full, 1, 0)
+        kn, vn = wl.cand_kv(n_full, layer_full, 1, 0)
+        t0 = time.perf_counter()
+        oracle.oda.full_pass(q, kn, vn, k, v, n, scale)
+        t_full += time.perf_counter() - t0
+        n_full += 1
+    mean_local, mean_full = t_local / n_local, t_full / n_full
+    step_s = wl.layers * mean_local + recall_rate * wl.layers * mean_full
     return {"value": 1.0 / step_s, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": ("fp64 oracle at step 0 (n=131073): %d Local layer-steps (%.4f s each) and 1 Full "
-                       "layer-step (%.3f s); per-step time = 36*t_local + 0.125*36*t_full; input "
-                       "generation not timed" % (n_local, t_local, t_full))}
+            "sample": ("fp64 oracle at n=131073: %d Local layer-steps (4 layers' sinks and windows, %.4f s each) "
+                       "and %d Full layer-steps (layer %d's whole history, %.3f s each), each with another "
+                       "step's candidates; %.1f s of oracle time; per-step time = 36*t_local + %.3f*36*t_full; "
+                       "input generation not timed" % (n_local, mean_local, n_full, layer_full, mean_full,
+                                                        t_local + t_full, recall_rate))}
 
 
 def always_full_rate(stack, feeder, wl, steps):
