@@ -1,9 +1,9 @@
-"""GPU parity of the decode kernel in the regimes only long contexts reach: waves with more
-than 64 tiles of one split (the descriptor chunks after the first: c0 > 0), and (request,
-KV head) pairs with more than 48 splits (the split merge in several rounds). The host
-arithmetic of each case's plan is stated next to it; outputs are checked against the fp64
-oracle, and the all-blocks list view bit for bit against the Full view (same tiles, same
-splits)."""
+"""GPU parity of the decode kernel in the regimes only long contexts or large pools reach:
+waves with more than 64 tiles of one split (the descriptor chunks after the first: c0 > 0),
+(request, KV head) pairs with more than 48 splits (the split merge in several rounds), and
+tiles past the 4 GiB offset of a pool. The host arithmetic of each case's plan is stated
+next to it; outputs are checked against the fp64 oracle, and the all-blocks list view bit
+for bit against the Full view (same tiles, same splits)."""
 
 import numpy as np
 import pytest
@@ -65,3 +65,38 @@ def test_full_many_splits_merge_in_rounds(n):
     out = ops.oda_decode_full(torch.as_tensor(q, device="cuda"), hc.kv).cpu().numpy()
     ref = attention.attend(q[0], hc.k[0], hc.v[0], keysets.full_keys(n), SCALE)
     check_close(out[0], ref, abs_tol=1e-5, row_rel_tol=1e-4, what="full Hkv=1 n=%d" % n)
+
+
+def test_pool_beyond_4gib():
+    # 400000 spare blocks at 8 KV heads: each of the K and V pools holds 13.1 GB, and the
+    # permuted placement puts about two thirds of the used blocks past the 4 GiB offset
+    # (block 131072), where tile offsets need 64-bit arithmetic. Full, Local and all-blocks
+    # list views with commits, against the fp64 oracle; the committed slots read back.
+    from sparse_kv_recall_amd import ops
+    Hq, Hkv = 32, 8
+    ns = [3001, 2100]
+    hc = HostCache(Hq, Hkv, ns, seed=84, spare_blocks=400000)
+    assert hc.kv.k_pool.numel() * 2 > (1 << 32)
+    assert (hc.bt[0, :(ns[0] + 15) // 16] >= 131072).sum() > 100
+    q = rand_f32(rng.mix_key(984), (2, Hq, 128), 1.0)
+    qt = torch.as_tensor(q, device="cuda")
+    kn = rand_bits(rng.mix_key(985, 1), 2, Hkv)
+    vn = rand_bits(rng.mix_key(985, 2), 2, Hkv)
+    kt, vt = bits_to_bf16_tensor(kn), bits_to_bf16_tensor(vn)
+    words = np.zeros((2, (hc.max_blocks + 31) // 32), np.uint32)
+    for b, n in enumerate(ns):
+        for blk in range((n + 15) // 16):
+            words[b, blk // 32] |= np.uint32(1 << (blk % 32))
+    mask = torch.as_tensor(words.view(np.int32), device="cuda")
+    outs = {"full": ops.oda_decode_full(qt, hc.kv, kt, vt).cpu().numpy(),
+            "local": ops.oda_decode_local(qt, hc.kv, kt, vt, sinks=4, window=2048).cpu().numpy(),
+            "blocks": ops.da_decode_blocks(qt, hc.kv, mask, kt, vt)[0].cpu().numpy()}
+    for b, n in enumerate(ns):
+        k, v = hc.k[b].copy(), hc.v[b].copy()
+        oracle.oda.commit(k, v, n, kn[b], vn[b])
+        for view, keys in (("full", keysets.full_keys(n)), ("local", keysets.local_keys(n, 4, 2048)),
+                           ("blocks", keysets.full_keys(n))):
+            ref = attention.attend(q[b], k, v, keys, SCALE)
+            check_close(outs[view][b], ref, abs_tol=1e-5, row_rel_tol=1e-4, what="%s n=%d" % (view, n))
+        kr, vr = ops.kv_read(hc.kv, b, n - 1, 1)
+        assert np.array_equal(bf16_tensor_to_bits(kr)[0], kn[b]) and np.array_equal(bf16_tensor_to_bits(vr)[0], vn[b])
