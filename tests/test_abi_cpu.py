@@ -181,3 +181,21 @@ def test_struct_layouts_match_the_header():
     assert ctypes.sizeof(_lib.PagedKVStruct) == 2 * 8 + 2 * 8 + 6 * 4 + 8  # 4 pointers, 6 int32, int64
     assert _lib.PagedKVStruct.num_phys_blocks.offset == 56
     assert ctypes.sizeof(_lib.DaTagsStruct) == 16
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """There is no CPU or PyTorch fallback behind the entry points: with the library
+    absent the binding raises LibraryMissing, and host tensors are refused before any
+    call (the kernels take device memory only)."""
+    import torch
+    from sparse_kv_recall_amd import ops
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "libsparsekv.so"))
+    monkeypatch.setattr(_lib, "_lib", None)
+    for fn in (lambda: ops.workspace_bytes(1, 8), lambda: ops.workspace(1, 8, device="cpu"),
+               lambda: _lib.call("sk_status_str", 0)):
+        with pytest.raises(_lib.LibraryMissing):
+            fn()
+    for fn in (lambda: ops.PagedKVCache(4, 1, 8, 2, 4, device="cpu"),
+               lambda: ops.stream_read(torch.zeros(64, dtype=torch.int32))):
+        with pytest.raises(ValueError, match="GPU tensor"):
+            fn()
