@@ -9,10 +9,10 @@
 // never goes back to the host.
 //
 // The head here is a two-layer MLP, q = <w2, GELU(W1 x + b1)> + b2 (exact-erf GELU).
-// It is a GEMV: each wave keeps one row of W1 (in_dim fp32) in registers and dots it
-// with every request's x; no matrix cores are used. Per-workgroup partial sums are
-// published with device-coherent stores and added in a fixed order by the last
-// workgroup (atomic ticket), so q is deterministic.
+// It is a GEMV: each group of four waves keeps one row of W1 (in_dim fp32, a quarter
+// each) in registers and dots it with every request's x; no matrix cores are used. Per-workgroup
+// partial sums are published with device-coherent stores and added in a fixed order by
+// the last workgroup (atomic ticket), so q is deterministic.
 #include <math.h>
 
 #include "sk_internal.h"
@@ -22,34 +22,51 @@ namespace {
 
 constexpr int kRecallMaxBatch = 64;
 constexpr int kRecallMaxIn = 65536;
-constexpr int kRecallWaves = 4;  // one W1 row per wave
-constexpr int kRecallMaxParts = 8192;  // workgroups x batch partial sums the last workgroup stages
+// Measured at 6144 -> 512, batch 1 (per call in a graph): 16 waves per workgroup, 4 per
+// row (128 workgroups) took 6.6 us; one row per wave in 4-wave workgroups 9.7 us; other
+// splits (1, 2 or 8 waves per row; 32 to 512 workgroups, i.e. fewer parallel loads or more
+// ticket atomics) 7.0-11.8 us.
+constexpr int kRecallWaves = 16;     // waves per workgroup
+constexpr int kRecallRowWaves = 4;   // waves sharing one W1 row (each a contiguous quarter of its columns)
+constexpr int kRecallRows = kRecallWaves / kRecallRowWaves;  // W1 rows per workgroup
+constexpr int kRecallMaxParts = 16384;  // workgroups x batch partial sums the last workgroup stages
 
 __device__ inline float gelu_erf(float a) { return 0.5f * a * (1.0f + erff(a * 0.70710678118654752f)); }
 
-// CHUNKS > 0: the W1 row (CHUNKS float4 per lane) stays in registers across requests.
-// CHUNKS == 0: long rows are streamed from memory once per request.
+// CHUNKS > 0: the wave's part of its W1 row (CHUNKS float4 per lane) stays in registers
+// across requests. CHUNKS == 0: long rows are streamed from memory once per request.
 template <int CHUNKS>
-__global__ __launch_bounds__(256) void recall_kernel(const float* __restrict__ x, const float* __restrict__ W1,
-                                                     const float* __restrict__ b1, const float* __restrict__ w2,
-                                                     const float* __restrict__ b2, int B, int in_dim, int hidden,
-                                                     float theta, float* __restrict__ q_out,
-                                                     int32_t* __restrict__ gate_out, float* partials,
-                                                     uint32_t* ticket) {
-  __shared__ float s_c[kRecallWaves][kRecallMaxBatch];
+__global__ __launch_bounds__(64 * kRecallWaves) void recall_kernel(
+    const float* __restrict__ x, const float* __restrict__ W1, const float* __restrict__ b1,
+    const float* __restrict__ w2, const float* __restrict__ b2, int B, int in_dim, int hidden, float theta,
+    float* __restrict__ q_out, int32_t* __restrict__ gate_out, float* partials, uint32_t* ticket) {
+  __shared__ float s_d[kRecallWaves][kRecallMaxBatch];
   __shared__ float s_part[kRecallMaxParts];
   __shared__ int s_last;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int row = blockIdx.x * kRecallWaves + wave;
+  const int row0 = blockIdx.x * kRecallRows;
+  const int row = row0 + wave / kRecallRowWaves;
+  // this wave's columns of the row, in float4 units: [c_begin, c_end)
   const int n4 = in_dim / 4;
+  const int per = (n4 + kRecallRowWaves - 1) / kRecallRowWaves;
+  const int c_begin = (wave % kRecallRowWaves) * per, c_end = min(n4, c_begin + per);
   const f32x4* wrow = reinterpret_cast<const f32x4*>(W1 + size_t(row < hidden ? row : 0) * in_dim);
+  // the rows' bias and output weight, requested with the row so that they are in
+  // registers when the row sums are finished
+  float b1r[kRecallRows], w2r[kRecallRows];
+#pragma unroll
+  for (int r = 0; r < kRecallRows; ++r) {
+    const bool ok = row0 + r < hidden;
+    b1r[r] = ok ? b1[row0 + r] : 0.f;
+    w2r[r] = ok ? w2[row0 + r] : 0.f;
+  }
   constexpr int R = CHUNKS > 0 ? CHUNKS : 1;
   f32x4 w[R];
   if (CHUNKS > 0) {
 #pragma unroll
     for (int i = 0; i < R; ++i) {
-      int c = lane + 64 * i;
-      w[i] = (row < hidden && c < n4) ? wrow[c] : f32x4{0.f, 0.f, 0.f, 0.f};
+      const int c = c_begin + lane + 64 * i;
+      w[i] = (row < hidden && c < c_end) ? wrow[c] : f32x4{0.f, 0.f, 0.f, 0.f};
     }
   }
   for (int b = 0; b < B; ++b) {
@@ -58,30 +75,36 @@ __global__ __launch_bounds__(256) void recall_kernel(const float* __restrict__ x
     if (CHUNKS > 0) {
 #pragma unroll
       for (int i = 0; i < R; ++i) {
-        int c = lane + 64 * i;
-        if (c < n4) {
+        const int c = c_begin + lane + 64 * i;
+        if (c < c_end) {
           f32x4 v = xb[c];
           dot += w[i].x * v.x + w[i].y * v.y + w[i].z * v.z + w[i].w * v.w;
         }
       }
     } else if (row < hidden) {
-      for (int c = lane; c < n4; c += 64) {
+      for (int c = c_begin + lane; c < c_end; c += 64) {
         f32x4 v = xb[c], u = wrow[c];
         dot += u.x * v.x + u.y * v.y + u.z * v.z + u.w * v.w;
       }
     }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) dot += __shfl_xor(dot, off);
-    if (lane == 0) s_c[wave][b] = (row < hidden) ? w2[row] * gelu_erf(dot + b1[row]) : 0.f;
+    if (lane == 0) s_d[wave][b] = dot;
   }
   __syncthreads();
-  // Workgroup sums are published with device-coherent stores; once they have completed,
-  // one thread takes the ticket. The last workgroup loads every workgroup's sums in one
-  // round of device-coherent loads into LDS and adds them in workgroup order.
+  // Row dots from their parts, then the workgroup's sum of w2 * GELU(W1 x + b1) over its
+  // rows. Workgroup sums are published with device-coherent stores; once they have
+  // completed, one thread takes the ticket. The last workgroup loads every workgroup's
+  // sums in one round of device-coherent loads into LDS and adds them in a fixed order.
   for (int b = tid; b < B; b += blockDim.x) {
     float s = 0.f;
 #pragma unroll
-    for (int i = 0; i < kRecallWaves; ++i) s += s_c[i][b];
+    for (int r = 0; r < kRecallRows; ++r) {
+      float d = 0.f;
+#pragma unroll
+      for (int h = 0; h < kRecallRowWaves; ++h) d += s_d[r * kRecallRowWaves + h][b];
+      if (row0 + r < hidden) s += w2r[r] * gelu_erf(d + b1r[r]);
+    }
     __hip_atomic_store(&partials[size_t(blockIdx.x) * B + b], s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's stores have completed
@@ -89,16 +112,22 @@ __global__ __launch_bounds__(256) void recall_kernel(const float* __restrict__ x
   if (tid == 0) s_last = (atomicAdd(ticket, 1u) == gridDim.x - 1);
   __syncthreads();
   if (!s_last) return;
-  const int total = int(gridDim.x) * B;
+  const int nwg = int(gridDim.x), total = nwg * B;
   for (int e = tid; e < total; e += blockDim.x)
     s_part[e] = __hip_atomic_load(&partials[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
-  for (int b = tid; b < B; b += blockDim.x) {
+  // wave w adds requests w, w + kRecallWaves, ...: lane u the workgroups u, u + 64, ...
+  // in order, then a butterfly over the lanes (a fixed order: deterministic)
+  for (int b = wave; b < B; b += kRecallWaves) {
     float s = 0.f;
-    for (unsigned i = 0; i < gridDim.x; ++i) s += s_part[i * B + b];
-    float q = s + b2[0];
-    q_out[b] = q;
-    gate_out[b] = (q > theta) ? 1 : 0;
+    for (int i = lane; i < nwg; i += 64) s += s_part[i * B + b];
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
+    if (lane == 0) {
+      const float q = s + b2[0];
+      q_out[b] = q;
+      gate_out[b] = (q > theta) ? 1 : 0;
+    }
   }
   if (tid == 0) *ticket = 0u;
 }
@@ -202,7 +231,7 @@ template <int CHUNKS>
 int launch_recall(const float* x, const float* W1, const float* b1, const float* w2, const float* b2, int B,
                   int in_dim, int hidden, float theta, float* q_out, int32_t* gate_out, void* ws,
                   hipStream_t stream) {
-  int nwg = (hidden + kRecallWaves - 1) / kRecallWaves;
+  int nwg = (hidden + kRecallRows - 1) / kRecallRows;
   float* partials = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(ws) + kPartialsOffset);
   uint32_t* ticket = reinterpret_cast<uint32_t*>(ws) + 1;
   hipLaunchKernelGGL(recall_kernel<CHUNKS>, dim3(nwg), dim3(64 * kRecallWaves), 0, stream, x, W1, b1, w2, b2, B,
@@ -223,13 +252,15 @@ int oda_recall_score(const float* x, const float* W1, const float* b1, const flo
   if (!x || !W1 || !b1 || !w2 || !b2 || !q_out || !gate_out || !ws) return SK_E_NULL;
   if (batch < 1 || batch > kRecallMaxBatch || in_dim < 4 || in_dim > kRecallMaxIn || (in_dim % 4) || hidden < 1)
     return SK_E_RANGE;
-  const size_t parts = size_t((hidden + kRecallWaves - 1) / kRecallWaves) * batch;
+  const size_t parts = size_t((hidden + kRecallRows - 1) / kRecallRows) * batch;
   if (parts > size_t(kRecallMaxParts)) return SK_E_RANGE;
   size_t need = kPartialsOffset + parts * 4;
   if (ws_bytes < need) return SK_E_WORKSPACE;
-  int chunks = (in_dim / 4 + 63) / 64;  // float4 per lane
+  const int per = (in_dim / 4 + kRecallRowWaves - 1) / kRecallRowWaves;  // float4 of a wave's part of a row
+  const int chunks = (per + 63) / 64;                                     // per lane
   if (chunks <= 8) return launch_recall<8>(x, W1, b1, w2, b2, batch, in_dim, hidden, theta, q_out, gate_out, ws, stream);
-  if (chunks <= 24) return launch_recall<24>(x, W1, b1, w2, b2, batch, in_dim, hidden, theta, q_out, gate_out, ws, stream);
+  if (chunks <= 12) return launch_recall<12>(x, W1, b1, w2, b2, batch, in_dim, hidden, theta, q_out, gate_out, ws, stream);
+  if (chunks <= 16) return launch_recall<16>(x, W1, b1, w2, b2, batch, in_dim, hidden, theta, q_out, gate_out, ws, stream);
   return launch_recall<0>(x, W1, b1, w2, b2, batch, in_dim, hidden, theta, q_out, gate_out, ws, stream);
 }
 
