@@ -188,7 +188,7 @@ int oda_decode_full(const float* q, sk_paged_kv kv, const void* k_new, const voi
  *  W1 : fp32 [hidden][in_dim] row-major;  b1, w2 : fp32 [hidden];  b2 : fp32 [1]
  *  q_out : fp32 [batch];  gate_out : int32 [batch]
  * Host-checked: 1 <= batch <= 64, in_dim % 4 == 0, 1 <= in_dim <= 65536,
- * 1 <= hidden, ceil(hidden / 4) * batch <= 8192. The reduction order is fixed,
+ * 1 <= hidden, ceil(hidden / 4) * batch <= 16384. The reduction order is fixed,
  * so results are deterministic. */
 int oda_recall_score(const float* x, const float* W1, const float* b1, const float* w2,
                      const float* b2, int32_t batch, int32_t in_dim, int32_t hidden,

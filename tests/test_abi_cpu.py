@@ -62,6 +62,9 @@ def test_other_entry_points_validation():
     assert L.oda_recall_score(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 6, 4, 0.0, FAKE, FAKE, FAKE, 1 << 20, None) == SK_E_RANGE
     assert L.oda_recall_score(FAKE, FAKE, FAKE, FAKE, FAKE, 65, 8, 4, 0.0, FAKE, FAKE, FAKE, 1 << 20, None) == SK_E_RANGE
     assert L.oda_recall_score(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, 4, 0.0, FAKE, FAKE, FAKE, 8, None) == SK_E_WORKSPACE
+    # the last workgroup stages ceil(hidden / 4) * batch partial sums: 16384 at most
+    assert L.oda_recall_score(FAKE, FAKE, FAKE, FAKE, FAKE, 64, 8, 1028, 0.0, FAKE, FAKE, FAKE, 1 << 20, None) == SK_E_RANGE
+    assert L.oda_recall_score(FAKE, FAKE, FAKE, FAKE, FAKE, 64, 8, 1024, 0.0, FAKE, FAKE, FAKE, 8, None) == SK_E_WORKSPACE
     assert L.oda_gate_scores(None, 1, 0.0, None, FAKE, None) == SK_E_NULL
     assert L.oda_gate_scores(FAKE, 0, 0.0, None, FAKE, None) == SK_E_RANGE
     assert L.da_keep_mask(None, kv(), 1024, FAKE, None) == SK_E_NULL
