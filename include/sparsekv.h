@@ -342,6 +342,28 @@ int da_decode_gathered(const float* q, sk_paged_kv kv, const void* k_new, const 
                        int32_t sel_value, float* out, void* ws, size_t ws_bytes,
                        hipStream_t stream);
 
+/* Per-request views of a batch in one launch ([ODA] "Approach": a step attends the
+ * Full view when recalled, else its local-first view; [DA] section 3: a request may
+ * instead attend the kept blocks of its rewritten block table). Request b attends
+ *   view[b] == SK_MODE_FULL   : [0, n)                       (as oda_decode_full)
+ *   view[b] == SK_MODE_LOCAL  : sinks + window               (as oda_decode_local)
+ *   view[b] == SK_MODE_BLOCKS : its gathered list            (as da_decode_gathered)
+ * and any other value runs nothing for b (out rows untouched, nothing committed).
+ * k_new / v_new, when given, are committed to position n-1 of every running
+ * request, as the single-view calls do. One launch instead of three: outputs
+ * equal those of the three selector calls up to the order of the split merge
+ * (the splits are planned over all running requests together).
+ *  view     : int32 [batch], device memory (oda_gate_scores writes it)
+ *  gathered, gathered_cnt, num_kept : da_gather's output for the SK_MODE_BLOCKS
+ *             requests (read only for them)
+ * Other arguments as oda_decode_local. Host-checked: view and the list arrays
+ * non-NULL, sinks >= 0, window >= 1. */
+int oda_decode_views(const float* q, sk_paged_kv kv, const void* k_new, const void* v_new,
+                     int32_t sinks, int32_t window, float scale, const int32_t* view,
+                     const int32_t* gathered, const int32_t* gathered_cnt,
+                     const int32_t* num_kept, float* out, void* ws, size_t ws_bytes,
+                     hipStream_t stream);
+
 /* Attention over the blocks a declared mode keeps ([DA] sections 1 and 3), with the
  * block-table rewrite done inside the decode kernel instead of through a keep mask and
  * a gathered list: decl and local_tokens as in da_keep_mask; the request attends exactly

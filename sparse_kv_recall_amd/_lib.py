@@ -64,6 +64,8 @@ _SIGNATURES = {
                             c_void_p]),
     "da_decode_gathered": (c_int32, [c_void_p, PagedKVStruct, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                      c_float, c_void_p, c_int32, c_void_p, c_void_p, c_size_t, c_void_p]),
+    "oda_decode_views": (c_int32, [c_void_p, PagedKVStruct, c_void_p, c_void_p, c_int32, c_int32, c_float, c_void_p,
+                                   c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
     "da_decode_blocks": (c_int32, [c_void_p, PagedKVStruct, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                    c_void_p, c_float, c_void_p, c_int32, c_void_p, c_void_p, c_size_t, c_void_p]),
 }

@@ -34,12 +34,18 @@
 namespace sk {
 namespace {
 
-enum { kFull = 0, kLocal = 1, kList = 2, kDecl = 3 };
+enum { kFull = 0, kLocal = 1, kList = 2, kDecl = 3, kViews = 4 };
 constexpr int kThreads = 64 * kWavesPerWG;
 constexpr int kMinTilesPerSplit = 8;                   // small launches: many short splits
 constexpr int kMaxSplits = 256;                     // splits per (request, KV head)
 constexpr int kGridCap = 256;                       // decode workgroups per launch (one per CU)
 constexpr int kMergeBatch = 48;                     // split accumulators loaded together in the merge
+// Per-request views in one launch: work items fill at most this many rounds of the grid
+// (4 x 256 workgroups = the items a workspace holds at the largest query group). Measured
+// on the ragged batch of 32 (tokens/s against one launch per view): 2 rounds -2.5 %, 4
+// rounds +1.8 %, 6 rounds +2.8 % (more items than the workspace holds at group 16), 8
+// rounds +0.2 % (longer split merges).
+constexpr int kViewRounds = 4;
 constexpr float kLog2e = 1.4426950408889634f;
 
 struct DecodeParams {
@@ -70,6 +76,13 @@ struct Tile {
 template <bool HAS_SEL>
 __device__ inline bool request_active(const DecodeParams& P, int b) {
   return !HAS_SEL || P.sel[b] == P.sel_value;
+}
+
+// Per-request views (MODE kViews): the selector value names the request's view, Full,
+// Local or the gathered block list (SK_MODE_*); the view as one of kFull / kLocal /
+// kList, or -1 for any other value (the request does not run).
+__device__ inline int view_of(int sel) {
+  return sel == SK_MODE_FULL ? int(kFull) : sel == SK_MODE_LOCAL ? int(kLocal) : sel == SK_MODE_BLOCKS ? int(kList) : -1;
 }
 
 // Kept blocks of a declared mode ([DA] sections 1 and 3) as at most two ascending,
@@ -120,11 +133,13 @@ __device__ inline Runs declared_runs(const DecodeParams& P, int b, int n) {
   return Runs{s0, e0 - s0, s1, e1 - s1};
 }
 
-// listed: the request's entry of list_num (block-list view only)
+// listed: the request's entry of list_num (block-list view only); view: the request's view
+// under MODE kViews (ignored otherwise)
 template <int MODE>
-__device__ inline int request_tiles(const DecodeParams& P, int b, int n, int listed) {
-  if (MODE == kFull) return (n + kBlock - 1) / kBlock;
-  if (MODE == kLocal) {
+__device__ inline int request_tiles(const DecodeParams& P, int b, int n, int listed, int view = MODE) {
+  const int m = (MODE == kViews) ? view : MODE;
+  if (m == kFull) return (n + kBlock - 1) / kBlock;
+  if (m == kLocal) {
     int s_end = min(P.sinks, n);
     int a = max(s_end, n - P.window);
     int st = (s_end + kBlock - 1) / kBlock;
@@ -140,14 +155,15 @@ __device__ inline int request_tiles(const DecodeParams& P, int b, int n, int lis
 }
 
 template <int MODE>
-__device__ inline Tile tile_at(const DecodeParams& P, int b, int n, int i) {
+__device__ inline Tile tile_at(const DecodeParams& P, int b, int n, int i, int view = MODE) {
   Tile t;
   const int32_t* bt = P.kv.block_tables + int64_t(b) * P.kv.max_blocks;
-  if (MODE == kFull) {
+  const int m = (MODE == kViews) ? view : MODE;
+  if (m == kFull) {
     t.lo = 0;
     t.hi = min(kBlock, n - kBlock * i);
     t.phys = bt[i];
-  } else if (MODE == kLocal) {
+  } else if (m == kLocal) {
     int s_end = min(P.sinks, n);
     int st = (s_end + kBlock - 1) / kBlock;
     int lb;
@@ -454,6 +470,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
   int* s_start = s_tiles + B;
   int* s_len = s_start + B + 1;  // [B] sequence lengths (large batches)
   int* s_misc = s_len + B;  // [0] tile sum, [1] T, [2] active requests, [3] last flag, [4] max tiles
+  int* s_view = s_misc + 8;  // [B] views of the requests (MODE kViews, large batches)
 
   if (tid == 0) {
     s_misc[0] = 0;
@@ -465,14 +482,19 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
   // workgroup leaves before touching the plan.
   // Small batches: lane b loads request b's length, selector and list length once, in one
   // round of loads (lanes past the batch read request 0 and ignore it).
-  int l_len = 0, l_listed = 0;
+  int l_len = 0, l_listed = 0, l_view = MODE;
   bool l_sel = true;
   if (B <= 64) {
     const int bl = (lane < B) ? lane : 0;
     l_len = P.kv.seq_lens[bl];
-    if (MODE == kList) l_listed = P.list_num[bl];
+    if (MODE == kList || MODE == kViews) l_listed = P.list_num[bl];
     if (HAS_SEL) {
-      l_sel = (lane < B) && P.sel[bl] == P.sel_value;
+      if (MODE == kViews) {
+        l_view = view_of(P.sel[bl]);
+        l_sel = (lane < B) && l_view >= 0;
+      } else {
+        l_sel = (lane < B) && P.sel[bl] == P.sel_value;
+      }
       if (__builtin_amdgcn_readfirstlane(__ballot(l_sel) != 0) == 0) return;
     }
   }
@@ -507,7 +529,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
     if (lane < B && l_sel) {
       const int n = l_len;
       const bool valid = n >= 1 && n <= maxb * kBlock;
-      if (valid) tiles = request_tiles<MODE>(P, lane, n, l_listed);
+      if (valid) tiles = request_tiles<MODE>(P, lane, n, l_listed, l_view);
       if (blockIdx.x == 0 && wave == 0 && (!valid || tiles == 0)) bad_request(lane, n, valid);
     }
     const int sum = wave_sum_i(tiles), act = wave_sum_i(tiles > 0), mx = wave_max_i(tiles);
@@ -537,6 +559,25 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
         x = wave_inclusive_scan(splits);
       }
     }
+    if (MODE == kViews && mx * act > 2 * sum) {
+      // Views of different sizes in one launch: the reserve above gives every running
+      // request a slot, so with as many requests as slots each gets one split and the
+      // longest Full views set the launch time. Size the splits instead so that the work
+      // items fill at most kViewRounds rounds of the grid: a workgroup then takes about
+      // that many items of at most T tiles, close to an even share.
+      auto count = [&](int t) { return wave_sum_i((tiles + t - 1) / t); };
+      const int cap = kViewRounds * slots;
+      int t = (sum + cap - 1) / cap;
+      const int t_cap = (mx + kMaxSplits - 1) / kMaxSplits;
+      if (t < t_cap) t = t_cap;
+      if (t < kMinTilesPerSplit) t = kMinTilesPerSplit;
+      for (int k = 0; k < 16 && t < T && count(t) > cap; ++k) t += (t >> 3) + 1;
+      if (t < T && count(t) <= cap) {  // within the items the workspace holds
+        T = t;
+        splits = (tiles + T - 1) / T;
+        x = wave_inclusive_scan(splits);
+      }
+    }
     w_tiles = tiles;
     w_len = (lane < B) ? l_len : 0;
     w_start = (x - splits) * Hkv;
@@ -546,10 +587,12 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
     int my_sum = 0, my_active = 0, my_max = 0;
     for (int b = tid; b < B; b += blockDim.x) {
       int tiles = 0;
-      if (request_active<HAS_SEL>(P, b)) {
+      const int view = (MODE == kViews) ? view_of(P.sel[b]) : MODE;
+      if (MODE == kViews) s_view[b] = view;
+      if (MODE == kViews ? view >= 0 : request_active<HAS_SEL>(P, b)) {
         const int n = P.kv.seq_lens[b];
         const bool valid = n >= 1 && n <= maxb * kBlock;
-        if (valid) tiles = request_tiles<MODE>(P, b, n, MODE == kList ? P.list_num[b] : 0);
+        if (valid) tiles = request_tiles<MODE>(P, b, n, (MODE == kList || MODE == kViews) ? P.list_num[b] : 0, view);
         if (blockIdx.x == 0 && (!valid || tiles == 0)) bad_request(b, n, valid);
       }
       s_tiles[b] = tiles;
@@ -592,13 +635,14 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
 
   for (int item = item_first; item < total_items; item += gridDim.x) {
     // locate the request: the one whose item range holds `item` (it has items)
-    int b, tiles_b, item_base, n;
+    int b, tiles_b, item_base, n, view = MODE;  // view: the request's view under kViews
     if (B <= 64) {
       const int end = w_start + ((w_tiles + T - 1) / T) * Hkv;
       b = __builtin_amdgcn_readfirstlane(__popcll(__ballot(lane < B && end <= item)));
       tiles_b = __builtin_amdgcn_readlane(w_tiles, b);
       n = __builtin_amdgcn_readlane(w_len, b);
       item_base = __builtin_amdgcn_readlane(w_start, b);
+      if (MODE == kViews) view = __builtin_amdgcn_readlane(l_view, b);
     } else {
       int lo_b = 0, hi_b = B - 1;
       while (lo_b < hi_b) {
@@ -609,6 +653,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
       tiles_b = s_tiles[b];
       n = s_len[b];
       item_base = s_start[b];
+      if (MODE == kViews) view = s_view[b];
     }
     const int splits = (tiles_b + T - 1) / T;
     const int local = item - item_base;
@@ -632,7 +677,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
     int commit_tile = -1;
     const int tl = (n - 1) % kBlock;
     if (P.k_new) {
-      if (MODE == kFull || MODE == kLocal) {
+      const int m = (MODE == kViews) ? view : MODE;
+      if (m == kFull || m == kLocal) {
         commit_tile = tiles_b - 1;
       } else if (MODE == kDecl) {
         // the current token's block is attended when it is the last kept block
@@ -669,7 +715,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
     auto load_desc = [&](int c0) {
       const int ti = t_begin + wave + (c0 + lane) * W;
       Tile tt = Tile{0, 0, 0};
-      if (c0 + lane < loop_tiles) tt = tile_at<MODE>(P, b, n, ti);
+      if (c0 + lane < loop_tiles) tt = tile_at<MODE>(P, b, n, ti, view);
       dphys = tt.phys;
       dlohi = tt.lo | (tt.hi << 8);
     };
@@ -797,7 +843,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
     if (own_commit) {
       // the request's last tile: attend with the current token substituted from LDS, then
       // write the token into its slot of the pool
-      Tile tt = tile_at<MODE>(P, b, n, commit_tile);
+      Tile tt = tile_at<MODE>(P, b, n, commit_tile, view);
       load_tile(kpool, vpool, tt.phys, g, Hkv, lane, k0, v0);
       substitute_token(s_new, tl, lane, k0, v0);
       process(k0, v0, tt.lo | (tt.hi << 8));
@@ -977,11 +1023,15 @@ int launch_decode(const float* q, sk_paged_kv kv, const void* k_new, const void*
   grid = (grid + 7) / 8 * 8;
   const int acc_region = std::max(kWavesPerWG * G * kHeadDim, 2 * kMaxSplits * G + 4 * kThreads);
   size_t lds = size_t(kThreads) * 16 + 128 * 4 + size_t(acc_region) * 4 + size_t(kWavesPerWG) * 16 * 4 * 2 +
-               size_t(3 * kv.batch + 1 + 8) * 4;
-  if (sel)
+               size_t(3 * kv.batch + 1 + 8 + (MODE == kViews ? kv.batch : 0)) * 4;
+  if constexpr (MODE == kViews) {  // the views are the selector: always present
     hipLaunchKernelGGL((decode_kernel<MODE, true>), dim3(unsigned(grid)), dim3(kThreads), lds, stream, P);
-  else
-    hipLaunchKernelGGL((decode_kernel<MODE, false>), dim3(unsigned(grid)), dim3(kThreads), lds, stream, P);
+  } else {
+    if (sel)
+      hipLaunchKernelGGL((decode_kernel<MODE, true>), dim3(unsigned(grid)), dim3(kThreads), lds, stream, P);
+    else
+      hipLaunchKernelGGL((decode_kernel<MODE, false>), dim3(unsigned(grid)), dim3(kThreads), lds, stream, P);
+  }
   return launch_status(hipGetLastError());
 }
 
@@ -1049,6 +1099,16 @@ int da_decode_gathered(const float* q, sk_paged_kv kv, const void* k_new, const 
   if (!gathered || !gathered_cnt || !num_kept) return SK_E_NULL;
   return launch_decode<kList>(q, kv, k_new, v_new, 0, 1, scale, sel, sel_value, gathered, gathered_cnt, num_kept,
                               out, ws, ws_bytes, stream);
+}
+
+int oda_decode_views(const float* q, sk_paged_kv kv, const void* k_new, const void* v_new, int32_t sinks,
+                     int32_t window, float scale, const int32_t* view, const int32_t* gathered,
+                     const int32_t* gathered_cnt, const int32_t* num_kept, float* out, void* ws, size_t ws_bytes,
+                     hipStream_t stream) {
+  if (!view || !gathered || !gathered_cnt || !num_kept) return SK_E_NULL;
+  if (sinks < 0 || window < 1) return SK_E_RANGE;
+  return launch_decode<kViews>(q, kv, k_new, v_new, sinks, window, scale, view, 0, gathered, gathered_cnt, num_kept,
+                               out, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

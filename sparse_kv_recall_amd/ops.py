@@ -284,6 +284,23 @@ def da_decode_gathered(q, kv, gathered, gathered_cnt, num_kept, k_new=None, v_ne
     return out
 
 
+def oda_decode_views(q, kv, view, gathered, gathered_cnt, num_kept, k_new=None, v_new=None, sinks=4, window=2048,
+                     scale=None, out=None, ws=None):
+    """Per-request views in one launch: request b attends Full, Local or its gathered
+    block list as view[b] is MODE_FULL, MODE_LOCAL or MODE_BLOCKS (any other value: b
+    does not run); the lists are da_gather's output for the MODE_BLOCKS requests."""
+    _check(view, torch.int32, "view", kv.batch)
+    out, ws = _decode_common(q, kv, k_new, v_new, view, out, ws)
+    _check(gathered, torch.int32, "gathered", kv.batch * kv.max_blocks)
+    _check(gathered_cnt, torch.int32, "gathered_cnt", kv.batch * kv.max_blocks)
+    _check(num_kept, torch.int32, "num_kept", kv.batch)
+    scale = 1.0 / math.sqrt(HEAD_DIM) if scale is None else float(scale)
+    _lib.call("oda_decode_views", q.data_ptr(), kv.abi(), _ptr(k_new), _ptr(v_new), int(sinks), int(window), scale,
+              view.data_ptr(), gathered.data_ptr(), gathered_cnt.data_ptr(), num_kept.data_ptr(), out.data_ptr(),
+              ws.data_ptr(), ws.numel(), _stream(q.device))
+    return out
+
+
 def da_decode_declared(q, kv, decl, local_tokens=1024, k_new=None, v_new=None, scale=None, sel=None,
                        sel_value=MODE_BLOCKS, out=None, ws=None):
     """Attention over the blocks a declared mode keeps (decl int32 [B][4] as for

@@ -75,9 +75,13 @@ class ODAStack:
 
 
 class RaggedBatch:
-    """One attention layer over a ragged batch with per-request views."""
+    """One attention layer over a ragged batch with per-request views. one_launch: the
+    three views in one decode launch (oda_decode_views, after da_gather for the block
+    requests); otherwise one selector launch per view."""
 
-    def __init__(self, cache, fallback, keep_mask, sinks=4, window=2048, scale=None, device="cuda"):
+    def __init__(self, cache, fallback, keep_mask, sinks=4, window=2048, scale=None, device="cuda",
+                 one_launch=True):
+        self.one_launch = one_launch
         self.cache = cache
         self.fallback = fallback
         self.keep_mask = keep_mask
@@ -94,6 +98,12 @@ class RaggedBatch:
     def step(self, q, k, v, scores, theta=0.0):
         """q: [B][Hq][128] fp32; k, v: [B][Hkv][128] bf16; scores: [B] fp32."""
         ops.oda_gate_scores(scores, theta, fallback=self.fallback, out=self.mode)
+        if self.one_launch:
+            ops.da_gather(self.cache, self.keep_mask, gathered=self.gathered, gathered_cnt=self.gathered_cnt,
+                          num_kept=self.num_kept, sel=self.mode, sel_value=ops.MODE_BLOCKS, ws=self.ws)
+            ops.oda_decode_views(q, self.cache, self.mode, self.gathered, self.gathered_cnt, self.num_kept, k, v,
+                                 self.sinks, self.window, self.scale, out=self.out, ws=self.ws)
+            return
         ops.oda_decode_full(q, self.cache, k, v, self.scale, sel=self.mode, sel_value=ops.MODE_FULL,
                             out=self.out, ws=self.ws)
         ops.oda_decode_local(q, self.cache, k, v, self.sinks, self.window, self.scale, sel=self.mode,

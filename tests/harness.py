@@ -297,7 +297,7 @@ class RaggedRun:
     """Ragged batch: per step each request takes Full (score > theta) or its fallback
     view (Local, or its fixed keep-list); host mirrors for ``check_requests``."""
 
-    def __init__(self, wl, check_requests, steps=None, use_graph=True):
+    def __init__(self, wl, check_requests, steps=None, use_graph=True, one_launch=True):
         self.wl = wl
         self.steps = wl.steps if steps is None else steps
         self.check = list(check_requests)
@@ -309,7 +309,7 @@ class RaggedRun:
             _fill_history(self.cache, wl, r, int(wl.H0[r]), request=r)
         self.rb = RaggedBatch(self.cache, torch.as_tensor(wl.fallback, device="cuda"),
                               torch.as_tensor(wl.keep_mask.view(np.int32), device="cuda"),
-                              sinks=wl.sinks, window=wl.window)
+                              sinks=wl.sinks, window=wl.window, one_launch=one_launch)
         self.feeder = sdev.Feeder(wl, seq, with_scores=True)
         self.mirror = {r: _mirror(wl, r, int(wl.H0[r]), self.steps) for r in self.check}
         self.graph = capture_graph(self._step) if use_graph else None

@@ -53,6 +53,14 @@ def test_decode_argument_validation():
     assert L.oda_decode_local(FAKE, kv(), None, None, 4, 0, 0.1, None, 0, FAKE, FAKE, 1 << 30, None) == SK_E_RANGE
     # k_new without v_new
     assert L.oda_decode_local(FAKE, kv(), FAKE, None, 4, 2048, 0.1, None, 0, FAKE, FAKE, 1 << 30, None) == SK_E_NULL
+    # per-request views: the view array and the gathered lists are required
+    views = lambda view=FAKE, gat=FAKE, sinks=4, window=2048, k=kv(): L.oda_decode_views(
+        FAKE, k, None, None, sinks, window, 0.1, view, gat, FAKE, FAKE, FAKE, FAKE, 1 << 30, None)
+    assert views(view=None) == SK_E_NULL
+    assert views(gat=None) == SK_E_NULL
+    assert views(sinks=-1) == SK_E_RANGE
+    assert views(window=0) == SK_E_RANGE
+    assert views(k=kv(num_q_heads=12)) == SK_E_HEADS
 
 
 def test_other_entry_points_validation():

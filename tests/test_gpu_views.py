@@ -1,0 +1,85 @@
+"""GPU parity of oda_decode_views, the per-request views of a batch in one launch: each
+running request against the fp64 oracle for its view (Full, Local, or its gathered block
+list), with fused commits; requests whose view value names no view keep their output rows
+and their slot n-1. Batches of 12 (per-wave planning) and 100 (workgroup planning)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import attention, keysets
+from synth import rng
+from tests.helpers import (SCALE, HostCache, bf16_tensor_to_bits, bits_to_bf16_tensor, check_close, rand_bits,
+                           rand_f32, requires_gpu)
+
+pytestmark = [pytest.mark.gpu, requires_gpu]
+
+
+def _mask_words(kept_per_req, max_blocks):
+    words = np.zeros((len(kept_per_req), (max_blocks + 31) // 32), np.uint32)
+    for b, kept in enumerate(kept_per_req):
+        for blk in kept:
+            words[b, blk // 32] |= np.uint32(1 << (blk % 32))
+    return words
+
+
+@pytest.mark.parametrize("B,sinks,window", [(12, 4, 2048), (100, 3, 40)])
+def test_views_one_launch(B, sinks, window):
+    from sparse_kv_recall_amd import ops
+    Hq, Hkv = 16, 4
+    g = np.random.default_rng(90 + B)
+    ns = [int(x) for x in g.integers(1, 6000, size=B)]
+    ns[:5] = [1, 16, 17, 2052, 5999]
+    hc = HostCache(Hq, Hkv, ns, seed=91)
+    # views: 0 Local, 1 Full, 2 blocks, 5 none (the request does not run)
+    view = g.choice([0, 1, 2, 5], size=B, p=[0.3, 0.3, 0.3, 0.1]).astype(np.int32)
+    view[:4] = [0, 1, 2, 5]
+    kept = []
+    for n in ns:
+        nb = (n + 15) // 16
+        kept.append(sorted(set(g.choice(nb, size=max(1, nb // 4), replace=False).tolist()) | {nb - 1}))
+    mask = torch.as_tensor(_mask_words(kept, hc.max_blocks).view(np.int32), device="cuda")
+    q = rand_f32(rng.mix_key(992, B), (B, Hq, 128), 1.0)
+    kn = rand_bits(rng.mix_key(993, B, 1), B, Hkv)
+    vn = rand_bits(rng.mix_key(993, B, 2), B, Hkv)
+    vt = torch.as_tensor(view, device="cuda")
+    gat = torch.zeros((B, hc.max_blocks), dtype=torch.int32, device="cuda")
+    cnt = torch.zeros_like(gat)
+    num = torch.zeros(B, dtype=torch.int32, device="cuda")
+    ws = ops.workspace(B, Hq)
+    ops.da_gather(hc.kv, mask, gathered=gat, gathered_cnt=cnt, num_kept=num, sel=vt, sel_value=ops.MODE_BLOCKS,
+                  ws=ws)
+    out = torch.full((B, Hq, 128), 7.0, device="cuda")
+    ops.oda_decode_views(torch.as_tensor(q, device="cuda"), hc.kv, vt, gat, cnt, num, bits_to_bf16_tensor(kn),
+                         bits_to_bf16_tensor(vn), sinks=sinks, window=window, out=out, ws=ws)
+    got = out.cpu().numpy()
+    assert ops.workspace_error(ws) == 0
+    for b, n in enumerate(ns):
+        kr, vr = ops.kv_read(hc.kv, b, n - 1, 1)
+        if view[b] not in (0, 1, 2):
+            assert (got[b] == 7.0).all(), b
+            assert np.array_equal(bf16_tensor_to_bits(kr)[0], hc.k[b][n - 1]), b
+            assert np.array_equal(bf16_tensor_to_bits(vr)[0], hc.v[b][n - 1]), b
+            continue
+        k, v = hc.k[b].copy(), hc.v[b].copy()
+        oracle.oda.commit(k, v, n, kn[b], vn[b])
+        keys = (keysets.local_keys(n, sinks, window), keysets.full_keys(n), keysets.block_keys(n, kept[b]))[view[b]]
+        ref = attention.attend(q[b], k, v, keys, SCALE)
+        check_close(got[b], ref, abs_tol=1e-5, row_rel_tol=1e-4, what="b=%d n=%d view=%d" % (b, n, view[b]))
+        assert np.array_equal(bf16_tensor_to_bits(kr)[0], kn[b]) and np.array_equal(bf16_tensor_to_bits(vr)[0], vn[b])
+
+
+def test_views_none_running():
+    # no request names a view: every workgroup leaves at once, nothing is written
+    from sparse_kv_recall_amd import ops
+    Hq, Hkv = 8, 2
+    ns = [300, 5000, 17]
+    hc = HostCache(Hq, Hkv, ns, seed=95)
+    q = torch.as_tensor(rand_f32(rng.mix_key(995), (3, Hq, 128), 1.0), device="cuda")
+    vt = torch.full((3,), 9, dtype=torch.int32, device="cuda")
+    gat = torch.zeros((3, hc.max_blocks), dtype=torch.int32, device="cuda")
+    out = torch.full((3, Hq, 128), 7.0, device="cuda")
+    ops.oda_decode_views(q, hc.kv, vt, gat, torch.zeros_like(gat), torch.zeros(3, dtype=torch.int32, device="cuda"),
+                         out=out)
+    assert (out.cpu().numpy() == 7.0).all()
