@@ -26,11 +26,12 @@ def _mask_words(kept_per_req, max_blocks):
     return words
 
 
-@pytest.mark.parametrize("B,sinks,window", [(12, 4, 2048), (64, 4, 2048), (65, 4, 300), (100, 3, 40)])
-def test_views_one_launch(B, sinks, window):
+@pytest.mark.parametrize("B,sinks,window,Hq,Hkv", [(12, 4, 2048, 16, 4), (64, 4, 2048, 16, 4), (65, 4, 300, 16, 4),
+                                                   (100, 3, 40, 16, 4), (12, 4, 2048, 32, 2), (70, 4, 500, 32, 2)])
+def test_views_one_launch(B, sinks, window, Hq, Hkv):
+    # query groups of 4 and of 16 (the merge then works on four output elements per thread)
     from sparse_kv_recall_amd import ops
-    Hq, Hkv = 16, 4
-    g = np.random.default_rng(90 + B)
+    g = np.random.default_rng(90 + B + Hkv)
     ns = [int(x) for x in g.integers(1, 6000, size=B)]
     ns[:5] = [1, 16, 17, 2052, 5999]
     hc = HostCache(Hq, Hkv, ns, seed=91)
