@@ -10,7 +10,8 @@ distributions are kept):
    recall head is a 6144 -> 512 -> 1 MLP with N(0, 0.02^2) weights, zero
    biases and N(0, 1) hidden states; theta = 0.
 3. ``oda_stack128k``  36 layers, 32 / 8 heads, history 131072 growing by 1024
-   steps, Full on exactly 128 seeded steps (12.5 %), block table = identity.
+   steps, Full on exactly 128 seeded steps (12.5 %): one at a seeded offset in
+   every aligned run of 8 steps; block table = identity.
 4. ``da_32k``  1 layer, 32 / 8 heads, context 32768 (1984 prompt blocks + 64
    blocks of earlier model output) growing by 512 steps; per step a seeded
    declared mode (global / focus on 128 blocks / local 1024 positions); the
@@ -182,10 +183,15 @@ def oda_stack16k(steps=256, H0=16384, layers=28):
                     block_tables=np.arange(mb, dtype=np.int32)[None, :], num_phys_blocks=mb)
 
 
-def oda_stack128k(steps=1024, H0=131072, layers=36, recalls=128):
+def oda_stack128k(steps=1024, H0=131072, layers=36, period=8):
+    """Full on exactly one seeded step of every aligned run of ``period`` steps (steps
+    8k .. 8k+7 at the default period): 128 of 1024 steps, and the 12.5 % rate holds in
+    every window that starts at step 0 and spans whole runs."""
     wid = 3
     g = np_rng(wid, C_SCHED)
-    chosen = g.choice(steps, size=recalls, replace=False)
+    runs = -(-steps // period)
+    chosen = np.arange(runs) * period + g.integers(0, period, size=runs)
+    chosen = chosen[chosen < steps]
     sched = -np.ones(steps, np.float32)
     sched[chosen] = 1.0
     mb = _blocks_for(H0 + steps)

@@ -59,6 +59,10 @@ def test_workload_invariants():
     assert w1.steps == 64 and w1.Hq == 8 and w1.Hkv == 2
     w3 = workloads.oda_stack128k()
     assert int((w3.sched_scores > 0).sum()) == 128
+    # one recall in every aligned run of 8 steps, at offsets that are not all the same
+    runs = (w3.sched_scores[:, 0] > 0).reshape(128, 8)
+    assert (runs.sum(axis=1) == 1).all()
+    assert len(set(np.argmax(runs, axis=1).tolist())) > 4
     assert w3.n_at(0)[0] == 131073 and w3.n_at(1023)[0] == 132096
     w4 = workloads.da_32k()
     assert sorted(w4.block_tables[0].tolist()) == list(range(w4.num_phys_blocks))
