@@ -181,6 +181,23 @@ int oda_decode_full(const float* q, sk_paged_kv kv, const void* k_new, const voi
                     float scale, const int32_t* sel, int32_t sel_value,
                     float* out, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* Allocation-free form of oda_decode_full, for callers that cannot allocate or
+ * pass a workspace (code under graph capture that may not call hipMalloc, tight
+ * serving loops, harnesses that forbid allocation). Same computation, kernels and
+ * results as oda_decode_full; the split tickets and partials live in a device array
+ * inside the library (16 MiB per GPU, held until the process ends), so no `ws`.
+ *  dev_err : NULL, or a caller-owned device int32 that receives the SK_DEVERR_*
+ *            bits (OR-ed in; the caller clears it)
+ * Limit: sk_workspace_bytes(batch, num_q_heads) <= 16 MiB (batch * num_q_heads up to
+ * about 15700), else SK_E_WORKSPACE and nothing is enqueued. The first call on a GPU
+ * looks up the array's address and enqueues its clearing on `stream`; it calls no
+ * hipMalloc / hipFree. Every call on one GPU shares that GPU's array: calls that
+ * overlap on one GPU (other streams, other threads) race; calls issued in order on
+ * one stream do not. Other arguments and errors as oda_decode_full. */
+int oda_decode_full_noalloc(const float* q, sk_paged_kv kv, const void* k_new, const void* v_new,
+                            float scale, const int32_t* sel, int32_t sel_value,
+                            float* out, int32_t* dev_err, hipStream_t stream);
+
 /* Recall head and gate ([ODA] "Approach" and "Developer perspective"), FP32:
  *   a = W1 x_b + b1;  u = GELU(a) (exact erf form);  q_b = <w2, u> + b2;
  *   gate_b = (q_b > theta) ? 1 : 0          (strict comparison)

@@ -28,6 +28,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "sk_internal.h"
 
@@ -982,16 +983,23 @@ __global__ __launch_bounds__(256) void gather_kernel(sk_paged_kv kv, const uint3
     num_kept[b] = s_prefix + s_wave[0] + s_wave[1] + s_wave[2] + s_wave[3];
 }
 
-template <int MODE>
-int launch_decode(const float* q, sk_paged_kv kv, const void* k_new, const void* v_new, int sinks, int window,
-                  float scale, const int32_t* sel, int sel_value, const int32_t* lp, const int32_t* lc,
-                  const int32_t* ln, float* out, void* ws, size_t ws_bytes, hipStream_t stream,
-                  const int32_t* decl = nullptr, int local_tokens = 0) {
+// Argument checks of every decode launch; the workspace is checked by the caller.
+int check_decode(const float* q, const sk_paged_kv& kv, const void* k_new, const void* v_new, const float* out) {
   int st = check_kv(kv);
   if (st) return st;
-  if (!q || !out || !ws) return SK_E_NULL;
+  if (!q || !out) return SK_E_NULL;
   if ((k_new == nullptr) != (v_new == nullptr)) return SK_E_NULL;
-  if (ws_bytes < sk_workspace_bytes(kv.batch, kv.num_q_heads)) return SK_E_WORKSPACE;
+  return SK_OK;
+}
+
+// Enqueues one decode launch. scratch: a cleared workspace layout (header, tickets at
+// kWsHeaderBytes, split partials at kPartialsOffset) of at least
+// sk_workspace_bytes(batch, Hq) bytes; err: the device error word (may be null).
+template <int MODE>
+int enqueue_decode(const float* q, sk_paged_kv kv, const void* k_new, const void* v_new, int sinks, int window,
+                   float scale, const int32_t* sel, int sel_value, const int32_t* lp, const int32_t* lc,
+                   const int32_t* ln, float* out, uint8_t* scratch, int32_t* err, hipStream_t stream,
+                   const int32_t* decl, int local_tokens) {
   DecodeParams P;
   P.q = q;
   P.kv = kv;
@@ -1003,9 +1011,9 @@ int launch_decode(const float* q, sk_paged_kv kv, const void* k_new, const void*
   P.list_cnt = lc;
   P.list_num = ln;
   P.out = out;
-  P.err = reinterpret_cast<int32_t*>(ws);
-  P.tickets = reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(ws) + kWsHeaderBytes);
-  P.partials = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(ws) + kPartialsOffset);
+  P.err = err;
+  P.tickets = reinterpret_cast<uint32_t*>(scratch + kWsHeaderBytes);
+  P.partials = reinterpret_cast<float*>(scratch + kPartialsOffset);
   P.sinks = sinks;
   P.window = window;
   P.qscale = scale * kLog2e;
@@ -1035,6 +1043,60 @@ int launch_decode(const float* q, sk_paged_kv kv, const void* k_new, const void*
   return launch_status(hipGetLastError());
 }
 
+template <int MODE>
+int launch_decode(const float* q, sk_paged_kv kv, const void* k_new, const void* v_new, int sinks, int window,
+                  float scale, const int32_t* sel, int sel_value, const int32_t* lp, const int32_t* lc,
+                  const int32_t* ln, float* out, void* ws, size_t ws_bytes, hipStream_t stream,
+                  const int32_t* decl = nullptr, int local_tokens = 0) {
+  int st = check_decode(q, kv, k_new, v_new, out);
+  if (st) return st;
+  if (!ws) return SK_E_NULL;
+  if (ws_bytes < sk_workspace_bytes(kv.batch, kv.num_q_heads)) return SK_E_WORKSPACE;
+  uint8_t* base = reinterpret_cast<uint8_t*>(ws);
+  return enqueue_decode<MODE>(q, kv, k_new, v_new, sinks, window, scale, sel, sel_value, lp, lc, ln, out, base,
+                              reinterpret_cast<int32_t*>(base), stream, decl, local_tokens);
+}
+
+// ---- allocation-free Full view: the workspace lives in a file-scope device array
+// (one copy per GPU, kept until the process ends). In host code `scratch` only names
+// the symbol; its device address on the current GPU comes from hipGetSymbolAddress.
+constexpr size_t kScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+__global__ void scratch_clear_kernel(uint32_t* p, uint32_t words) {
+  const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < words) p[i] = 0u;
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+uint8_t* g_scratch[kMaxDevices];  // device address of `scratch` per GPU (null until set up)
+
+// The scratch array's address on the current GPU; on the first call for that GPU, looks
+// the address up and enqueues the clearing of its header and tickets on `stream`
+// (a fill kernel, not a memset: the call may be captured in a graph).
+int scratch_on_device(hipStream_t stream, uint8_t** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return launch_status(e);
+  if (dev < 0 || dev >= kMaxDevices) return SK_E_RANGE;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return launch_status(e);
+    if (!ptr) return launch_status(hipErrorInvalidSymbol);
+    const uint32_t words = uint32_t(kPartialsOffset / 4);
+    hipLaunchKernelGGL(scratch_clear_kernel, dim3((words + 255) / 256), dim3(256), 0, stream,
+                       reinterpret_cast<uint32_t*>(ptr), words);
+    e = hipGetLastError();
+    if (e != hipSuccess) return launch_status(e);
+    g_scratch[dev] = reinterpret_cast<uint8_t*>(ptr);
+  }
+  *out = g_scratch[dev];
+  return SK_OK;
+}
+
 }  // namespace
 }  // namespace sk
 
@@ -1055,6 +1117,19 @@ int oda_decode_full(const float* q, sk_paged_kv kv, const void* k_new, const voi
                     hipStream_t stream) {
   return launch_decode<kFull>(q, kv, k_new, v_new, 0, 1, scale, sel, sel_value, nullptr, nullptr, nullptr, out,
                               ws, ws_bytes, stream);
+}
+
+int oda_decode_full_noalloc(const float* q, sk_paged_kv kv, const void* k_new, const void* v_new, float scale,
+                            const int32_t* sel, int32_t sel_value, float* out, int32_t* dev_err,
+                            hipStream_t stream) {
+  int st = check_decode(q, kv, k_new, v_new, out);
+  if (st) return st;
+  if (sk_workspace_bytes(kv.batch, kv.num_q_heads) > kScratchBytes) return SK_E_WORKSPACE;
+  uint8_t* base = nullptr;
+  st = scratch_on_device(stream, &base);
+  if (st) return st;
+  return enqueue_decode<kFull>(q, kv, k_new, v_new, 0, 1, scale, sel, sel_value, nullptr, nullptr, nullptr, out, base,
+                               dev_err, stream, nullptr, 0);
 }
 
 int da_decode_blocks(const float* q, sk_paged_kv kv, const void* k_new, const void* v_new,

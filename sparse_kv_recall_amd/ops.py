@@ -152,6 +152,22 @@ def oda_decode_full(q, kv, k_new=None, v_new=None, scale=None, sel=None, sel_val
     return out
 
 
+def oda_decode_full_noalloc(q, kv, out, k_new=None, v_new=None, scale=None, sel=None, sel_value=1, dev_err=None):
+    """oda_decode_full without a workspace (the library's own device array serves as one);
+    `out` is required, so nothing is allocated on this path."""
+    _check(q, torch.float32, "q", kv.batch * kv.num_q_heads * HEAD_DIM)
+    n = kv.batch * kv.num_kv_heads * HEAD_DIM
+    _check(k_new, torch.bfloat16, "k_new", n)
+    _check(v_new, torch.bfloat16, "v_new", n)
+    _check(sel, torch.int32, "sel", kv.batch)
+    _check(out, torch.float32, "out", kv.batch * kv.num_q_heads * HEAD_DIM)
+    _check(dev_err, torch.int32, "dev_err", 1)
+    scale = 1.0 / math.sqrt(HEAD_DIM) if scale is None else float(scale)
+    _lib.call("oda_decode_full_noalloc", q.data_ptr(), kv.abi(), _ptr(k_new), _ptr(v_new), scale, _ptr(sel),
+              int(sel_value), out.data_ptr(), _ptr(dev_err), _stream(q.device))
+    return out
+
+
 def oda_recall_score(x, W1, b1, w2, b2, theta=0.0, q_out=None, gate_out=None, ws=None):
     batch, in_dim = x.shape
     hidden = W1.shape[0]

@@ -63,6 +63,23 @@ def test_decode_argument_validation():
     assert views(k=kv(num_q_heads=12)) == SK_E_HEADS
 
 
+def test_decode_full_noalloc_validation():
+    # the allocation-free Full view checks its arguments, and the size its device array
+    # holds (16 MiB: batch * num_q_heads up to about 15700), before any HIP call
+    L = lib()
+    call = lambda k, q=FAKE, out=FAKE, kn=None, vn=None: L.oda_decode_full_noalloc(
+        q, k, kn, vn, 0.1, None, 1, out, None, None)
+    assert call(kv(k_pool=None)) == SK_E_NULL
+    assert call(kv(), q=None) == SK_E_NULL
+    assert call(kv(), out=None) == SK_E_NULL
+    assert call(kv(), kn=FAKE) == SK_E_NULL
+    assert call(kv(head_dim=64)) == SK_E_SHAPE
+    assert call(kv(num_q_heads=12)) == SK_E_HEADS
+    assert call(kv(batch=1024, num_q_heads=32)) == SK_E_WORKSPACE
+    assert call(kv(batch=512, num_q_heads=32)) == SK_E_WORKSPACE
+    assert L.sk_workspace_bytes(480, 32) <= 16 << 20 < L.sk_workspace_bytes(512, 32)
+
+
 def test_other_entry_points_validation():
     L = lib()
     assert L.oda_recall_score(None, FAKE, FAKE, FAKE, FAKE, 1, 8, 4, 0.0, FAKE, FAKE, FAKE, 1 << 20, None) == SK_E_NULL
