@@ -39,6 +39,7 @@ class Report:
         self.decisions = 0
         self.decisions_in_band = 0
         self.recalls = 0
+        self.commit_layers = 0
 
     def add(self, got, ref, what):
         a, r = check_close(got, ref, what=what)
@@ -105,9 +106,14 @@ class OdaStackRun:
         p = self.rpass
         s.full_pass(f.q[:, p], f.k[:, p], f.v[:, p], gated=True)
 
-    def run(self, full_check_steps=None, check_feed_steps=(0,)):
+    def run(self, full_check_steps=None, check_feed_steps=(0,), commit_all_layers=False):
+        """full_check_steps: recall steps whose Full outputs are checked (None: all);
+        commit_all_layers: also check the committed slots of every layer (not only the
+        mirrored ones) against the selected pass's candidates regenerated from the
+        seeded streams."""
         wl, rep = self.wl, Report()
         H0 = int(wl.H0[0])
+        gates = []
         for t in range(self.steps):
             if self.graph is not None:
                 self.graph.replay()
@@ -139,6 +145,7 @@ class OdaStackRun:
                 assert gate == bool(gpu_gate), t
             rep.decisions += 1
             rep.recalls += int(gate)
+            gates.append(bool(gate))
             out_l = self.stack.out.cpu().numpy() if self.check_layers else None
             out_f = self.stack.out_full.cpu().numpy() if (gate and self.check_layers) else None
             for l in self.check_layers:
@@ -165,6 +172,14 @@ class OdaStackRun:
             k, v = ops.kv_read(self.stack.caches[l], 0, H0, self.steps)
             assert np.array_equal(bf16_tensor_to_bits(k), hk[H0:H0 + self.steps]), l
             assert np.array_equal(bf16_tensor_to_bits(v), hv[H0:H0 + self.steps]), l
+        if commit_all_layers:
+            for l in range(wl.layers):
+                k, v = ops.kv_read(self.stack.caches[l], 0, H0, self.steps)
+                kb, vb = bf16_tensor_to_bits(k), bf16_tensor_to_bits(v)
+                for t in range(self.steps):
+                    ke, ve = wl.cand_kv(t, l, self.rpass if gates[t] else 0, 0)
+                    assert np.array_equal(kb[t], ke) and np.array_equal(vb[t], ve), (l, t, gates[t])
+            rep.commit_layers = wl.layers
         return rep
 
 

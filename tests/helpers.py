@@ -60,6 +60,68 @@ def check_close(got, ref, abs_tol=ABS_TOL, row_rel_tol=ROW_REL_TOL, what=""):
     return max_abs, row_rel
 
 
+# ---- kernel error model (for the tight checks) --------------------------------
+# The decode kernels take q' = q * scale * log2(e) in fp32 and split it into bf16
+# high + low parts; K and V are exact bf16; the logits (base 2) accumulate in fp32 on
+# the matrix cores; the softmax weights p enter the PV product as bf16 high + low
+# parts too, while their sum l stays fp32. Two round-to-nearest roundings to 8
+# significant bits leave a residual of at most 2^-16 of the value, so:
+#   logit error     |dt_j| <= (2^-16 + 2^-20) * A_j,  A_j = sum_d |q'_d| |k_jd|
+#                   (2^-20 covers the fp32 accumulation of the 8 chained products)
+#   weight error    eps_j  <= ln 2 * |dt_j| + 2^-22   (exp2 of the hardware)
+#   normalised      |do_d| <= 2 E / (1 - E) * sum_j p_j |v_jd - o_d|,  E = max_j eps_j
+#   PV split        |do_d| <= 2^-16 * sum_j p_j |v_jd|
+# plus the fp32 sums over tiles, waves and splits, taken as a random walk of unit
+# roundoffs, 2^-22 * sqrt(tiles + 1) * max|v|, and one rounding of the output. The
+# bound is per (request, head) row and is computed from the inputs themselves.
+LOG2E = 1.4426950408889634
+
+
+def hilo_bound(q, k_bits, v_bits, keys, scale):
+    """Per-row bound [Hq] of |GPU - fp64| for attention over `keys` (see above)."""
+    from oracle.bf16 import bf16_bits_to_f64
+    q = np.asarray(q, np.float64)
+    keys = np.asarray(keys, np.int64)
+    Hq = q.shape[0]
+    Hkv = k_bits.shape[1]
+    G = Hq // Hkv
+    tiles = -(-int(keys.size) // 16)
+    out = np.zeros(Hq)
+    for g in range(Hkv):
+        K = bf16_bits_to_f64(k_bits[keys, g])  # [nk][D]
+        V = bf16_bits_to_f64(v_bits[keys, g])
+        vmax = float(np.abs(V).max())
+        for i in range(G):
+            h = g * G + i
+            qp = q[h] * scale * LOG2E
+            A = np.abs(K) @ np.abs(qp)
+            E = float(math.log(2.0) * (2.0 ** -16 + 2.0 ** -20) * A.max() + 2.0 ** -22)
+            z = scale * (K @ q[h])
+            w = np.exp(z - z.max())
+            p = w / w.sum()
+            o = p @ V
+            s1 = p @ np.abs(V - o)
+            s2 = p @ np.abs(V)
+            row = 2 * E / (1 - E) * s1 + 2.0 ** -16 * s2
+            out[h] = float(row.max()) + 2.0 ** -22 * math.sqrt(tiles + 1) * vmax + 2.0 ** -24 * float(np.abs(o).max())
+    return out
+
+
+def check_tight(got, ref, q, k_bits, v_bits, keys, scale=SCALE, what=""):
+    """Every (head) row of `got` [Hq][D] within the error model's bound of the fp64
+    reference `ref`; also the tolerance reading of the scope (check_close). Returns the
+    largest observed |error| / bound over the rows."""
+    check_close(got, ref, what=what)
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    bound = hilo_bound(q, k_bits, v_bits, keys, scale)
+    err = np.abs(got - ref).max(axis=1)
+    bad = np.flatnonzero(err > bound)
+    assert bad.size == 0, "rows %s: error %s above the hi+lo bound %s %s" % (
+        bad[:4].tolist(), err[bad[:4]].tolist(), bound[bad[:4]].tolist(), what)
+    return float((err / bound).max())
+
+
 class HostCache:
     """Logical per-request K/V (bf16 bits) mirrored into a GPU paged cache."""
 

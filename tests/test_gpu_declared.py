@@ -12,8 +12,8 @@ import torch
 import oracle
 from oracle import attention, gather, keysets
 from synth import rng
-from tests.helpers import (SCALE, HostCache, bf16_tensor_to_bits, bits_to_bf16_tensor, check_close, rand_bits,
-                           rand_f32, requires_gpu)
+from tests.helpers import (SCALE, HostCache, bf16_tensor_to_bits, bits_to_bf16_tensor, check_close, check_tight,
+                           rand_bits, rand_f32, requires_gpu)
 
 pytestmark = [pytest.mark.gpu, requires_gpu]
 
@@ -87,7 +87,8 @@ def test_declared_matches_oracle_and_list_path(local_tokens, commit):
             assert not got[b].any(), b  # empty key set: zero row
             continue
         ref = attention.attend(q[b], k, v, keysets.block_keys(n, kept), SCALE)
-        check_close(got[b], ref, abs_tol=1e-5, row_rel_tol=1e-4, what="declared n=%d decl=%s" % (n, decl[b]))
+        check_tight(got[b], ref, q[b], k, v, keysets.block_keys(n, kept), SCALE,
+                    what="declared n=%d decl=%s" % (n, decl[b]))
 
 
 def test_declared_with_selector_skips_requests():
@@ -107,7 +108,7 @@ def test_declared_with_selector_skips_requests():
         kept = gather.da_mode_blocks(int(decl[b, 0]), ns[b], int(decl[b, 1]), int(decl[b, 2]), int(decl[b, 3]),
                                      local_tokens=1024)
         ref = attention.attend(q[b], hc.k[b], hc.v[b], keysets.block_keys(ns[b], kept), SCALE)
-        check_close(got[b], ref, abs_tol=1e-5, row_rel_tol=1e-4)
+        check_tight(got[b], ref, q[b], hc.k[b], hc.v[b], keysets.block_keys(ns[b], kept), SCALE)
 
 
 def test_declared_large_batch_matches_list_path():

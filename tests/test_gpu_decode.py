@@ -11,8 +11,8 @@ import torch
 import oracle
 from oracle import attention, gather, keysets
 from synth import rng
-from tests.helpers import (SCALE, HostCache, bf16_tensor_to_bits, bits_to_bf16_tensor, check_close, rand_bits,
-                           rand_f32, requires_gpu)
+from tests.helpers import (SCALE, HostCache, bf16_tensor_to_bits, bits_to_bf16_tensor, check_close, check_tight,
+                           rand_bits, rand_f32, requires_gpu)
 
 pytestmark = [pytest.mark.gpu, requires_gpu]
 
@@ -40,7 +40,7 @@ def test_full_edge_lengths(Hq, Hkv):
         ref = attention.attend(q[b], hc.k[b], hc.v[b], keysets.full_keys(n), SCALE)
         check_close(got[b], ref, what="full n=%d" % n)
         if n <= 5000:
-            check_close(got[b], ref, abs_tol=1e-5, row_rel_tol=1e-4, what="full tight n=%d" % n)
+            check_tight(got[b], ref, q[b], hc.k[b], hc.v[b], keysets.full_keys(n), SCALE, what="full tight n=%d" % n)
 
 
 @pytest.mark.parametrize("sinks,window", [(4, 2048), (3, 20), (0, 17), (20, 5), (4, 1)])
@@ -54,7 +54,8 @@ def test_local_edge_lengths(sinks, window):
     got = out.cpu().numpy()
     for b, n in enumerate(ns):
         ref = attention.attend(q[b], hc.k[b], hc.v[b], keysets.local_keys(n, sinks, window), SCALE)
-        check_close(got[b], ref, abs_tol=1e-5, row_rel_tol=1e-4, what="local n=%d s=%d w=%d" % (n, sinks, window))
+        check_tight(got[b], ref, q[b], hc.k[b], hc.v[b], keysets.local_keys(n, sinks, window), SCALE,
+                    what="local n=%d s=%d w=%d" % (n, sinks, window))
 
 
 def test_local_equals_full_up_to_s_plus_w():
@@ -68,8 +69,8 @@ def test_local_equals_full_up_to_s_plus_w():
     f = ops.oda_decode_full(qt, hc.kv).cpu().numpy()
     for b, n in enumerate(ns):
         ref = attention.attend(q[b], hc.k[b], hc.v[b], keysets.full_keys(n), SCALE)
-        check_close(a[b], ref, abs_tol=1e-5, row_rel_tol=1e-4)
-        check_close(f[b], ref, abs_tol=1e-5, row_rel_tol=1e-4)
+        check_tight(a[b], ref, q[b], hc.k[b], hc.v[b], keysets.full_keys(n), SCALE)
+        check_tight(f[b], ref, q[b], hc.k[b], hc.v[b], keysets.full_keys(n), SCALE)
 
 
 def test_peaky_queries_rescale_path():
@@ -91,7 +92,7 @@ def test_peaky_queries_rescale_path():
     for b, n in enumerate(ns):
         ref = attention.attend(q[b], hc.k[b], hc.v[b], keysets.full_keys(n), SCALE)
         check_close(got[b], ref, what="peaky n=%d" % n)
-        check_close(got[b], ref, abs_tol=1e-4, row_rel_tol=1e-4, what="peaky tight n=%d" % n)
+        check_tight(got[b], ref, q[b], hc.k[b], hc.v[b], keysets.full_keys(n), SCALE, what="peaky tight n=%d" % n)
 
 
 def oracle_bits(x):
@@ -122,7 +123,7 @@ def test_fused_commit_full_and_local():
             oracle.oda.commit(k, v, n, kn[b], vn[b])
             keys = keysets.local_keys(n) if mode == "local" else keysets.full_keys(n)
             ref = attention.attend(q[b], k, v, keys, SCALE)
-            check_close(got[b], ref, abs_tol=1e-5, row_rel_tol=1e-4, what="%s commit n=%d" % (mode, n))
+            check_tight(got[b], ref, q[b], k, v, keys, SCALE, what="%s commit n=%d" % (mode, n))
             kr, vr = ops.kv_read(hc.kv, b, n - 1, 1)
             assert np.array_equal(bf16_tensor_to_bits(kr)[0], kn[b])
             assert np.array_equal(bf16_tensor_to_bits(vr)[0], vn[b])
@@ -156,7 +157,7 @@ def test_selector_and_gate_skip_requests():
             v = hc.v[b].copy()
             oracle.oda.commit(k, v, n, kn[b], vn[b])
             ref = attention.attend(q[b], k, v, keysets.full_keys(n), SCALE)
-            check_close(got[b], ref, abs_tol=1e-5, row_rel_tol=1e-4)
+            check_tight(got[b], ref, q[b], k, v, keysets.full_keys(n), SCALE)
 
 
 def _mask_words(kept_lists, max_blocks):
@@ -194,7 +195,8 @@ def test_blocks_gather_and_attention(seed):
         assert np.array_equal(gat[b, :num[b]], phys)
         assert np.array_equal(cnt[b, :num[b]], c)
         ref = attention.attend(q[b], hc.k[b], hc.v[b], keysets.block_keys(n, kept[b]), SCALE)
-        check_close(got[b], ref, abs_tol=1e-5, row_rel_tol=1e-4, what="blocks n=%d" % n)
+        check_tight(got[b], ref, q[b], hc.k[b], hc.v[b], keysets.block_keys(n, kept[b]), SCALE,
+                    what="blocks n=%d" % n)
 
 
 def test_blocks_all_kept_equals_full_and_commit_when_unkept():
@@ -210,8 +212,8 @@ def test_blocks_all_kept_equals_full_and_commit_when_unkept():
     o_f = ops.oda_decode_full(qt, hc.kv)
     for b, n in enumerate(ns):
         ref = attention.attend(q[b], hc.k[b], hc.v[b], keysets.full_keys(n), SCALE)
-        check_close(o_b.cpu().numpy()[b], ref, abs_tol=1e-5, row_rel_tol=1e-4)
-        check_close(o_f.cpu().numpy()[b], ref, abs_tol=1e-5, row_rel_tol=1e-4)
+        check_tight(o_b.cpu().numpy()[b], ref, q[b], hc.k[b], hc.v[b], keysets.full_keys(n), SCALE)
+        check_tight(o_f.cpu().numpy()[b], ref, q[b], hc.k[b], hc.v[b], keysets.full_keys(n), SCALE)
     # keep-list without the current token's block: the token is committed, not attended
     kn = rand_bits(rng.mix_key(904, 1), B, Hkv)
     vn = rand_bits(rng.mix_key(904, 2), B, Hkv)
@@ -224,7 +226,7 @@ def test_blocks_all_kept_equals_full_and_commit_when_unkept():
         v = hc.v[b].copy()
         oracle.oda.commit(k, v, n, kn[b], vn[b])
         ref = attention.attend(q[b], k, v, keysets.block_keys(n, kept[b]), SCALE)
-        check_close(out.cpu().numpy()[b], ref, abs_tol=1e-5, row_rel_tol=1e-4)
+        check_tight(out.cpu().numpy()[b], ref, q[b], k, v, keysets.block_keys(n, kept[b]), SCALE)
         kr, vr = ops.kv_read(hc.kv, b, n - 1, 1)
         assert np.array_equal(bf16_tensor_to_bits(kr)[0], kn[b])
         assert np.array_equal(bf16_tensor_to_bits(vr)[0], vn[b])
@@ -249,7 +251,7 @@ def test_gather_once_decode_per_layer():
         assert torch.equal(o1, o2) and torch.equal(gat, g2) and torch.equal(cnt, c2) and torch.equal(num, n2)
         for b, n in enumerate(ns):
             ref = attention.attend(q[b], hc.k[b], hc.v[b], keysets.block_keys(n, kept[b]), SCALE)
-            check_close(o1.cpu().numpy()[b], ref, abs_tol=1e-5, row_rel_tol=1e-4)
+            check_tight(o1.cpu().numpy()[b], ref, q[b], hc.k[b], hc.v[b], keysets.block_keys(n, kept[b]), SCALE)
 
 
 def test_gathered_list_with_bad_block_id():
@@ -269,8 +271,9 @@ def test_gathered_list_with_bad_block_id():
     ws = ops.workspace(1, Hq)
     out = ops.da_decode_gathered(torch.as_tensor(q, device="cuda"), hc.kv, gat, cnt, num, ws=ws)
     assert ops.workspace_error(ws) & 1  # SK_DEVERR_BLOCK_ID
-    ref = attention.attend(q[0], hc.k[0], hc.v[0], keysets.block_keys(300, [blocks[0], blocks[2]]), SCALE)
-    check_close(out.cpu().numpy()[0], ref, abs_tol=1e-5, row_rel_tol=1e-4)
+    keys = keysets.block_keys(300, [blocks[0], blocks[2]])
+    ref = attention.attend(q[0], hc.k[0], hc.v[0], keys, SCALE)
+    check_tight(out.cpu().numpy()[0], ref, q[0], hc.k[0], hc.v[0], keys, SCALE)
 
 
 def test_large_batch_all_views_with_selector():
@@ -305,7 +308,7 @@ def test_large_batch_all_views_with_selector():
         oracle.oda.commit(k, v, n, kn[b], vn[b])
         keys = (keysets.local_keys(n, 4, 64), keysets.full_keys(n), keysets.block_keys(n, kept[b]))[view[b]]
         ref = attention.attend(q[b], k, v, keys, SCALE)
-        check_close(got[b], ref, abs_tol=1e-5, row_rel_tol=1e-4, what="b=%d n=%d view=%d" % (b, n, view[b]))
+        check_tight(got[b], ref, q[b], k, v, keys, SCALE, what="b=%d n=%d view=%d" % (b, n, view[b]))
         kr, vr = ops.kv_read(hc.kv, b, n - 1, 1)
         assert np.array_equal(bf16_tensor_to_bits(kr)[0], kn[b]) and np.array_equal(bf16_tensor_to_bits(vr)[0], vn[b])
 
@@ -322,7 +325,7 @@ def test_maximum_batch():
     out = ops.oda_decode_full(torch.as_tensor(q, device="cuda"), hc.kv).cpu().numpy()
     for b in range(0, B, 7):
         ref = attention.attend(q[b], hc.k[b], hc.v[b], keysets.full_keys(ns[b]), SCALE)
-        check_close(out[b], ref, abs_tol=1e-5, row_rel_tol=1e-4, what="b=%d" % b)
+        check_tight(out[b], ref, q[b], hc.k[b], hc.v[b], keysets.full_keys(ns[b]), SCALE, what="b=%d" % b)
 
 
 def test_keep_mask_modes():
@@ -387,7 +390,7 @@ def test_invalid_lengths_set_device_error_and_zero_rows():
     got = out.cpu().numpy()
     assert (got[0] == 0).all()
     ref = attention.attend(q[1], hc.k[1], hc.v[1], keysets.full_keys(60), SCALE)
-    check_close(got[1], ref, abs_tol=1e-5, row_rel_tol=1e-4)
+    check_tight(got[1], ref, q[1], hc.k[1], hc.v[1], keysets.full_keys(60), SCALE)
 
 
 def test_kv_write_read_roundtrip_and_layout():
@@ -421,10 +424,40 @@ def test_deterministic_replay():
     first = [ops.oda_decode_full(q, hc.kv, ws=ws).cpu().numpy() for hc in hcs]
     for b, n in enumerate([40000, 3000, 131]):
         ref = attention.attend(q.cpu().numpy()[b], hcs[0].k[b], hcs[0].v[b], keysets.full_keys(n), SCALE)
-        check_close(first[0][b], ref, abs_tol=1e-5, row_rel_tol=1e-4)
+        check_tight(first[0][b], ref, q.cpu().numpy()[b], hcs[0].k[b], hcs[0].v[b], keysets.full_keys(n), SCALE)
     for rep in range(20):
         for i, hc in enumerate(hcs):
             o = ops.oda_decode_full(q, hc.kv, ws=ws)
             o2 = ops.oda_decode_local(q, hc.kv, ws=ws)
             assert np.array_equal(o.cpu().numpy(), first[i]), rep
             assert np.isfinite(o2.cpu().numpy()).all()
+
+
+@pytest.mark.parametrize("with_sel", [False, True])
+def test_kv_append_standalone(with_sel):
+    # the stand-alone commit writes the current token into slot n-1 of every selected
+    # request and nothing else; an invalid length sets the device error bit
+    from sparse_kv_recall_amd import ops
+    Hq, Hkv = 32, 8
+    ns = [1, 16, 17, 300, 4097, 33]
+    hc = HostCache(Hq, Hkv, ns, seed=90)
+    B = len(ns)
+    kn = rand_bits(rng.mix_key(906, 1), B, Hkv)
+    vn = rand_bits(rng.mix_key(906, 2), B, Hkv)
+    sel = torch.tensor([1, 0, 1, 1, 0, 1], dtype=torch.int32, device="cuda") if with_sel else None
+    ws = ops.workspace(B, Hq)
+    ops.kv_append(hc.kv, bits_to_bf16_tensor(kn), bits_to_bf16_tensor(vn), sel=sel, sel_value=1, ws=ws)
+    torch.cuda.synchronize()
+    assert ops.workspace_error(ws) == 0
+    for b, n in enumerate(ns):
+        k, v = hc.k[b][:n].copy(), hc.v[b][:n].copy()
+        if sel is None or int(sel[b]) == 1:
+            oracle.oda.commit(k, v, n, kn[b], vn[b])
+        kr, vr = ops.kv_read(hc.kv, b, 0, n)
+        assert np.array_equal(bf16_tensor_to_bits(kr), k), b
+        assert np.array_equal(bf16_tensor_to_bits(vr), v), b
+    # a request of length 0 is refused on the device: error bit, nothing written
+    hc.set_lens([0] + ns[1:])
+    ws = ops.workspace(B, Hq)
+    ops.kv_append(hc.kv, bits_to_bf16_tensor(kn), bits_to_bf16_tensor(vn), ws=ws)
+    assert ops.workspace_error(ws) & 2  # SK_DEVERR_SEQ_LEN

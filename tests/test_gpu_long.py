@@ -12,8 +12,8 @@ import torch
 import oracle
 from oracle import attention, keysets
 from synth import rng
-from tests.helpers import (SCALE, HostCache, bf16_tensor_to_bits, bits_to_bf16_tensor, check_close, rand_bits,
-                           rand_f32, requires_gpu)
+from tests.helpers import (SCALE, HostCache, bf16_tensor_to_bits, bits_to_bf16_tensor, check_close, check_tight,
+                           rand_bits, rand_f32, requires_gpu)
 
 pytestmark = [pytest.mark.gpu, requires_gpu]
 
@@ -43,12 +43,13 @@ def test_full_long_context_descriptor_chunks_and_blocks_view():
     k, v = hc.k[0].copy(), hc.v[0].copy()
     oracle.oda.commit(k, v, n, kn[0], vn[0])
     ref = attention.attend(q[0], k, v, keysets.full_keys(n), SCALE)
-    check_close(out[0], ref, abs_tol=1e-5, row_rel_tol=1e-4, what="full n=%d" % n)
+    check_tight(out[0], ref, q[0], k, v, keysets.full_keys(n), SCALE, what="full n=%d" % n)
     kr, vr = ops.kv_read(hc.kv, 0, n - 1, 1)
     assert np.array_equal(bf16_tensor_to_bits(kr)[0], kn[0]) and np.array_equal(bf16_tensor_to_bits(vr)[0], vn[0])
     # before the commit the Full view attended the old slot n - 1
     ref0 = attention.attend(q[0], hc.k[0], hc.v[0], keysets.full_keys(n), SCALE)
-    check_close(out_f0.cpu().numpy()[0], ref0, abs_tol=1e-5, row_rel_tol=1e-4, what="full n=%d (no commit)" % n)
+    check_tight(out_f0.cpu().numpy()[0], ref0, q[0], hc.k[0], hc.v[0], keysets.full_keys(n), SCALE,
+                what="full n=%d (no commit)" % n)
 
 
 @pytest.mark.parametrize("n", [9337, 70001, 4096 * 16 * 4 + 3])
@@ -64,7 +65,7 @@ def test_full_many_splits_merge_in_rounds(n):
     q = rand_f32(rng.mix_key(982, n), (1, Hq, 128), 1.0)
     out = ops.oda_decode_full(torch.as_tensor(q, device="cuda"), hc.kv).cpu().numpy()
     ref = attention.attend(q[0], hc.k[0], hc.v[0], keysets.full_keys(n), SCALE)
-    check_close(out[0], ref, abs_tol=1e-5, row_rel_tol=1e-4, what="full Hkv=1 n=%d" % n)
+    check_tight(out[0], ref, q[0], hc.k[0], hc.v[0], keysets.full_keys(n), SCALE, what="full Hkv=1 n=%d" % n)
 
 
 def test_pool_beyond_4gib():
@@ -97,6 +98,76 @@ def test_pool_beyond_4gib():
         for view, keys in (("full", keysets.full_keys(n)), ("local", keysets.local_keys(n, 4, 2048)),
                            ("blocks", keysets.full_keys(n))):
             ref = attention.attend(q[b], k, v, keys, SCALE)
-            check_close(outs[view][b], ref, abs_tol=1e-5, row_rel_tol=1e-4, what="%s n=%d" % (view, n))
+            check_tight(outs[view][b], ref, q[b], k, v, keys, SCALE, what="%s n=%d" % (view, n))
         kr, vr = ops.kv_read(hc.kv, b, n - 1, 1)
         assert np.array_equal(bf16_tensor_to_bits(kr)[0], kn[b]) and np.array_equal(bf16_tensor_to_bits(vr)[0], vn[b])
+
+
+# Split partials of the workspace start after the 256-byte header and the 16384 ticket
+# words; the partials of a launch are written before they are merged, so a merge that
+# read a slot no split of this launch wrote would bring NaN into the output.
+PARTIALS_OFFSET = 256 + 16384 * 4
+
+
+def _poisoned_workspace(B, Hq):
+    from sparse_kv_recall_amd import ops
+    ws = ops.workspace(B, Hq)
+    assert ops.workspace_bytes(1, 1) - PARTIALS_OFFSET == (1024 + 1) * 130 * 4  # the documented layout
+    return ws
+
+
+def _poison(ws):
+    ws[PARTIALS_OFFSET:].fill_(0xFF)  # every float of the partials region is NaN
+
+
+def test_merge_reads_only_this_launchs_partials():
+    # Full and all-blocks list views at n = 9337 on one KV head (73 splits, merged in a
+    # round of 48 and one of 25), the Local view on one KV head (2052 positions: 17
+    # splits), and the per-request views launch over a mixed batch, each launched on a
+    # workspace whose partials region was filled with NaN just before
+    from sparse_kv_recall_amd import ops
+    Hq, Hkv = 4, 1
+    ns = [9337, 2100, 40, 5000]
+    hc = HostCache(Hq, Hkv, ns, seed=85)
+    B = len(ns)
+    q = rand_f32(rng.mix_key(985), (B, Hq, 128), 1.0)
+    qt = torch.as_tensor(q, device="cuda")
+    ws = _poisoned_workspace(B, Hq)
+    single = lambda b: dict(q=qt[b:b + 1].contiguous(), kv=ops.PagedKVCache(
+        hc.kv.num_phys_blocks, 1, Hq, Hkv, hc.max_blocks, block_tables=hc.kv.block_tables[b:b + 1].contiguous(),
+        seq_lens=hc.kv.seq_lens[b:b + 1].contiguous(), k_pool=hc.kv.k_pool, v_pool=hc.kv.v_pool))
+    for view in ("full", "list", "local"):
+        b = 0 if view != "local" else 1
+        a = single(b)
+        _poison(ws)
+        if view == "full":
+            out = ops.oda_decode_full(a["q"], a["kv"], ws=ws)
+            keys = keysets.full_keys(ns[b])
+        elif view == "local":
+            out = ops.oda_decode_local(a["q"], a["kv"], ws=ws)
+            keys = keysets.local_keys(ns[b])
+        else:
+            nb = (ns[b] + 15) // 16
+            words = np.zeros((1, (hc.max_blocks + 31) // 32), np.uint32)
+            for blk in range(nb):
+                words[0, blk // 32] |= np.uint32(1 << (blk % 32))
+            out, _, _, _ = ops.da_decode_blocks(a["q"], a["kv"], torch.as_tensor(words.view(np.int32), device="cuda"),
+                                                ws=ws)
+            keys = keysets.full_keys(ns[b])
+        got = out.cpu().numpy()[0]
+        ref = attention.attend(q[b], hc.k[b], hc.v[b], keys, SCALE)
+        check_tight(got, ref, q[b], hc.k[b], hc.v[b], keys, SCALE, what="%s after poisoning" % view)
+    # per-request views: Full, Local, blocks, Full
+    view = torch.tensor([1, 0, 2, 1], dtype=torch.int32, device="cuda")
+    kept = [None, None, [0, 2], None]
+    words = np.zeros((B, (hc.max_blocks + 31) // 32), np.uint32)
+    words[2, 0] = 0b101
+    gat, cnt, num = ops.da_gather(hc.kv, torch.as_tensor(words.view(np.int32), device="cuda"), sel=view,
+                                  sel_value=2, ws=ws)
+    _poison(ws)
+    out = ops.oda_decode_views(qt, hc.kv, view, gat, cnt, num, ws=ws).cpu().numpy()
+    for b, n in enumerate(ns):
+        keys = (keysets.local_keys(n), keysets.full_keys(n), keysets.block_keys(n, kept[b] or []))[int(view[b])]
+        ref = attention.attend(q[b], hc.k[b], hc.v[b], keys, SCALE)
+        check_tight(out[b], ref, q[b], hc.k[b], hc.v[b], keys, SCALE, what="views b=%d after poisoning" % b)
+    assert ops.workspace_error(ws) == 0
