@@ -449,14 +449,18 @@ __device__ inline void load_tile(const uint8_t* kpool, const uint8_t* vpool, int
 // HAS_SEL: requests are filtered by sel[b] == sel_value (gated / per-request views).
 // Without a selector a separate instance runs, so a profile tells gated launches
 // (which exit at once on non-recall steps) apart from unconditional ones.
-template <int MODE, bool HAS_SEL>
+// SINGLE: a launch on one request. Its plan is the same as the small-batch plan below
+// (same tiles per split, so the same work items and the same results), computed on the
+// uniform length alone: no cross-lane reductions, scans or request search, which shortens
+// the chain of instructions before the first tile is requested.
+template <int MODE, bool HAS_SEL, bool SINGLE>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
   constexpr int W = kWavesPerWG;
   extern __shared__ float smem[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int B = P.kv.batch, Hkv = P.kv.num_kv_heads, Hq = P.kv.num_q_heads, G = Hq / Hkv;
+  const int B = SINGLE ? 1 : P.kv.batch, Hkv = P.kv.num_kv_heads, Hq = P.kv.num_q_heads, G = Hq / Hkv;
   const int maxb = P.kv.max_blocks;
   const int acc_region = max(W * G * kHeadDim, 2 * kMaxSplits * G + 4 * kThreads);
 
@@ -485,7 +489,14 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
   // round of loads (lanes past the batch read request 0 and ignore it).
   int l_len = 0, l_listed = 0, l_view = MODE;
   bool l_sel = true;
-  if (B <= 64) {
+  if (SINGLE) {  // uniform values, one round of loads
+    const int n0 = P.kv.seq_lens[0];
+    const int listed0 = (MODE == kList) ? P.list_num[0] : 0;
+    const int sel0 = HAS_SEL ? P.sel[0] : 0;
+    l_len = __builtin_amdgcn_readfirstlane(n0);
+    l_listed = __builtin_amdgcn_readfirstlane(listed0);
+    if (HAS_SEL && __builtin_amdgcn_readfirstlane(sel0) != P.sel_value) return;
+  } else if (B <= 64) {
     const int bl = (lane < B) ? lane : 0;
     l_len = P.kv.seq_lens[bl];
     if (MODE == kList || MODE == kViews) l_listed = P.list_num[bl];
@@ -524,7 +535,31 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
   int T, total_items;
   int w_tiles = 0, w_start = 0, w_len = 0;  // small batches: lane b holds request b's tiles,
                                              // first item and sequence length
-  if (B <= 64) {
+  if (SINGLE) {
+    // the small-batch plan below for one request: the rounding reserve, then, when the
+    // splits would leave more than a quarter of the slots idle, the smallest split size
+    // from tiles / slots up (its splits always fit the slots)
+    const int n = l_len;
+    const bool valid = n >= 1 && n <= maxb * kBlock;
+    const int tiles = valid ? request_tiles<MODE>(P, 0, n, l_listed) : 0;
+    if (blockIdx.x == 0 && wave == 0 && lane == 0 && (!valid || tiles == 0)) bad_request(0, n, valid);
+    T = split_size(tiles, tiles > 0 ? 1 : 0, tiles);
+    const int slots = int(gridDim.x) / Hkv;
+    int splits = (tiles + T - 1) / T;
+    if (4 * splits < 3 * slots) {
+      int t = (tiles + slots - 1) / slots;
+      const int t_cap = (tiles + kMaxSplits - 1) / kMaxSplits;
+      if (t < t_cap) t = t_cap;
+      if (t < kMinTilesPerSplit) t = kMinTilesPerSplit;
+      if (t < T) {
+        T = t;
+        splits = (tiles + T - 1) / T;
+      }
+    }
+    w_tiles = tiles;
+    w_len = n;
+    total_items = splits * Hkv;
+  } else if (B <= 64) {
     // every wave plans on its own with register reductions; no workgroup barrier
     int tiles = 0;
     if (lane < B && l_sel) {
@@ -634,10 +669,21 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
   const uint8_t* kpool = reinterpret_cast<const uint8_t*>(P.kv.k_pool);
   const uint8_t* vpool = reinterpret_cast<const uint8_t*>(P.kv.v_pool);
 
-  for (int item = item_first; item < total_items; item += gridDim.x) {
+  // One work item. A single-request launch has at most one item per workgroup (its plan
+  // never makes more items than the grid has workgroups; the host picks that instance only
+  // for grids of at least two workgroups per KV head), so it runs the body once, as
+  // straight-line code: kept in a loop, the compiler hoists the loop-invariant values and
+  // spills them to vector lanes at the loop head, about 500 instructions before the first
+  // request of a launch.
+  auto item_body = [&](const int item) {
     // locate the request: the one whose item range holds `item` (it has items)
     int b, tiles_b, item_base, n, view = MODE;  // view: the request's view under kViews
-    if (B <= 64) {
+    if (SINGLE) {
+      b = 0;
+      tiles_b = w_tiles;
+      n = w_len;
+      item_base = 0;
+    } else if (B <= 64) {
       const int end = w_start + ((w_tiles + T - 1) / T) * Hkv;
       b = __builtin_amdgcn_readfirstlane(__popcll(__ballot(lane < B && end <= item)));
       tiles_b = __builtin_amdgcn_readlane(w_tiles, b);
@@ -661,11 +707,27 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
     const int g = local / splits, split = local % splits;
     const int t_begin = split * T, t_end = min(t_begin + T, tiles_b);
 
-    // q rows of the G heads of KV head g for the operand staging below, requested first so
-    // that their latency overlaps the descriptor loads. Waves 0-3 load them (wave c the
-    // dims of chunk c) and stage both bf16 parts; waves 4-7 request nothing here, so the
-    // workgroup's first round of loads stays small. Lanes past the G heads read head 0
-    // (and stage zeros).
+    // Tiles of this wave: wave, wave + W, ... of the split. Their descriptors (physical
+    // block, valid range; lane r for tile r of a chunk of 64) are requested first: the
+    // first tile's request waits for them, and the loads issued after them (q rows, the
+    // commit lookups, the current token) stay in flight meanwhile. The descriptors are
+    // bounded by the wave's tiles, the commit tile included (a descriptor loaded and not
+    // used costs nothing).
+    const int my_tiles = (t_end - t_begin > wave) ? (t_end - t_begin - wave + W - 1) / W : 0;
+    int dphys = 0, dlohi = 0;
+    auto load_desc = [&](int c0) {
+      const int ti = t_begin + wave + (c0 + lane) * W;
+      Tile tt = Tile{0, 0, 0};
+      if (c0 + lane < my_tiles) tt = tile_at<MODE>(P, b, n, ti, view);
+      dphys = tt.phys;
+      dlohi = tt.lo | (tt.hi << 8);
+    };
+    load_desc(0);
+
+    // q rows of the G heads of KV head g for the operand staging below. Waves 0-3 load
+    // them (wave c the dims of chunk c) and stage both bf16 parts; waves 4-7 request
+    // nothing here, so the workgroup's first round of loads stays small. Lanes past the G
+    // heads read head 0 (and stage zeros).
     const int qc = wave & 3, qcol = lane & 15, qgrp = lane >> 4;
     const float* qrow = P.q + (int64_t(b) * Hq + g * G + (qcol < G ? qcol : 0)) * kHeadDim + 8 * (4 * qc + qgrp);
     f32x4 qa0 = {0.f, 0.f, 0.f, 0.f}, qa1 = {0.f, 0.f, 0.f, 0.f};
@@ -694,11 +756,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
       }
     }
 
-    // Tiles of this wave: wave, wave + W, ... of the split. The tile that receives the
-    // current token (the request's last tile) is the owning wave's last tile; its key and
-    // value come from LDS, staged below together with q, so the pipeline never waits on
-    // them.
-    const int my_tiles = (t_end - t_begin > wave) ? (t_end - t_begin - wave + W - 1) / W : 0;
+    // The tile that receives the current token (the request's last tile) is the owning
+    // wave's last tile; its key and value come from LDS, staged below together with q, so
+    // the pipeline never waits on them.
     const bool split_commits = commit_tile >= t_begin && commit_tile < t_end;
     const bool own_commit = split_commits && (commit_tile - t_begin) % W == wave;
     const int loop_tiles = my_tiles - (own_commit ? 1 : 0);
@@ -710,23 +770,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
     if (split_commits && wave < 2)
       tok_word = reinterpret_cast<const uint32_t*>((wave ? P.v_new : P.k_new) + (int64_t(b) * Hkv + g) * kHeadDim)[lane];
 
-    // descriptors (physical block, valid range) of this wave's first 64 tiles, lane r for
-    // tile r
-    int dphys = 0, dlohi = 0;
-    auto load_desc = [&](int c0) {
-      const int ti = t_begin + wave + (c0 + lane) * W;
-      Tile tt = Tile{0, 0, 0};
-      if (c0 + lane < loop_tiles) tt = tile_at<MODE>(P, b, n, ti, view);
-      dphys = tt.phys;
-      dlohi = tt.lo | (tt.hi << 8);
-    };
-    load_desc(0);
-
     // q -> MFMA B operands (hi and lo bf16 parts), staged in LDS: entry (c, part, lane) holds
     // dims 8*(4c + lane/16) .. +7 of head lane%16. The wave's first tile is requested
-    // before the q rows are used, so its latency overlaps the staging. A wave without loop
-    // tiles requests its first descriptor (block 0 of the pool when it has none) and never
-    // uses it, so the request needs no branch.
+    // before the q rows are used, so its latency overlaps the staging. A wave without tiles
+    // requests block 0 of the pool and never uses it, so the request needs no branch.
     u32x4 k0[4], v0[4], k1[4], v1[4];
     load_tile(kpool, vpool, __builtin_amdgcn_readfirstlane(dphys), g, Hkv, lane, k0, v0);
     if (split_commits && tid < 128) s_new[tid] = tok_word;
@@ -843,9 +890,16 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
     }
     if (own_commit) {
       // the request's last tile: attend with the current token substituted from LDS, then
-      // write the token into its slot of the pool
-      Tile tt = tile_at<MODE>(P, b, n, commit_tile, view);
-      load_tile(kpool, vpool, tt.phys, g, Hkv, lane, k0, v0);
+      // write the token into its slot of the pool. When it is the wave's only tile, the
+      // first request above already fetched it (lane 0's descriptor is that tile).
+      Tile tt;
+      if (loop_tiles == 0) {
+        const int lohi = __builtin_amdgcn_readfirstlane(dlohi);
+        tt = Tile{__builtin_amdgcn_readfirstlane(dphys), lohi & 255, lohi >> 8};
+      } else {
+        tt = tile_at<MODE>(P, b, n, commit_tile, view);
+        load_tile(kpool, vpool, tt.phys, g, Hkv, lane, k0, v0);
+      }
       substitute_token(s_new, tl, lane, k0, v0);
       process(k0, v0, tt.lo | (tt.hi << 8));
       if (tt.hi > tt.lo) commit_from_lds(P, s_new, tt.phys, g, tl, lane);
@@ -931,6 +985,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
       }
     }
     __syncthreads();
+  };
+  if constexpr (SINGLE) {
+    if (item_first < total_items) item_body(item_first);
+  } else {
+    for (int item = item_first; item < total_items; item += gridDim.x) item_body(item);
   }
 }
 
@@ -1033,12 +1092,17 @@ int enqueue_decode(const float* q, sk_paged_kv kv, const void* k_new, const void
   size_t lds = size_t(kThreads) * 16 + 128 * 4 + size_t(acc_region) * 4 + size_t(kWavesPerWG) * 16 * 4 * 2 +
                size_t(3 * kv.batch + 1 + 8 + (MODE == kViews ? kv.batch : 0)) * 4;
   if constexpr (MODE == kViews) {  // the views are the selector: always present
-    hipLaunchKernelGGL((decode_kernel<MODE, true>), dim3(unsigned(grid)), dim3(kThreads), lds, stream, P);
+    hipLaunchKernelGGL((decode_kernel<MODE, true, false>), dim3(unsigned(grid)), dim3(kThreads), lds, stream, P);
+  } else if (kv.batch == 1 && grid >= 2 * int64_t(kv.num_kv_heads)) {
+    if (sel)
+      hipLaunchKernelGGL((decode_kernel<MODE, true, true>), dim3(unsigned(grid)), dim3(kThreads), lds, stream, P);
+    else
+      hipLaunchKernelGGL((decode_kernel<MODE, false, true>), dim3(unsigned(grid)), dim3(kThreads), lds, stream, P);
   } else {
     if (sel)
-      hipLaunchKernelGGL((decode_kernel<MODE, true>), dim3(unsigned(grid)), dim3(kThreads), lds, stream, P);
+      hipLaunchKernelGGL((decode_kernel<MODE, true, false>), dim3(unsigned(grid)), dim3(kThreads), lds, stream, P);
     else
-      hipLaunchKernelGGL((decode_kernel<MODE, false>), dim3(unsigned(grid)), dim3(kThreads), lds, stream, P);
+      hipLaunchKernelGGL((decode_kernel<MODE, false, false>), dim3(unsigned(grid)), dim3(kThreads), lds, stream, P);
   }
   return launch_status(hipGetLastError());
 }
