@@ -657,6 +657,105 @@ def other_workloads(device, reps=2):
     return res
 
 
+def config_lines(device, reps=3, min_bytes=1 << 30):
+    """Per-configuration figures beside the metric:
+    * oda_small (1 layer, 8 q / 2 KV heads, 4K history, 64 steps, Full on a seeded
+      Bernoulli(0.4) step): microseconds per step, each step one graph replay (feed,
+      Local, gate, gated Full). 4 MiB of KV stay cache resident: a latency figure.
+    * da_32k's three declared modes at the first step (n = 32769, the block list gathered
+      through the device's keep mask), each attended over enough pools that the attended
+      bytes of one graph replay reach `min_bytes` (at least 8 pools), so the last-level
+      cache cannot serve them: microseconds per launch and GB/s of attended positions
+      (4096 B each, plus q and out), with the commit of the current token."""
+    import math as _m
+
+    import numpy as np
+    import torch
+    from sparse_kv_recall_amd import ops
+    from sparse_kv_recall_amd.stack import ODAStack, capture_graph
+    from synth import device as sdev
+    from synth import rng
+    from synth import workloads
+
+    res = {}
+    wl = workloads.oda_small()
+    H0 = int(wl.H0[0])
+    seq = torch.zeros(1, dtype=torch.int32, device=device)
+    stack = ODAStack(wl.layers, 1, wl.Hq, wl.Hkv, wl.num_phys_blocks, wl.max_blocks,
+                     torch.as_tensor(wl.block_tables, device=device), seq, sinks=wl.sinks, window=wl.window,
+                     device=device)
+    _stage_history(stack.caches[0], wl, 0, H0, 0, device)
+    feeder = sdev.Feeder(wl, seq, device=device, with_scores=True)
+
+    def step_small():
+        feeder.step()
+        stack.local_pass(feeder.q[:, 0], feeder.k[:, 0], feeder.v[:, 0])
+        stack.gate_from_scores(feeder.scores, wl.theta)
+        stack.full_pass(feeder.q[:, 1], feeder.k[:, 1], feeder.v[:, 1], gated=True)
+
+    graph = capture_graph(step_small)
+    ms = _time_replays(graph, wl.steps, lambda: feeder.set_step(0), reps)
+    res["oda_small"] = {"steps": wl.steps, "recall_steps": int((wl.sched_scores[:, 0] > 0).sum()),
+                        "us_per_step": round(ms * 1e3 / wl.steps, 2),
+                        "note": "4 MiB of KV, cache resident: latency, no HBM claim"}
+    del graph, stack, feeder
+    torch.cuda.empty_cache()
+
+    wl = workloads.da_32k()
+    n = int(wl.H0[0]) + 1
+    mb = wl.max_blocks
+    seq = torch.full((1,), n, dtype=torch.int32, device=device)
+    ident = torch.arange(mb, dtype=torch.int32, device=device)[None]
+    probe = ops.PagedKVCache(1, 1, wl.Hq, wl.Hkv, mb, block_tables=ident, seq_lens=seq, device=device)
+    ws = ops.workspace(1, wl.Hq, device)
+    modes = {}
+    for mode, name in ((ops.DA_GLOBAL, "global"), (ops.DA_FOCUS, "focus"), (ops.DA_LOCAL, "local")):
+        first = int(np.flatnonzero(wl.decl[:, 0, 0] == mode)[0])
+        decl = torch.as_tensor(wl.decl[first], device=device)
+        mask = ops.da_keep_mask(decl, probe, wl.da_local_tokens)
+        gat, cnt, num = ops.da_gather(probe, mask, ws=ws)  # identity table: the kept logical blocks
+        K = int(num[0].item())
+        kept = gat[0, :K].cpu().numpy()
+        positions = int(cnt[0, :K].sum().item())
+        nbytes = positions * wl.Hkv * 512 + 2 * wl.Hq * 512
+        P = max(8, -(-min_bytes // nbytes))
+        kpool = torch.empty((P * K, wl.Hkv, 2048), dtype=torch.bfloat16, device=device)
+        vpool = torch.empty_like(kpool)
+        sdev.fill_normal_(kpool, rng.mix_key(4, 40, mode), 0)
+        sdev.fill_normal_(vpool, rng.mix_key(4, 41, mode), 0)
+        views, lists = [], []
+        for p in range(P):
+            bt = np.zeros((1, mb), np.int32)
+            bt[0, kept] = p * K + np.arange(K, dtype=np.int32)
+            c = ops.PagedKVCache(P * K, 1, wl.Hq, wl.Hkv, mb, block_tables=torch.as_tensor(bt, device=device),
+                                 seq_lens=seq, k_pool=kpool, v_pool=vpool)
+            views.append(c)
+            lists.append(ops.da_gather(c, mask, ws=ws))
+        q = torch.randn(P, 1, wl.Hq, 128, device=device)
+        kn = torch.randn(P, 1, wl.Hkv, 128, device=device).to(torch.bfloat16)
+        vn = torch.randn(P, 1, wl.Hkv, 128, device=device).to(torch.bfloat16)
+        out = torch.zeros(P, 1, wl.Hq, 128, device=device)
+
+        def run():
+            for p in range(P):
+                g_, c_, n_ = lists[p]
+                ops.da_decode_gathered(q[p], views[p], g_, c_, n_, kn[p], vn[p], out=out[p], ws=ws)
+
+        graph = capture_graph(run)
+        ms = _time_replays(graph, 4, lambda: None, reps)
+        us = ms * 1e3 / (4 * P)
+        modes[name] = {"kept_blocks": K, "kept_positions": positions, "pools": P,
+                       "attended_bytes_per_replay": P * nbytes, "us_per_launch": round(us, 2),
+                       "achieved_GBs": round(nbytes / (us * 1e-6) / 1e9, 1),
+                       "frac": round(nbytes / (us * 1e-6) / (HBM_PEAK_GBS * 1e9), 4)}
+        log("da_32k %s over %d pools: %s" % (name, P, json.dumps(modes[name])))
+        del graph, views, lists, kpool, vpool
+        torch.cuda.empty_cache()
+    res["da_32k_modes_rotated"] = dict(modes, note="n = 32769 (step 0), permuted-table lists from the device's "
+                                                   "keep mask; pools rotated so one replay attends >= 1 GiB")
+    return res
+
+
 def da_tags_rate(device, reps=2):
     """Declaration-driven DA decode at 32K (the ``da_tags_32k`` workload): per step the
     input token advances the device parser (declaration + keep mask), then the kept
@@ -980,6 +1079,8 @@ def main():
     if not args.no_other:
         res["other_workloads"] = other_workloads(device)
         log("other workloads: %s" % json.dumps(res["other_workloads"]))
+        res["config_lines"] = config_lines(device)
+        log("config lines: %s" % json.dumps(res["config_lines"]))
     if args.sweep:  # after the metric stack is freed: fresh pools, as in a process of their own
         res["view_sweep"] = view_sweep(device)
     if not args.no_cpu_baseline:
