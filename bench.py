@@ -341,11 +341,17 @@ def roofline_blocks(stack, feeder, reps, seed=11):
 
 
 def kernel_source_hash():
+    """Hash of the decode kernel's source with comments and whitespace removed, so that the
+    counter summary stays valid across comment edits and is dropped on any code change."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in ("sparse_kv_recall_amd/csrc/decode.hip", "sparse_kv_recall_amd/csrc/sk_internal.h"):
-        with open(os.path.join(ROOT, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, f)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

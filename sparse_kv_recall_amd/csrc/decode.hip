@@ -449,10 +449,11 @@ __device__ inline void load_tile(const uint8_t* kpool, const uint8_t* vpool, int
 // HAS_SEL: requests are filtered by sel[b] == sel_value (gated / per-request views).
 // Without a selector a separate instance runs, so a profile tells gated launches
 // (which exit at once on non-recall steps) apart from unconditional ones.
-// SINGLE: a launch on one request. Its plan is the same as the small-batch plan below
-// (same tiles per split, so the same work items and the same results), computed on the
-// uniform length alone: no cross-lane reductions, scans or request search, which shortens
-// the chain of instructions before the first tile is requested.
+// SINGLE: a launch on one request. Its plan is the small-batch plan below for one request
+// on the same grid (the same tiles per split, so the same work items and results as that
+// request alone in a batch on the same grid), computed on the uniform length alone: no
+// cross-lane reductions, scans or request search, which shortens the chain of
+// instructions before the first tile is requested.
 template <int MODE, bool HAS_SEL, bool SINGLE>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
   constexpr int W = kWavesPerWG;

@@ -461,3 +461,70 @@ def test_kv_append_standalone(with_sel):
     ws = ops.workspace(B, Hq)
     ops.kv_append(hc.kv, bits_to_bf16_tensor(kn), bits_to_bf16_tensor(vn), ws=ws)
     assert ops.workspace_error(ws) & 2  # SK_DEVERR_SEQ_LEN
+
+
+@pytest.mark.parametrize("view", ["full", "list"])
+def test_single_request_instance_equals_small_batch_plan(view):
+    # A launch on one request runs its own kernel instance, whose plan is the small-batch
+    # plan for that request alone on the same grid. With at least 256 blocks per request
+    # table both launches get the full grid, so the same request in a batch of two, the
+    # other request filtered out by the selector, must give the same output bits.
+    from sparse_kv_recall_amd import ops
+    Hq, Hkv = 32, 8
+    for n in (3, 2069, 9000, 40001):
+        hc = HostCache(Hq, Hkv, [n, 700], seed=95, max_blocks=2600)
+        q = _q(Hq, 2, seed=96)
+        qt = torch.as_tensor(q, device="cuda")
+        kn = bits_to_bf16_tensor(rand_bits(rng.mix_key(907, 1), 2, Hkv))
+        vn = bits_to_bf16_tensor(rand_bits(rng.mix_key(907, 2), 2, Hkv))
+        one = ops.PagedKVCache(hc.kv.num_phys_blocks, 1, Hq, Hkv, hc.max_blocks,
+                               block_tables=hc.kv.block_tables[:1].contiguous(),
+                               seq_lens=hc.kv.seq_lens[:1].contiguous(), k_pool=hc.kv.k_pool, v_pool=hc.kv.v_pool)
+        sel = torch.tensor([1, 0], dtype=torch.int32, device="cuda")
+        nb = (n + 15) // 16
+        kept = sorted(set(range(0, nb, 3)) | {nb - 1})
+        mask = torch.as_tensor(_mask_words([kept, [0]], hc.max_blocks).view(np.int32), device="cuda")
+        outs = []
+        for batch_of_two in (False, True):
+            kv = hc.kv if batch_of_two else one
+            s = sel if batch_of_two else None
+            qq = qt if batch_of_two else qt[:1].contiguous()
+            kk = kn if batch_of_two else kn[:1].contiguous()
+            vv = vn if batch_of_two else vn[:1].contiguous()
+            out = torch.zeros((kv.batch, Hq, 128), device="cuda")
+            if view == "full":
+                ops.oda_decode_full(qq, kv, kk, vv, sel=s, sel_value=1, out=out)
+            else:
+                m = mask if batch_of_two else mask[:1].contiguous()
+                ops.da_decode_blocks(qq, kv, m, kk, vv, sel=s, sel_value=1, out=out)
+            outs.append(out[0].cpu().numpy())
+            # restore the slot the commit wrote, so the second launch starts from the same history
+            ops.kv_write(hc.kv, 0, n - 1, bits_to_bf16_tensor(hc.k[0][n - 1:n]), bits_to_bf16_tensor(hc.v[0][n - 1:n]))
+        assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32)), (view, n)
+        keys = keysets.full_keys(n) if view == "full" else keysets.block_keys(n, kept)
+        k, v = hc.k[0].copy(), hc.v[0].copy()
+        oracle.oda.commit(k, v, n, bf16_tensor_to_bits(kn)[0], bf16_tensor_to_bits(vn)[0])
+        ref = attention.attend(q[0], k, v, keys, SCALE)
+        check_tight(outs[0], ref, q[0], k, v, keys, SCALE, what="%s n=%d" % (view, n))
+
+
+def test_single_request_local_view_commit_tile_alone():
+    # At one request the Local view's last split can hold only the tile that receives the
+    # current token, which its wave then takes from its first request: lengths that put 0,
+    # 1 and 2 window positions in the last block, with the commit checked bit for bit
+    from sparse_kv_recall_amd import ops
+    Hq, Hkv = 32, 8
+    for n in (2069, 2070, 2084, 4097, 4112):
+        hc = HostCache(Hq, Hkv, [n], seed=97)
+        q = _q(Hq, 1, seed=98)
+        kn = rand_bits(rng.mix_key(908, n, 1), 1, Hkv)
+        vn = rand_bits(rng.mix_key(908, n, 2), 1, Hkv)
+        out = ops.oda_decode_local(torch.as_tensor(q, device="cuda"), hc.kv, bits_to_bf16_tensor(kn),
+                                   bits_to_bf16_tensor(vn)).cpu().numpy()
+        k, v = hc.k[0].copy(), hc.v[0].copy()
+        oracle.oda.commit(k, v, n, kn[0], vn[0])
+        keys = keysets.local_keys(n)
+        ref = attention.attend(q[0], k, v, keys, SCALE)
+        check_tight(out[0], ref, q[0], k, v, keys, SCALE, what="local n=%d" % n)
+        kr, vr = ops.kv_read(hc.kv, 0, n - 1, 1)
+        assert np.array_equal(bf16_tensor_to_bits(kr)[0], kn[0]) and np.array_equal(bf16_tensor_to_bits(vr)[0], vn[0])
