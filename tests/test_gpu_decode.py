@@ -528,3 +528,37 @@ def test_single_request_local_view_commit_tile_alone():
         check_tight(out[0], ref, q[0], k, v, keys, SCALE, what="local n=%d" % n)
         kr, vr = ops.kv_read(hc.kv, 0, n - 1, 1)
         assert np.array_equal(bf16_tensor_to_bits(kr)[0], kn[0]) and np.array_equal(bf16_tensor_to_bits(vr)[0], vn[0])
+
+
+def test_single_request_invalid_length_and_empty_list():
+    # the single-request instance's own handling of a request it cannot attend: a length of
+    # 0 or past the block table sets SK_DEVERR_SEQ_LEN and zeroes the row; an empty
+    # gathered list sets SK_DEVERR_EMPTY, zeroes the row and still commits the token
+    from sparse_kv_recall_amd import ops
+    Hq, Hkv = 32, 8
+    hc = HostCache(Hq, Hkv, [300], seed=99)
+    q = torch.as_tensor(_q(Hq, 1, seed=100), device="cuda")
+    for bad_n in (0, hc.max_blocks * 16 + 1):
+        hc.set_lens([bad_n])
+        for call in ("full", "local"):
+            ws = ops.workspace(1, Hq)
+            out = torch.full((1, Hq, 128), 5.0, device="cuda")
+            if call == "full":
+                ops.oda_decode_full(q, hc.kv, out=out, ws=ws)
+            else:
+                ops.oda_decode_local(q, hc.kv, out=out, ws=ws)
+            assert ops.workspace_error(ws) & 2, (bad_n, call)
+            assert not out.cpu().numpy().any(), (bad_n, call)
+    hc.set_lens([300])
+    kn = rand_bits(rng.mix_key(909, 1), 1, Hkv)
+    vn = rand_bits(rng.mix_key(909, 2), 1, Hkv)
+    gat = torch.zeros((1, hc.max_blocks), dtype=torch.int32, device="cuda")
+    cnt = torch.zeros_like(gat)
+    num = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ws = ops.workspace(1, Hq)
+    out = torch.full((1, Hq, 128), 5.0, device="cuda")
+    ops.da_decode_gathered(q, hc.kv, gat, cnt, num, bits_to_bf16_tensor(kn), bits_to_bf16_tensor(vn), out=out, ws=ws)
+    assert ops.workspace_error(ws) & 4  # SK_DEVERR_EMPTY
+    assert not out.cpu().numpy().any()
+    kr, vr = ops.kv_read(hc.kv, 0, 299, 1)
+    assert np.array_equal(bf16_tensor_to_bits(kr)[0], kn[0]) and np.array_equal(bf16_tensor_to_bits(vr)[0], vn[0])
