@@ -78,20 +78,35 @@ __device__ inline float dot8(u32x4 w, const float* xs) {
   return s;
 }
 
-// Stage the prologue's input vector (cols floats) in LDS.
-template <int PRO>
-__device__ inline void stage_input(const float* __restrict__ x, const uint16_t* __restrict__ gamma, float eps,
-                                   int cols, float* xs, float* red) {
+// The thread's share of the input vector (cols = 512 J floats, 512 threads): elements
+// t + 512 j, j < J, and their RMSNorm gains. Requested before the weights, so that the
+// wait for them leaves the weight loads in flight: the loads of a wave complete in issue
+// order, and a staging loop issued after the weights would wait for them on every
+// iteration.
+template <int J, int PRO>
+__device__ inline void load_input(const float* __restrict__ x, const uint16_t* __restrict__ gamma, float (&xv)[J],
+                                  float (&gv)[J]) {
+#pragma unroll
+  for (int j = 0; j < J; ++j) xv[j] = x[threadIdx.x + 512 * j];
+  if (PRO == SK_PRO_RMSNORM) {
+#pragma unroll
+    for (int j = 0; j < J; ++j) gv[j] = bf16f(gamma[threadIdx.x + 512 * j]);
+  }
+}
+
+// Stage the prologue's input vector in LDS (RMSNorm over all cols values when PRO asks).
+template <int J, int PRO>
+__device__ inline void stage_input(const float (&xv)[J], const float (&gv)[J], float eps, float* xs, float* red) {
   if (PRO == SK_PRO_RMSNORM) {
     float ss = 0.f;
-    for (int i = threadIdx.x; i < cols; i += blockDim.x) {
-      const float v = x[i];
-      ss = fmaf(v, v, ss);
-    }
-    const float r = 1.f / sqrtf(block_sum(ss, red) / float(cols) + eps);
-    for (int i = threadIdx.x; i < cols; i += blockDim.x) xs[i] = x[i] * r * bf16f(gamma[i]);
+#pragma unroll
+    for (int j = 0; j < J; ++j) ss = fmaf(xv[j], xv[j], ss);
+    const float r = 1.f / sqrtf(block_sum(ss, red) / float(512 * J) + eps);
+#pragma unroll
+    for (int j = 0; j < J; ++j) xs[threadIdx.x + 512 * j] = xv[j] * r * gv[j];
   } else {
-    for (int i = threadIdx.x; i < cols; i += blockDim.x) xs[i] = x[i];
+#pragma unroll
+    for (int j = 0; j < J; ++j) xs[threadIdx.x + 512 * j] = xv[j];
   }
   __syncthreads();
 }
@@ -120,6 +135,16 @@ __device__ inline void load_row(const uint16_t* W, int row, int cols, bool ok, i
     w[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, 16 * (lane + 64 * j), 0, kNonTemporal));
 }
 
+// residual[row], or 0 when there is no residual or no row: one unconditional load through
+// a buffer range that is empty in those cases (no memory access), so that the number of
+// loads in flight, which the waits count, does not depend on a branch.
+__device__ inline float load_residual(const float* residual, int rows, int row, bool ok) {
+  const int bytes = residual ? rows * 4 : 0;
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(residual), 0, bytes, kBufferFlags);
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, ok ? row * 4 : bytes, 0, 0));
+}
+
 template <int J>
 __device__ inline float row_dot(const u32x4 (&w)[J], const float* xs, int lane) {
   float acc = 0.f;
@@ -146,39 +171,44 @@ __global__ __launch_bounds__(64 * kGemvWaves) void gemv_kernel(const uint16_t* _
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int G = int(gridDim.x) * kGemvWaves;
   int it = int(blockIdx.x) * kGemvWaves + wave;
+  float xv[J], gv[J];
+  load_input<J, PRO>(x, gamma, xv, gv);
   u32x4 b0[NR][J], b1[NR][J];  // b1 is only used (and allocated) with the ring
-  auto fetch = [&](u32x4 (&b)[NR][J], int item) {
+  float r0 = 0.f, r1 = 0.f;     // the residuals of the rows in b0 / b1
+  // A row's weights and its residual are requested together.
+  auto fetch = [&](u32x4 (&b)[NR][J], float& res, int item) {
     const bool ok = item < rows;
     const int r = ok ? item : 0;
 #pragma unroll
     for (int k = 0; k < NR; ++k) load_row<J>(W, r + k * rows, cols, ok, lane, b[k]);
+    if (EPI != SK_EPI_SWIGLU) res = load_residual(residual, rows, r, ok);
   };
-  auto finish = [&](u32x4 (&b)[NR][J], int item) {
+  auto finish = [&](u32x4 (&b)[NR][J], float res, int item) {
     const float a0 = row_dot<J>(b[0], xs, lane);
     float v;
     if (EPI == SK_EPI_SWIGLU) {
       const float a1 = row_dot<J>(b[NR - 1], xs, lane);
       v = a0 / (1.f + expf(-a0)) * a1;
     } else {
-      v = a0 + (residual ? residual[item] : 0.f);
+      v = a0 + res;
     }
     if (lane == 0) y[item] = v;
   };
-  fetch(b0, it);
-  stage_input<PRO>(x, gamma, eps, cols, xs, red);
+  fetch(b0, r0, it);
+  stage_input<J, PRO>(xv, gv, eps, xs, red);
   if constexpr (kRing) {
     for (; it + G < rows; it += 2 * G) {
-      fetch(b1, it + G);
-      finish(b0, it);
-      fetch(b0, it + 2 * G);
-      finish(b1, it + G);
+      fetch(b1, r1, it + G);
+      finish(b0, r0, it);
+      fetch(b0, r0, it + 2 * G);
+      finish(b1, r1, it + G);
     }
-    if (it < rows) finish(b0, it);
+    if (it < rows) finish(b0, r0, it);
   } else {  // wide rows: one row (pair) in flight per wave, the other waves overlap it
-    finish(b0, it);
+    finish(b0, r0, it);
     for (it += G; it < rows; it += G) {
-      fetch(b0, it);
-      finish(b0, it);
+      fetch(b0, r0, it);
+      finish(b0, r0, it);
     }
   }
 }
