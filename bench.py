@@ -72,6 +72,52 @@ def capture_step(stack, feeder):
     return capture_graph(step)
 
 
+def host_routed_rate(stack, feeder, wl, steps, warmup):
+    """The metric workload's first `steps` steps again with the recall branch taken on the
+    host: graph 1 (feed, Local pass, gate), a 4-byte readback of the gate, and graph 2 (the
+    36 gated Full launches) replayed only on recall steps. Same launches and results as the
+    one-graph step; the skipped launches cost no graph nodes, each step pays one host round
+    trip instead. Weighted 1 : 7 like the metric."""
+    import numpy as np
+    import torch
+    from sparse_kv_recall_amd.stack import HostRoutedStep
+
+    q, k, v = feeder.q, feeder.k, feeder.v
+
+    def first():
+        feeder.step()
+        stack.local_pass(q[:, 0, :], k[:, 0, :], v[:, 0, :])
+        stack.gate_from_scores(feeder.scores, 0.0)
+
+    def recall():
+        stack.full_pass(q[:, 1, :], k[:, 1, :], v[:, 1, :], gated=True)
+
+    step = HostRoutedStep(first, recall, stack.gate)
+    feeder.set_step(0)
+    for _ in range(warmup):
+        step.replay()
+    feeder.set_step(0)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ran = np.zeros(steps, bool)
+    wall0 = time.perf_counter()
+    ev[0].record()
+    for i in range(steps):
+        ran[i] = step.replay()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    per_step = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)])
+    rec = wl.sched_scores[:steps, 0] > 0
+    assert np.array_equal(ran, rec), "host routing disagrees with the schedule"
+    ms_rec, ms_non = float(per_step[rec].mean()), float(per_step[~rec].mean())
+    ms = (ms_rec + (RECALL_PERIOD - 1) * ms_non) / RECALL_PERIOD
+    del step
+    return {"tok_s": round(wl.batch / (ms / 1e3), 2), "ms_per_step": round(ms, 4), "recall_step_ms": round(ms_rec, 4),
+            "other_step_ms": round(ms_non, 4), "steps": steps, "recall_steps": int(rec.sum()),
+            "wall_ms_per_step": round(wall * 1e3 / steps, 4)}
+
+
 def roofline_full(stack, feeder, reps):
     """Average duration of the Full-view kernel over all layers at the current n, with HIP
     events on the launching stream; every launch runs (no gate)."""
@@ -821,7 +867,7 @@ def decoder_rates(device, contexts=(4096, 131072), steps=64, recalls=8):
     import torch
     from sparse_kv_recall_amd import ops
     from sparse_kv_recall_amd.model import DecoderShape, ODADecoder
-    from sparse_kv_recall_amd.stack import capture_graph
+    from sparse_kv_recall_amd.stack import HostRoutedStep, capture_graph
     from synth import device as sdev
     from synth.decoder import decoder_qwen3_1_7b
     from synth.workloads import np_rng
@@ -865,9 +911,29 @@ def decoder_rates(device, contexts=(4096, 131072), steps=64, recalls=8):
             feed()
             model.always_full_step()
 
+        def oda_first():
+            feed()
+            model.local_pass()
+            model.recall_gate(0.0)
+            ops.oda_gate_scores(score, 0.0, out=model.gate)
+
+        def oda_recall():
+            model.recall_pass(gated=True)
+            oda_select()
+
+        def oda_select():
+            ops.select(model.gate, model.final_full, model.h_local_final, model.h_prev)
+
         res = {}
-        for name, fn in (("oda", oda_step), ("always_full", full_step)):
-            graph = capture_graph(fn)
+        for name, fn in (("oda", oda_step), ("always_full", full_step), ("oda_host_routed", None)):
+            if fn is None:
+                graph = HostRoutedStep(oda_first, oda_recall, model.gate, skip=oda_select)
+            else:
+                graph = capture_graph(fn)
+            seq.fill_(H0)
+            t_idx.zero_()
+            for _ in range(4):  # warm replays, then back to step 0
+                graph.replay()
             seq.fill_(H0)
             t_idx.zero_()
             torch.cuda.synchronize()
@@ -883,6 +949,9 @@ def decoder_rates(device, contexts=(4096, 131072), steps=64, recalls=8):
                               "always_full_ms_per_step": round(res["always_full"], 4),
                               "always_full_tok_s": round(1e3 / res["always_full"], 2),
                               "oda_speedup": round(res["always_full"] / res["oda"], 3),
+                              "host_routed_oda_ms_per_step": round(res["oda_host_routed"], 4),
+                              "host_routed_oda_tok_s": round(1e3 / res["oda_host_routed"], 2),
+                              "host_routed_oda_speedup": round(res["always_full"] / res["oda_host_routed"], 3),
                               "recall_steps": recalls, "steps": steps}
         del model, caches
         torch.cuda.empty_cache()
@@ -1003,6 +1072,8 @@ def main():
                                   ("keep_12.5pct_positions", blocks["keep_12.5pct"]["kept_positions"] * wl.Hkv * 512),
                                   ("full_n", n_now * wl.Hkv * 512)])
     log("size-matched streaming reference: %s" % json.dumps(floor))
+    host_routed = host_routed_rate(stack, feeder, wl, args.steps, min(args.warmup, 8))
+    log("host-routed recall branch: %s" % json.dumps(host_routed))
     full_only = always_full_rate(stack, feeder, wl, min(64, args.steps))
     log("always-Full baseline: %s" % json.dumps(full_only))
     hybrid = hybrid_rate(stack, feeder, wl, min(256, args.steps))
@@ -1074,6 +1145,10 @@ def main():
                      "gated_off_us_per_nonrecall_step": round(gated_off_ms * 1e3 * wl.layers, 1),
                      "note": "one feed, 36 Local, the gate and 36 gated Full launches per step; on a "
                              "non-recall step the Full launches exit at once but each still costs a graph node"},
+        "host_routed": dict(host_routed, note="the same step as two graphs split at the gate: the host reads the "
+                                              "gate back and replays the 36 Full launches only on recall steps "
+                                              "(no graph nodes for skipped launches; one host round trip per "
+                                              "step)"),
         "hybrid_local_only": hybrid,
         "da_declared_step": da_tags,
         "whole_model_decode": whole_model,

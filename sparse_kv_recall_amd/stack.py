@@ -9,6 +9,13 @@ ODA step (On-Demand Attention summary page, "Approach"; Figure 1 caption):
 The step never reads the gate on the host, so it can be captured once as a HIP
 graph and replayed ("Developer perspective": one GPU execution flow).
 
+Host-routed form (HostRoutedStep): the same launches in two graphs, split at the gate.
+The host reads the gate back (4 bytes per request) and replays the recall-pass graph only
+when some request is selected. Its launches still carry the device gate as their
+selector, so the results are those of the one-graph step. Without a conditional graph
+node, every skipped launch of the one-graph step still costs a graph node, and the
+readback costs one host round trip per step instead.
+
 Per-layer access control ("Developer perspective", the note on hybrid backbones: the
 runtime may restrict chosen layers to the Local range): a layer marked local-only runs
 its Local view in step 3 as well, under the same gate, so it never reads beyond the
@@ -23,6 +30,7 @@ This module only sequences library calls; it computes nothing itself.
 
 import math
 
+import numpy as np
 import torch
 
 from . import ops
@@ -167,6 +175,38 @@ class DATagStep(DAStep):
             return
         ops.da_decode_blocks(q, self.cache, self.mask, k, v, self.scale, out=self.out, gathered=self.gathered,
                              gathered_cnt=self.gathered_cnt, num_kept=self.num_kept, ws=self.ws)
+
+
+class HostRoutedStep:
+    """One decode step as graphs with the recall branch taken on the host.
+
+    first: the launches up to and including the gate (feed, Local pass, gate);
+    recall: the gated recall pass (and whatever follows it on a recall step);
+    skip: optional launches that replace `recall` on a step without a recall.
+    gate: the int32 gate tensor that `first` writes, one entry per request.
+    replay() returns whether the recall graph ran.
+    """
+
+    def __init__(self, first, recall, gate, skip=None):
+        self.first = capture_graph(first)
+        self.recall = capture_graph(recall)
+        self.skip = capture_graph(skip) if skip is not None else None
+        self.gate = gate
+        self.host_gate = torch.zeros(gate.numel(), dtype=torch.int32, pin_memory=True)
+        self.host_view = self.host_gate.numpy()
+        self.read = torch.cuda.Event()
+
+    def replay(self):
+        self.first.replay()
+        self.host_gate.copy_(self.gate, non_blocking=True)
+        self.read.record()
+        self.read.synchronize()
+        recalled = bool(np.any(self.host_view))
+        if recalled:
+            self.recall.replay()
+        elif self.skip is not None:
+            self.skip.replay()
+        return recalled
 
 
 def capture_graph(fn):

@@ -21,7 +21,7 @@ import torch
 import oracle
 from oracle import attention, gather, keysets
 from sparse_kv_recall_amd import ops
-from sparse_kv_recall_amd.stack import DAStep, ODAStack, RaggedBatch, capture_graph
+from sparse_kv_recall_amd.stack import DAStep, HostRoutedStep, ODAStack, RaggedBatch, capture_graph
 from synth import device as sdev
 from synth import rng
 from synth.workloads import C_KHIST, C_VHIST
@@ -69,7 +69,8 @@ class OdaStackRun:
     """ODA stack (Local every step, on-device gate, gated Full) with host mirrors of
     ``check_layers``."""
 
-    def __init__(self, wl, check_layers, steps=None, use_graph=True, local_only=(), same_candidates=False):
+    def __init__(self, wl, check_layers, steps=None, use_graph=True, local_only=(), same_candidates=False,
+                 host_routed=False):
         self.wl = wl
         self.steps = wl.steps if steps is None else steps
         self.check_layers = list(check_layers)
@@ -93,9 +94,12 @@ class OdaStackRun:
             self.host_w = (W1, b1, w2, b2)
             self.dev_w = tuple(torch.as_tensor(a, device="cuda") for a in (W1, b1, w2, b2))
         self.mirror = {l: _mirror(wl, l, H0, self.steps) for l in self.check_layers}
-        self.graph = capture_graph(self._step) if use_graph else None
+        if host_routed:  # two graphs, the recall pass replayed on the host's reading of the gate
+            self.graph = HostRoutedStep(self._first, self._recall, self.stack.gate)
+        else:
+            self.graph = capture_graph(self._step) if use_graph else None
 
-    def _step(self):
+    def _first(self):
         f, s = self.feeder, self.stack
         f.step()
         s.local_pass(f.q[:, 0], f.k[:, 0], f.v[:, 0])
@@ -103,8 +107,14 @@ class OdaStackRun:
             s.gate_from_recall_head(f.x, *self.dev_w, theta=self.wl.theta)
         else:
             s.gate_from_scores(f.scores, self.wl.theta)
-        p = self.rpass
-        s.full_pass(f.q[:, p], f.k[:, p], f.v[:, p], gated=True)
+
+    def _recall(self):
+        f, p = self.feeder, self.rpass
+        self.stack.full_pass(f.q[:, p], f.k[:, p], f.v[:, p], gated=True)
+
+    def _step(self):
+        self._first()
+        self._recall()
 
     def run(self, full_check_steps=None, check_feed_steps=(0,), commit_all_layers=False):
         """full_check_steps: recall steps whose Full outputs are checked (None: all);
@@ -115,14 +125,13 @@ class OdaStackRun:
         H0 = int(wl.H0[0])
         gates = []
         for t in range(self.steps):
-            if self.graph is not None:
-                self.graph.replay()
-            else:
-                self._step()
+            ran = self.graph.replay() if self.graph is not None else self._step()
             torch.cuda.synchronize()
             n = H0 + t + 1
             assert int(self.stack.seq_lens[0].item()) == n
             gpu_gate = int(self.stack.gate[0].item())
+            if isinstance(self.graph, HostRoutedStep):  # the recall graph ran exactly on gated steps
+                assert ran == bool(gpu_gate), (t, ran, gpu_gate)
             if t in check_feed_steps:  # the device feed reproduces the host streams bit for bit
                 for l in self.check_layers:
                     assert np.array_equal(self.feeder.q[l, 1, 0].cpu().numpy(), wl.cand_q(t, l, 1, 0))

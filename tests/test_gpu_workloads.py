@@ -106,3 +106,44 @@ def test_da_tag_stream_every_step(in_kernel_rewrite):
     rep = DaTagsRun(wl, in_kernel_rewrite=in_kernel_rewrite).run()
     assert rep.checked_outputs == 512 and rep.recalls > 0
     print("da_tags_32k: focus steps %d/512, max-abs %.2e, row-rel %.2e" % (rep.recalls, rep.max_abs, rep.max_row_rel))
+
+
+def test_oda_stack16k_host_routed():
+    # the step as two graphs with the recall branch taken on the host: the recall-head
+    # workload checked like the one-graph step, and the recall graph replayed only on the
+    # steps whose device gate is set
+    from tests.harness import OdaStackRun
+    wl = workloads.oda_stack16k(steps=48)
+    rep = OdaStackRun(wl, check_layers=[0, 13, 27], host_routed=True).run(commit_all_layers=True)
+    assert rep.decisions == 48 and 0 < rep.recalls < 48
+    print("host-routed 16K: recalls %d/48, max-abs %.2e, row-rel %.2e" % (rep.recalls, rep.max_abs, rep.max_row_rel))
+
+
+def test_host_routed_equals_one_graph_step():
+    # same launches, same order: per-step outputs and the committed slots are bit-identical
+    import torch
+    from sparse_kv_recall_amd import ops
+    from tests.harness import OdaStackRun
+    wl = workloads.oda_stack16k(steps=24, layers=4)
+    runs = [OdaStackRun(wl, check_layers=[], host_routed=h) for h in (False, True)]
+    outs = [[], []]
+    for i, r in enumerate(runs):
+        for t in range(wl.steps):
+            r.graph.replay()
+            torch.cuda.synchronize()
+            outs[i].append((r.stack.out.clone(), r.stack.out_full.clone() if r.stack.gate[0].item() else None))
+    recalls = 0
+    for t in range(wl.steps):
+        (a, af), (b, bf) = outs[0][t], outs[1][t]
+        assert torch.equal(a, b), t
+        assert (af is None) == (bf is None), t
+        if af is not None:
+            assert torch.equal(af, bf), t
+            recalls += 1
+    assert 0 < recalls < wl.steps
+    H0 = int(wl.H0[0])
+    for l in range(wl.layers):
+        ka, va = ops.kv_read(runs[0].stack.caches[l], 0, H0, wl.steps)
+        kb, vb = ops.kv_read(runs[1].stack.caches[l], 0, H0, wl.steps)
+        assert torch.equal(ka.view(torch.int16), kb.view(torch.int16)) and torch.equal(va.view(torch.int16),
+                                                                                        vb.view(torch.int16)), l
