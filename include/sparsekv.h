@@ -181,6 +181,29 @@ int oda_decode_full(const float* q, sk_paged_kv kv, const void* k_new, const voi
                     float scale, const int32_t* sel, int32_t sel_value,
                     float* out, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* Local and Full views of one decoder layer straight from its raw q/k/v
+ * projection ([ODA] "Approach": both passes run the layer's attention; the layer
+ * is the Qwen3-family layer the pages name as backbone): the per-head finish that
+ * sk_qkv_rope does in a launch of its own is applied while the decode kernel
+ * stages its operands.
+ *  qkv  : fp32 [batch][Hq + 2 Hkv][128], the projection W_qkv x per request
+ *         (q heads, then k heads, then v heads), e.g. sk_gemv's output
+ *  g_q, g_k : bf16 [128] RMSNorm gains of the q and k heads;  eps >= 0
+ *  rope_base > 0 : each q and k head, RMS-normalised over its 128 values with
+ *         its gains, is rotated at pos = n - 1 (rotate-half pairs (i, i + 64),
+ *         angle pos * rope_base^(-i/64), computed and reduced in fp64)
+ * The finished k and the raw v, rounded to bf16 (nearest even), are the current
+ * token's candidate: committed to position n - 1 as k_new / v_new are. Other
+ * arguments, the selector and errors as oda_decode_local / oda_decode_full. */
+int oda_decode_local_qkv(const float* qkv, const uint16_t* g_q, const uint16_t* g_k, float eps,
+                         float rope_base, sk_paged_kv kv, int32_t sinks, int32_t window, float scale,
+                         const int32_t* sel, int32_t sel_value,
+                         float* out, void* ws, size_t ws_bytes, hipStream_t stream);
+int oda_decode_full_qkv(const float* qkv, const uint16_t* g_q, const uint16_t* g_k, float eps,
+                        float rope_base, sk_paged_kv kv, float scale,
+                        const int32_t* sel, int32_t sel_value,
+                        float* out, void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* Allocation-free form of oda_decode_full, for callers that cannot allocate or
  * pass a workspace (code under graph capture that may not call hipMalloc, tight
  * serving loops, harnesses that forbid allocation). Same computation, kernels and

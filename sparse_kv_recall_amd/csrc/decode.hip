@@ -49,6 +49,8 @@ constexpr int kMergeBatch = 48;                     // split accumulators loaded
 constexpr int kViewRounds = 4;
 constexpr float kLog2e = 1.4426950408889634f;
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
 struct DecodeParams {
   const float* q;
   sk_paged_kv kv;
@@ -68,6 +70,15 @@ struct DecodeParams {
   float qscale;
   const int32_t* decl;  // declared view: {mode, focus_begin, focus_end, output_begin} per request
   int local_tokens;
+  // Decoding from a layer's raw q/k/v projection (the kernel's QK instances): q holds
+  // [B][Hq + 2 Hkv][128] fp32 rows (q heads, then k heads, then v heads); q and k heads
+  // are RMS-normalised over their 128 values with gains g_q / g_k and rotated to position
+  // n - 1 (pairs (i, i + 64), angle (n - 1) base^(-i/64)) before use; the current token's
+  // k and v are rounded to bf16 for the commit.
+  const uint16_t* g_q;
+  const uint16_t* g_k;
+  float qk_eps;
+  float rope_base;
 };
 
 struct Tile {
@@ -416,6 +427,84 @@ __device__ inline void commit_from_lds(const DecodeParams& P, const uint32_t* s_
   }
 }
 
+// QK instances: the layer's per-head q/k RMSNorm and rotary positions, applied while
+// the q operands and the current token are staged. Every wave of the workgroup calls it
+// (it holds a barrier). Wave 4, idle here otherwise, computes the 64 rotary (cos, sin)
+// pairs of position n - 1 into LDS (angle in fp64, reduced to [-pi, pi] before its sine
+// and cosine). Waves 0-3 hold the raw values of dims d0 .. d0 + 7 of q head qcol and
+// publish them with their wave's share of the head's sum of squares; after the barrier
+// each lane normalises its values and their rotary partners (dims d ^ 64, held by wave
+// qc ^ 2), applies the gains and rotates. Waves 0 and 1 of the split that commits turn
+// the raw k row (normalised within the wave, partner dims in lane ^ 32, rotated) and the
+// raw v row into the bf16 words of s_new (word l: dims 2 l, 2 l + 1).
+__device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+__device__ inline uint32_t bf16_bits(float x) { return __builtin_bit_cast(uint16_t, __bf16(x)); }
+
+__device__ inline void qk_finish_staged(const DecodeParams& P, int n, int wave, int lane, int qc, int qcol, int d0,
+                                        int G, float (&xq)[8], const u32x4& gq, const u32x4& gqp, bool commits,
+                                        f32x2 tok, uint32_t gk, float* scratch, uint32_t* s_new) {
+  float* s_raw = scratch;                  // [G][128] raw q rows
+  float* s_part = scratch + G * kHeadDim;  // [4][16] each wave's share of the heads' sums of squares
+  float* s_rope = s_part + 64;             // [64] (cos, sin)
+  if (wave == 4) {
+    const double ang = double(n - 1) * exp2(-double(lane) / 64.0 * log2(double(P.rope_base)));
+    const double red = ang - 6.283185307179586 * rint(ang * 0.15915494309189535);
+    double sd, cd;
+    sincos(red, &sd, &cd);
+    s_rope[2 * lane] = float(cd);
+    s_rope[2 * lane + 1] = float(sd);
+  }
+  if (wave < 4) {
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss = fmaf(xq[e], xq[e], ss);
+    ss = rows_sum(ss);  // the wave's 32 dims of head qcol
+    if (qcol < G) {
+      *reinterpret_cast<f32x4*>(s_raw + qcol * kHeadDim + d0) = f32x4{xq[0], xq[1], xq[2], xq[3]};
+      *reinterpret_cast<f32x4*>(s_raw + qcol * kHeadDim + d0 + 4) = f32x4{xq[4], xq[5], xq[6], xq[7]};
+      if (lane < 16) s_part[qc * 16 + qcol] = ss;
+    }
+  }
+  __syncthreads();
+  if (wave < 4 && qcol < G) {
+    const float tot = ((s_part[qcol] + s_part[16 + qcol]) + s_part[32 + qcol]) + s_part[48 + qcol];
+    const float r = 1.f / sqrtf(tot / float(kHeadDim) + P.qk_eps);
+    const f32x4 pa = *reinterpret_cast<const f32x4*>(s_raw + qcol * kHeadDim + (d0 ^ 64));
+    const f32x4 pb = *reinterpret_cast<const f32x4*>(s_raw + qcol * kHeadDim + (d0 ^ 64) + 4);
+    const float xp[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
+    const uint32_t g8[4] = {gq.x, gq.y, gq.z, gq.w}, gp8[4] = {gqp.x, gqp.y, gqp.z, gqp.w};
+    const int i0 = d0 & 63;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float c = s_rope[2 * (i0 + e)], sn = s_rope[2 * (i0 + e) + 1];
+      const float v = xq[e] * r * ((e & 1) ? bf16_hi(g8[e >> 1]) : bf16_lo(g8[e >> 1]));
+      const float vp = xp[e] * r * ((e & 1) ? bf16_hi(gp8[e >> 1]) : bf16_lo(gp8[e >> 1]));
+      xq[e] = (d0 < 64) ? v * c - vp * sn : v * c + vp * sn;
+    }
+  }
+  if (commits && wave < 2) {
+    float o0 = tok.x, o1 = tok.y;
+    if (wave == 0) {
+      float ss = fmaf(tok.x, tok.x, tok.y * tok.y);
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) ss += __shfl_xor(ss, o);  // same total in every lane
+      const float r = 1.f / sqrtf(ss / float(kHeadDim) + P.qk_eps);
+      const float v0 = tok.x * r * bf16_lo(gk), v1 = tok.y * r * bf16_hi(gk);
+      float a, b;
+      partner<true>(v0, a, b);
+      const float p0 = (lane < 32) ? b : a;
+      partner<true>(v1, a, b);
+      const float p1 = (lane < 32) ? b : a;
+      const int i0 = (2 * lane) & 63;
+      const float c0 = s_rope[2 * i0], s0 = s_rope[2 * i0 + 1], c1 = s_rope[2 * i0 + 2], s1 = s_rope[2 * i0 + 3];
+      o0 = (lane < 32) ? v0 * c0 - p0 * s0 : v0 * c0 + p0 * s0;
+      o1 = (lane < 32) ? v1 * c1 - p1 * s1 : v1 * c1 + p1 * s1;
+    }
+    s_new[wave * 64 + lane] = bf16_bits(o0) | (bf16_bits(o1) << 16);
+  }
+}
+
 // Zero the V halves of tokens outside [lo, hi) so that 0-weight tokens cannot bring in
 // non-finite garbage (0 * NaN) through the PV product.
 __device__ inline void mask_v(u32x4 (&vr)[4], int lo, int hi, int grp) {
@@ -454,7 +543,7 @@ __device__ inline void load_tile(const uint8_t* kpool, const uint8_t* vpool, int
 // request alone in a batch on the same grid), computed on the uniform length alone: no
 // cross-lane reductions, scans or request search, which shortens the chain of
 // instructions before the first tile is requested.
-template <int MODE, bool HAS_SEL, bool SINGLE>
+template <int MODE, bool HAS_SEL, bool SINGLE, bool QK = false>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
   constexpr int W = kWavesPerWG;
   extern __shared__ float smem[];
@@ -730,17 +819,24 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
     // nothing here, so the workgroup's first round of loads stays small. Lanes past the G
     // heads read head 0 (and stage zeros).
     const int qc = wave & 3, qcol = lane & 15, qgrp = lane >> 4;
-    const float* qrow = P.q + (int64_t(b) * Hq + g * G + (qcol < G ? qcol : 0)) * kHeadDim + 8 * (4 * qc + qgrp);
+    const int q_rows = QK ? Hq + 2 * Hkv : Hq;  // rows of one request in P.q
+    const int d0 = 8 * (4 * qc + qgrp);         // this lane's first q dim
+    const float* qrow = P.q + (int64_t(b) * q_rows + g * G + (qcol < G ? qcol : 0)) * kHeadDim + d0;
     f32x4 qa0 = {0.f, 0.f, 0.f, 0.f}, qa1 = {0.f, 0.f, 0.f, 0.f};
+    u32x4 gq = {0u, 0u, 0u, 0u}, gqp = {0u, 0u, 0u, 0u};  // QK: gains of dims d0.. and of their partners
     if (wave < 4) {
       qa0 = *reinterpret_cast<const f32x4*>(qrow);
       qa1 = *reinterpret_cast<const f32x4*>(qrow + 4);
+      if (QK) {
+        gq = *reinterpret_cast<const u32x4*>(P.g_q + d0);
+        gqp = *reinterpret_cast<const u32x4*>(P.g_q + (d0 ^ 64));
+      }
     }
 
     // which tile receives the current token (-1: none attended here)
     int commit_tile = -1;
     const int tl = (n - 1) % kBlock;
-    if (P.k_new) {
+    if (QK || P.k_new) {
       const int m = (MODE == kViews) ? view : MODE;
       if (m == kFull || m == kLocal) {
         commit_tile = tiles_b - 1;
@@ -768,8 +864,18 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
     // loads below are waited for before the first tile is requested), so it costs no
     // wait-count precision
     uint32_t tok_word = 0u;
-    if (split_commits && wave < 2)
-      tok_word = reinterpret_cast<const uint32_t*>((wave ? P.v_new : P.k_new) + (int64_t(b) * Hkv + g) * kHeadDim)[lane];
+    f32x2 tok_raw = {0.f, 0.f};  // QK: dims 2 lane, 2 lane + 1 of the projection's k (wave 0) or v (wave 1) row
+    uint32_t gk = 0u;            // QK: their k gains
+    if (split_commits && wave < 2) {
+      if (QK) {
+        const float* row = P.q + (int64_t(b) * q_rows + Hq + wave * Hkv + g) * kHeadDim;
+        tok_raw = reinterpret_cast<const f32x2*>(row)[lane];
+        if (wave == 0) gk = reinterpret_cast<const uint32_t*>(P.g_k)[lane];
+      } else {
+        tok_word =
+            reinterpret_cast<const uint32_t*>((wave ? P.v_new : P.k_new) + (int64_t(b) * Hkv + g) * kHeadDim)[lane];
+      }
+    }
 
     // q -> MFMA B operands (hi and lo bf16 parts), staged in LDS: entry (c, part, lane) holds
     // dims 8*(4c + lane/16) .. +7 of head lane%16. The wave's first tile is requested
@@ -777,7 +883,14 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
     // requests block 0 of the pool and never uses it, so the request needs no branch.
     u32x4 k0[4], v0[4], k1[4], v1[4];
     load_tile(kpool, vpool, __builtin_amdgcn_readfirstlane(dphys), g, Hkv, lane, k0, v0);
-    if (split_commits && tid < 128) s_new[tid] = tok_word;
+    if (QK) {
+      float xq[8] = {qa0.x, qa0.y, qa0.z, qa0.w, qa1.x, qa1.y, qa1.z, qa1.w};
+      qk_finish_staged(P, n, wave, lane, qc, qcol, d0, G, xq, gq, gqp, split_commits, tok_raw, gk, s_acc, s_new);
+      qa0 = f32x4{xq[0], xq[1], xq[2], xq[3]};
+      qa1 = f32x4{xq[4], xq[5], xq[6], xq[7]};
+    } else if (split_commits && tid < 128) {
+      s_new[tid] = tok_word;
+    }
     if (wave < 4) {
       const float x[8] = {qa0.x, qa0.y, qa0.z, qa0.w, qa1.x, qa1.y, qa1.z, qa1.w};
       bf16x8 oh, ol;
@@ -1055,11 +1168,28 @@ int check_decode(const float* q, const sk_paged_kv& kv, const void* k_new, const
 // Enqueues one decode launch. scratch: a cleared workspace layout (header, tickets at
 // kWsHeaderBytes, split partials at kPartialsOffset) of at least
 // sk_workspace_bytes(batch, Hq) bytes; err: the device error word (may be null).
+// The per-head q/k finish of a decode from a layer's raw q/k/v projection.
+struct QKFinish {
+  const uint16_t* g_q;
+  const uint16_t* g_k;
+  float eps;
+  float rope_base;
+};
+
+template <int MODE, bool QK, bool HAS_SEL>
+void launch_instance(bool single, int64_t grid, size_t lds, hipStream_t stream, const DecodeParams& P) {
+  if (single)
+    hipLaunchKernelGGL((decode_kernel<MODE, HAS_SEL, true, QK>), dim3(unsigned(grid)), dim3(kThreads), lds, stream, P);
+  else
+    hipLaunchKernelGGL((decode_kernel<MODE, HAS_SEL, false, QK>), dim3(unsigned(grid)), dim3(kThreads), lds, stream,
+                       P);
+}
+
 template <int MODE>
 int enqueue_decode(const float* q, sk_paged_kv kv, const void* k_new, const void* v_new, int sinks, int window,
                    float scale, const int32_t* sel, int sel_value, const int32_t* lp, const int32_t* lc,
                    const int32_t* ln, float* out, uint8_t* scratch, int32_t* err, hipStream_t stream,
-                   const int32_t* decl, int local_tokens) {
+                   const int32_t* decl, int local_tokens, const QKFinish* qk = nullptr) {
   DecodeParams P;
   P.q = q;
   P.kv = kv;
@@ -1079,6 +1209,10 @@ int enqueue_decode(const float* q, sk_paged_kv kv, const void* k_new, const void
   P.qscale = scale * kLog2e;
   P.decl = decl;
   P.local_tokens = local_tokens;
+  P.g_q = qk ? qk->g_q : nullptr;
+  P.g_k = qk ? qk->g_k : nullptr;
+  P.qk_eps = qk ? qk->eps : 0.f;
+  P.rope_base = qk ? qk->rope_base : 0.f;
   const int G = kv.num_q_heads / kv.num_kv_heads;
   // Grid: one workgroup per CU at most, fewer for small launches (an upper bound of the
   // work items from max_blocks), rounded to a multiple of the 8 XCDs.
@@ -1092,9 +1226,20 @@ int enqueue_decode(const float* q, sk_paged_kv kv, const void* k_new, const void
   const int acc_region = std::max(kWavesPerWG * G * kHeadDim, 2 * kMaxSplits * G + 4 * kThreads);
   size_t lds = size_t(kThreads) * 16 + 128 * 4 + size_t(acc_region) * 4 + size_t(kWavesPerWG) * 16 * 4 * 2 +
                size_t(3 * kv.batch + 1 + 8 + (MODE == kViews ? kv.batch : 0)) * 4;
+  const bool single = kv.batch == 1 && grid >= 2 * int64_t(kv.num_kv_heads);
+  if constexpr (MODE == kFull || MODE == kLocal) {
+    if (qk) {
+      if (sel)
+        launch_instance<MODE, true, true>(single, grid, lds, stream, P);
+      else
+        launch_instance<MODE, true, false>(single, grid, lds, stream, P);
+      return launch_status(hipGetLastError());
+    }
+  }
+  if (qk) return SK_E_RANGE;  // the q/k finish exists for the Full and Local views
   if constexpr (MODE == kViews) {  // the views are the selector: always present
     hipLaunchKernelGGL((decode_kernel<MODE, true, false>), dim3(unsigned(grid)), dim3(kThreads), lds, stream, P);
-  } else if (kv.batch == 1 && grid >= 2 * int64_t(kv.num_kv_heads)) {
+  } else if (single) {
     if (sel)
       hipLaunchKernelGGL((decode_kernel<MODE, true, true>), dim3(unsigned(grid)), dim3(kThreads), lds, stream, P);
     else
@@ -1112,14 +1257,20 @@ template <int MODE>
 int launch_decode(const float* q, sk_paged_kv kv, const void* k_new, const void* v_new, int sinks, int window,
                   float scale, const int32_t* sel, int sel_value, const int32_t* lp, const int32_t* lc,
                   const int32_t* ln, float* out, void* ws, size_t ws_bytes, hipStream_t stream,
-                  const int32_t* decl = nullptr, int local_tokens = 0) {
+                  const int32_t* decl = nullptr, int local_tokens = 0, const QKFinish* qk = nullptr) {
   int st = check_decode(q, kv, k_new, v_new, out);
   if (st) return st;
   if (!ws) return SK_E_NULL;
   if (ws_bytes < sk_workspace_bytes(kv.batch, kv.num_q_heads)) return SK_E_WORKSPACE;
   uint8_t* base = reinterpret_cast<uint8_t*>(ws);
   return enqueue_decode<MODE>(q, kv, k_new, v_new, sinks, window, scale, sel, sel_value, lp, lc, ln, out, base,
-                              reinterpret_cast<int32_t*>(base), stream, decl, local_tokens);
+                              reinterpret_cast<int32_t*>(base), stream, decl, local_tokens, qk);
+}
+
+int check_qk(const float* qkv, const uint16_t* g_q, const uint16_t* g_k, float eps, float rope_base) {
+  if (!qkv || !g_q || !g_k) return SK_E_NULL;
+  if (!(rope_base > 0.f) || !(eps >= 0.f)) return SK_E_RANGE;
+  return SK_OK;
 }
 
 // ---- allocation-free Full view: the workspace lives in a file-scope device array
@@ -1182,6 +1333,27 @@ int oda_decode_full(const float* q, sk_paged_kv kv, const void* k_new, const voi
                     hipStream_t stream) {
   return launch_decode<kFull>(q, kv, k_new, v_new, 0, 1, scale, sel, sel_value, nullptr, nullptr, nullptr, out,
                               ws, ws_bytes, stream);
+}
+
+int oda_decode_local_qkv(const float* qkv, const uint16_t* g_q, const uint16_t* g_k, float eps, float rope_base,
+                         sk_paged_kv kv, int32_t sinks, int32_t window, float scale, const int32_t* sel,
+                         int32_t sel_value, float* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int st = check_qk(qkv, g_q, g_k, eps, rope_base);
+  if (st) return st;
+  if (sinks < 0 || window < 1) return SK_E_RANGE;
+  const QKFinish qk{g_q, g_k, eps, rope_base};
+  return launch_decode<kLocal>(qkv, kv, nullptr, nullptr, sinks, window, scale, sel, sel_value, nullptr, nullptr,
+                               nullptr, out, ws, ws_bytes, stream, nullptr, 0, &qk);
+}
+
+int oda_decode_full_qkv(const float* qkv, const uint16_t* g_q, const uint16_t* g_k, float eps, float rope_base,
+                        sk_paged_kv kv, float scale, const int32_t* sel, int32_t sel_value, float* out, void* ws,
+                        size_t ws_bytes, hipStream_t stream) {
+  int st = check_qk(qkv, g_q, g_k, eps, rope_base);
+  if (st) return st;
+  const QKFinish qk{g_q, g_k, eps, rope_base};
+  return launch_decode<kFull>(qkv, kv, nullptr, nullptr, 0, 1, scale, sel, sel_value, nullptr, nullptr, nullptr, out,
+                              ws, ws_bytes, stream, nullptr, 0, &qk);
 }
 
 int oda_decode_full_noalloc(const float* q, sk_paged_kv kv, const void* k_new, const void* v_new, float scale,

@@ -10,10 +10,12 @@ ones committed. Here every launch of the recall pass carries the gate as its
 selector, so the step is one fixed sequence of launches (a HIP graph) with no host
 round trip ("Developer perspective").
 
-Layer (Qwen3-family): sk_qkv_rope (RMSNorm, q/k/v projection, per-head q/k norm,
-RoPE; the k/v candidate in bf16) -> oda_decode_local / oda_decode_full (attention with
-the candidate committed at n-1) -> sk_gemv W_o (+ residual) -> sk_gemv W_gate|up
-(RMSNorm prologue, SwiGLU epilogue) -> sk_gemv W_down (+ residual).
+Layer (Qwen3-family): sk_gemv W_qkv (RMSNorm prologue; the raw q/k/v projection) ->
+oda_decode_local_qkv / oda_decode_full_qkv (per-head q/k norm and RoPE applied while the
+attention stages its operands; the bf16 k/v candidate committed at n-1) -> sk_gemv W_o
+(+ residual) -> sk_gemv W_gate|up (RMSNorm prologue, SwiGLU epilogue) -> sk_gemv W_down
+(+ residual). With fuse_qk=False the per-head finish runs as its own launch
+(sk_qkv_rope) before oda_decode_local / oda_decode_full.
 
 This module only sequences library calls; it computes nothing itself.
 """
@@ -44,8 +46,9 @@ class ODADecoder:
     """
 
     def __init__(self, shape, weights, caches, sinks=4, window=2048, scale=None, device="cuda",
-                 local_only=()):
+                 local_only=(), fuse_qk=True):
         s = shape
+        self.fuse_qk = fuse_qk
         self.s, self.w, self.caches = s, weights, caches
         self.sinks, self.window = sinks, window
         self.scale = 1.0 / math.sqrt(ops.HEAD_DIM) if scale is None else scale
@@ -79,15 +82,27 @@ class ODADecoder:
 
     def _layer(self, l, h, full, sel):
         s, w = self.s, self.w
-        ops.qkv_rope(w["qkv.%d" % l], h, w["g_attn.%d" % l], w["g_q.%d" % l], w["g_k.%d" % l], s.q_heads,
-                     s.kv_heads, self.seq_lens, self.qkv_raw, self.q, self.k, self.v, eps=s.eps,
-                     rope_base=s.rope_base, sel=sel, sel_value=1)
-        if full and l not in self.local_only:
-            ops.oda_decode_full(self.q, self.caches[l], self.k, self.v, self.scale, sel=sel, sel_value=1,
-                                out=self.attn, ws=self.ws)
+        use_full = full and l not in self.local_only
+        if self.fuse_qk:
+            ops.gemv(w["qkv.%d" % l], h, self.qkv_raw, prologue=ops.PRO_RMSNORM, gamma=w["g_attn.%d" % l], eps=s.eps,
+                     sel=sel)
+            qk = dict(eps=s.eps, rope_base=s.rope_base, scale=self.scale, sel=sel, sel_value=1, out=self.attn,
+                      ws=self.ws)
+            if use_full:
+                ops.oda_decode_full_qkv(self.qkv_raw, w["g_q.%d" % l], w["g_k.%d" % l], self.caches[l], **qk)
+            else:
+                ops.oda_decode_local_qkv(self.qkv_raw, w["g_q.%d" % l], w["g_k.%d" % l], self.caches[l],
+                                         sinks=self.sinks, window=self.window, **qk)
         else:
-            ops.oda_decode_local(self.q, self.caches[l], self.k, self.v, self.sinks, self.window, self.scale,
-                                 sel=sel, sel_value=1, out=self.attn, ws=self.ws)
+            ops.qkv_rope(w["qkv.%d" % l], h, w["g_attn.%d" % l], w["g_q.%d" % l], w["g_k.%d" % l], s.q_heads,
+                         s.kv_heads, self.seq_lens, self.qkv_raw, self.q, self.k, self.v, eps=s.eps,
+                         rope_base=s.rope_base, sel=sel, sel_value=1)
+            if use_full:
+                ops.oda_decode_full(self.q, self.caches[l], self.k, self.v, self.scale, sel=sel, sel_value=1,
+                                    out=self.attn, ws=self.ws)
+            else:
+                ops.oda_decode_local(self.q, self.caches[l], self.k, self.v, self.sinks, self.window, self.scale,
+                                     sel=sel, sel_value=1, out=self.attn, ws=self.ws)
         ops.gemv(w["o.%d" % l], self.attn.view(-1), h, residual=h, sel=sel)
         ops.gemv(w["gu.%d" % l], h, self.act, prologue=ops.PRO_RMSNORM, gamma=w["g_mlp.%d" % l], eps=s.eps,
                  epilogue=ops.EPI_SWIGLU, sel=sel)

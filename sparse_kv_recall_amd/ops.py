@@ -152,6 +152,40 @@ def oda_decode_full(q, kv, k_new=None, v_new=None, scale=None, sel=None, sel_val
     return out
 
 
+def _qkv_common(qkv, g_q, g_k, kv, sel, out, ws):
+    heads = kv.num_q_heads + 2 * kv.num_kv_heads
+    _check(qkv, torch.float32, "qkv", kv.batch * heads * HEAD_DIM)
+    _check(g_q, torch.bfloat16, "g_q", HEAD_DIM)
+    _check(g_k, torch.bfloat16, "g_k", HEAD_DIM)
+    if qkv is None or g_q is None or g_k is None:
+        raise ValueError("qkv, g_q and g_k are required")
+    return _decode_common(qkv, kv, None, None, sel, out, ws)
+
+
+def oda_decode_local_qkv(qkv, g_q, g_k, kv, eps=1e-6, rope_base=1.0e6, sinks=4, window=2048, scale=None, sel=None,
+                         sel_value=MODE_LOCAL, out=None, ws=None):
+    """oda_decode_local from a layer's raw q/k/v projection qkv [B][Hq + 2 Hkv][128] fp32:
+    per-head RMSNorm (gains g_q, g_k) and rotary positions at n - 1 are applied on load,
+    and the finished k and v (bf16) are committed at n - 1."""
+    out, ws = _qkv_common(qkv, g_q, g_k, kv, sel, out, ws)
+    scale = 1.0 / math.sqrt(HEAD_DIM) if scale is None else float(scale)
+    _lib.call("oda_decode_local_qkv", qkv.data_ptr(), g_q.data_ptr(), g_k.data_ptr(), float(eps), float(rope_base),
+              kv.abi(), int(sinks), int(window), scale, _ptr(sel), int(sel_value), out.data_ptr(), ws.data_ptr(),
+              ws.numel(), _stream(qkv.device))
+    return out
+
+
+def oda_decode_full_qkv(qkv, g_q, g_k, kv, eps=1e-6, rope_base=1.0e6, scale=None, sel=None, sel_value=1, out=None,
+                        ws=None):
+    """oda_decode_full from a layer's raw q/k/v projection (see oda_decode_local_qkv)."""
+    out, ws = _qkv_common(qkv, g_q, g_k, kv, sel, out, ws)
+    scale = 1.0 / math.sqrt(HEAD_DIM) if scale is None else float(scale)
+    _lib.call("oda_decode_full_qkv", qkv.data_ptr(), g_q.data_ptr(), g_k.data_ptr(), float(eps), float(rope_base),
+              kv.abi(), scale, _ptr(sel), int(sel_value), out.data_ptr(), ws.data_ptr(), ws.numel(),
+              _stream(qkv.device))
+    return out
+
+
 def oda_decode_full_noalloc(q, kv, out, k_new=None, v_new=None, scale=None, sel=None, sel_value=1, dev_err=None):
     """oda_decode_full without a workspace (the library's own device array serves as one);
     `out` is required, so nothing is allocated on this path."""

@@ -396,7 +396,7 @@ class DecoderRun:
     """Weight-bearing ODA steps (Local pass through every layer, recall head on the real
     Local hidden state, gated recall pass, select) against the fp64 decoder oracle."""
 
-    def __init__(self, wl, local_only=()):
+    def __init__(self, wl, local_only=(), fuse_qk=True):
         from sparse_kv_recall_amd.model import DecoderShape, ODADecoder
         self.wl = wl
         L, Hkv = wl.layers, wl.kv_heads
@@ -417,7 +417,7 @@ class DecoderRun:
         shape = DecoderShape(L, wl.hidden, wl.q_heads, Hkv, wl.intermediate, wl.vocab, wl.recall_hidden, wl.eps,
                              wl.rope_base)
         self.model = ODADecoder(shape, wl.device_weights(), self.caches, wl.sinks, wl.window,
-                                local_only=local_only)
+                                local_only=local_only, fuse_qk=fuse_qk)
         self.local_only = frozenset(local_only)
         self.oracle = oracle.decoder.Decoder(
             oracle.decoder.DecoderShape(L, wl.hidden, wl.q_heads, Hkv, wl.intermediate, wl.vocab, wl.recall_hidden,

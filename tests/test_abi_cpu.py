@@ -80,6 +80,29 @@ def test_decode_full_noalloc_validation():
     assert L.sk_workspace_bytes(480, 32) <= 16 << 20 < L.sk_workspace_bytes(512, 32)
 
 
+def test_decode_from_projection_validation():
+    # the Local / Full views from a raw q/k/v projection check the projection, its gains
+    # and the rotary base before any HIP call, then the decode arguments as the plain views
+    L = lib()
+    loc = lambda qkv=FAKE, gq=FAKE, gk=FAKE, eps=1e-6, base=1e6, k=None, sinks=4, window=2048, ws=FAKE: \
+        L.oda_decode_local_qkv(qkv, gq, gk, eps, base, k or kv(), sinks, window, 0.1, None, 1, FAKE, ws, 1 << 20,
+                               None)
+    full = lambda qkv=FAKE, gq=FAKE, gk=FAKE, eps=1e-6, base=1e6, k=None, ws=FAKE: \
+        L.oda_decode_full_qkv(qkv, gq, gk, eps, base, k or kv(), 0.1, None, 1, FAKE, ws, 1 << 20, None)
+    for call in (loc, full):
+        assert call(qkv=None) == SK_E_NULL
+        assert call(gq=None) == SK_E_NULL
+        assert call(gk=None) == SK_E_NULL
+        assert call(base=0.0) == SK_E_RANGE
+        assert call(base=float("nan")) == SK_E_RANGE
+        assert call(eps=-1.0) == SK_E_RANGE
+        assert call(k=kv(head_dim=64)) == SK_E_SHAPE
+        assert call(k=kv(num_q_heads=12)) == SK_E_HEADS
+        assert call(ws=None) == SK_E_NULL
+    assert loc(sinks=-1) == SK_E_RANGE
+    assert loc(window=0) == SK_E_RANGE
+
+
 def test_other_entry_points_validation():
     L = lib()
     assert L.oda_recall_score(None, FAKE, FAKE, FAKE, FAKE, 1, 8, 4, 0.0, FAKE, FAKE, FAKE, 1 << 20, None) == SK_E_NULL

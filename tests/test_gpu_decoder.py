@@ -10,13 +10,16 @@ from tests.helpers import requires_gpu
 pytestmark = [pytest.mark.gpu, requires_gpu]
 
 
-def test_decoder_oda_steps():
+@pytest.mark.parametrize("fuse_qk", [True, False])
+def test_decoder_oda_steps(fuse_qk):
+    # fuse_qk: the per-head q/k finish inside the decode launches (the model's default),
+    # else as a launch of its own
     from tests.harness import DecoderRun
     wl = decoder_small()
-    rep = DecoderRun(wl).run()
+    rep = DecoderRun(wl, fuse_qk=fuse_qk).run()
     assert rep.decisions == wl.steps and 0 < rep.recalls < wl.steps
-    print("decoder_small: recalls %d/%d, max-abs %.2e, row-rel %.2e, commit bf16 mismatches %.4f"
-          % (rep.recalls, wl.steps, rep.max_abs, rep.max_row_rel, rep.commit_mismatch_frac))
+    print("decoder_small fuse_qk=%s: recalls %d/%d, max-abs %.2e, row-rel %.2e, commit bf16 mismatches %.4f"
+          % (fuse_qk, rep.recalls, wl.steps, rep.max_abs, rep.max_row_rel, rep.commit_mismatch_frac))
 
 
 def test_decoder_oda_steps_hybrid():
@@ -65,3 +68,51 @@ def test_qkv_rope_two_positions():
             gt = got.float().cpu().numpy().reshape(-1, 128)
             # bf16 outputs: within one bf16 unit (2^-8 relative) of the fp64 value
             assert np.all(np.abs(gt - ref) <= np.abs(ref) * 2.0 ** -7 + 1e-6), call
+
+
+@pytest.mark.parametrize("view,G,n", [("local", 2, 131072), ("full", 4, 2999), ("local", 8, 6), ("full", 1, 40)])
+def test_decode_from_projection(view, G, n):
+    """The Local / Full views from a raw q/k/v projection (per-head q/k RMSNorm and the
+    rotation at n - 1 applied inside the decode launch) against the fp64 layer pieces of
+    the decoder oracle: the committed v bit for bit, the committed k within one bf16 unit
+    of the rounded fp64 key, and the output within the hi+lo error bound of fp64
+    attention of the fp64 q over the history with the committed key."""
+    import numpy as np
+    import torch
+    from oracle import attention, keysets
+    from oracle import decoder as od
+    from oracle.bf16 import bf16_bits_to_f64, f64_to_bf16_bits
+    from sparse_kv_recall_amd import ops
+    from synth import rng
+    from tests.helpers import SCALE, bf16_tensor_to_bits, bits_to_bf16_tensor, check_tight, rand_bits
+    Hkv, eps, base = 2, 1e-6, 1.0e6
+    Hq = G * Hkv
+    g = np.random.default_rng(100 * G + n % 997)
+    mb = -(-n // 16)
+    hk = rand_bits(rng.mix_key(911, G, 1), n, Hkv)
+    hv = rand_bits(rng.mix_key(911, G, 2), n, Hkv)
+    seq = torch.tensor([n], dtype=torch.int32, device="cuda")
+    bt = torch.arange(mb, dtype=torch.int32, device="cuda")[None]
+    cache = ops.PagedKVCache(mb, 1, Hq, Hkv, mb, block_tables=bt, seq_lens=seq)
+    if n > 1:
+        ops.kv_write(cache, 0, 0, bits_to_bf16_tensor(hk[:n - 1]), bits_to_bf16_tensor(hv[:n - 1]))
+    raw = (g.standard_normal((Hq + 2 * Hkv, 128)) * 0.7 + 0.1).astype(np.float32)
+    gains = [torch.as_tensor(1.0 + 0.2 * g.standard_normal(128)).to(torch.bfloat16) for _ in range(2)]
+    gq, gk = (t.float().numpy().astype(np.float64) for t in gains)
+    fn = ops.oda_decode_local_qkv if view == "local" else ops.oda_decode_full_qkv
+    out = fn(torch.as_tensor(raw).cuda(), gains[0].cuda(), gains[1].cuda(), cache, eps=eps, rope_base=base)
+    torch.cuda.synchronize()
+    kc, vc = ops.kv_read(cache, 0, n - 1, 1)
+    kb, vb = bf16_tensor_to_bits(kc)[0], bf16_tensor_to_bits(vc)[0]
+    raw64 = raw.astype(np.float64)
+    q = od.rope(od.rms_norm(raw64[:Hq], gq, eps), n - 1, base)
+    k = od.rope(od.rms_norm(raw64[Hq:Hq + Hkv], gk, eps), n - 1, base)
+    assert np.array_equal(vb, f64_to_bf16_bits(raw64[Hq + Hkv:]))
+    kr = f64_to_bf16_bits(k)
+    a, b = bf16_bits_to_f64(kb), bf16_bits_to_f64(kr)
+    assert np.all(np.abs(a - b) <= 2.0 ** -7 * np.maximum(np.abs(a), np.abs(b)) + 1e-30)
+    assert (kb != kr).mean() < 0.05, (kb != kr).mean()
+    hk[n - 1], hv[n - 1] = kb, vb
+    keys = keysets.local_keys(n) if view == "local" else keysets.full_keys(n)
+    ref = attention.attend(q, hk, hv, keys, SCALE)
+    check_tight(out[0].cpu().numpy(), ref, q, hk, hv, keys, SCALE, what="%s from projection G=%d n=%d" % (view, G, n))
