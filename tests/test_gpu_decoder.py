@@ -116,3 +116,63 @@ def test_decode_from_projection(view, G, n):
     keys = keysets.local_keys(n) if view == "local" else keysets.full_keys(n)
     ref = attention.attend(q, hk, hv, keys, SCALE)
     check_tight(out[0].cpu().numpy(), ref, q, hk, hv, keys, SCALE, what="%s from projection G=%d n=%d" % (view, G, n))
+
+
+@pytest.mark.parametrize("view", ["local", "full"])
+def test_decode_from_projection_batch(view):
+    """The batch (workgroup-planned) instances of the views from a raw projection: three
+    requests of different lengths, each with its own projection rows; with a selector
+    that skips the second request (its output rows and its slot stay untouched)."""
+    import numpy as np
+    import torch
+    from oracle import attention, keysets
+    from oracle import decoder as od
+    from oracle.bf16 import bf16_bits_to_f64, f64_to_bf16_bits
+    from sparse_kv_recall_amd import ops
+    from synth import rng
+    from tests.helpers import SCALE, bf16_tensor_to_bits, bits_to_bf16_tensor, check_tight, rand_bits
+    B, Hkv, G, eps, base = 3, 2, 4, 1e-6, 1.0e6
+    Hq = G * Hkv
+    ns = [5000, 300, 2100]
+    g = np.random.default_rng(5)
+    mb = max(-(-n // 16) for n in ns)
+    seq = torch.tensor(ns, dtype=torch.int32, device="cuda")
+    bt = torch.arange(B * mb, dtype=torch.int32, device="cuda").view(B, mb)
+    cache = ops.PagedKVCache(B * mb, B, Hq, Hkv, mb, block_tables=bt, seq_lens=seq)
+    hist = []
+    for b, n in enumerate(ns):
+        hk = rand_bits(rng.mix_key(912, b, 1), n, Hkv)
+        hv = rand_bits(rng.mix_key(912, b, 2), n, Hkv)
+        ops.kv_write(cache, b, 0, bits_to_bf16_tensor(hk[:n - 1]), bits_to_bf16_tensor(hv[:n - 1]))
+        hist.append((hk, hv))
+    slot_before = [tuple(bf16_tensor_to_bits(t)[0].copy() for t in ops.kv_read(cache, b, ns[b] - 1, 1))
+                   for b in range(B)]
+    raw = (g.standard_normal((B, Hq + 2 * Hkv, 128)) * 0.7 + 0.1).astype(np.float32)
+    gains = [torch.as_tensor(1.0 + 0.2 * g.standard_normal(128)).to(torch.bfloat16) for _ in range(2)]
+    gq, gk = (t.float().numpy().astype(np.float64) for t in gains)
+    sel = torch.tensor([1, 0, 1], dtype=torch.int32, device="cuda")
+    out = torch.full((B, Hq, 128), 7.0, device="cuda")
+    fn = ops.oda_decode_local_qkv if view == "local" else ops.oda_decode_full_qkv
+    fn(torch.as_tensor(raw).cuda(), gains[0].cuda(), gains[1].cuda(), cache, eps=eps, rope_base=base, sel=sel,
+       sel_value=1, out=out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    for b, n in enumerate(ns):
+        kc, vc = ops.kv_read(cache, b, n - 1, 1)
+        kb, vb = bf16_tensor_to_bits(kc)[0], bf16_tensor_to_bits(vc)[0]
+        if b == 1:  # not selected: nothing written
+            assert np.all(got[b] == 7.0)
+            assert np.array_equal(kb, slot_before[b][0]) and np.array_equal(vb, slot_before[b][1])
+            continue
+        r64 = raw[b].astype(np.float64)
+        q = od.rope(od.rms_norm(r64[:Hq], gq, eps), n - 1, base)
+        k = od.rope(od.rms_norm(r64[Hq:Hq + Hkv], gk, eps), n - 1, base)
+        assert np.array_equal(vb, f64_to_bf16_bits(r64[Hq + Hkv:])), b
+        kr = f64_to_bf16_bits(k)
+        a, c = bf16_bits_to_f64(kb), bf16_bits_to_f64(kr)
+        assert np.all(np.abs(a - c) <= 2.0 ** -7 * np.maximum(np.abs(a), np.abs(c)) + 1e-30), b
+        hk, hv = hist[b]
+        hk[n - 1], hv[n - 1] = kb, vb
+        keys = keysets.local_keys(n) if view == "local" else keysets.full_keys(n)
+        ref = attention.attend(q, hk, hv, keys, SCALE)
+        check_tight(got[b], ref, q, hk, hv, keys, SCALE, what="%s from projection b=%d n=%d" % (view, b, n))
