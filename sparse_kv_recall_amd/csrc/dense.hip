@@ -228,6 +228,9 @@ __global__ __launch_bounds__(kHeadDim) void qk_finish_kernel(const float* __rest
   const int head = blockIdx.x, t = threadIdx.x;
   const bool is_q = head < Hq, is_v = head >= Hq + Hkv;
   float v = raw[head * kHeadDim + t];
+  // the gain is requested with the projection row, not after the reduction's barriers
+  // (v heads read a k gain they do not use, so the load needs no branch)
+  const uint16_t gain = (is_q ? g_q : g_k)[t];
   // rotary angle of pair t % 64 at position n - 1, in fp64 and reduced to [-pi, pi]
   // before the sine and cosine (|angle| < 2^31 rad, so the reduction error stays far
   // below fp32 resolution); computed while the projection row is still loading
@@ -242,7 +245,7 @@ __global__ __launch_bounds__(kHeadDim) void qk_finish_kernel(const float* __rest
     s = float(sd);
   }
   const float ss = block_sum(v * v, red);
-  if (!is_v) v = v * (1.f / sqrtf(ss / float(kHeadDim) + eps)) * bf16f((is_q ? g_q : g_k)[t]);
+  if (!is_v) v = v * (1.f / sqrtf(ss / float(kHeadDim) + eps)) * bf16f(gain);
   s_val[t] = v;
   __syncthreads();
   float o = v;
