@@ -625,6 +625,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
   int T, total_items;
   int w_tiles = 0, w_start = 0, w_len = 0;  // small batches: lane b holds request b's tiles,
                                              // first item and sequence length
+  // views launch, small batches: lane b holds request b's items before its last splits
+  // (v_full, from v_fstart in the execution order) and the rank of its last split's size
+  int v_full = 0, v_fstart = 0, v_rank = 0, n_full = 0;
   if (SINGLE) {
     // the small-batch plan below for one request: the rounding reserve, then, when the
     // splits would leave more than a quarter of the slots idle, the smallest split size
@@ -708,6 +711,22 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
     w_len = (lane < B) ? l_len : 0;
     w_start = (x - splits) * Hkv;
     total_items = __builtin_amdgcn_readlane(x, 63) * Hkv;
+    if (MODE == kViews) {
+      // Execution order of the items (the loop at the end): every request's splits but
+      // its last first, then the last splits, largest first (ties by request), so that
+      // the short items fill in at the end instead of lengthening some workgroups' share.
+      v_full = (splits > 0) ? (splits - 1) * Hkv : 0;
+      const int f = wave_inclusive_scan(v_full);
+      v_fstart = f - v_full;
+      n_full = __builtin_amdgcn_readlane(f, 63);
+      const int rem = (splits > 0) ? tiles - (splits - 1) * T : -1;
+      int rank = 0;
+      for (int o = 0; o < 64; ++o) {
+        const int ro = __builtin_amdgcn_readlane(rem, o);
+        rank += (ro > rem || (ro == rem && o < lane)) ? 1 : 0;
+      }
+      v_rank = rank;
+    }
   } else {
     __syncthreads();
     int my_sum = 0, my_active = 0, my_max = 0;
@@ -1102,6 +1121,28 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
   };
   if constexpr (SINGLE) {
     if (item_first < total_items) item_body(item_first);
+  } else if (MODE == kViews && B <= 64) {
+    // Position i of the execution order -> the item (its partials keep the item's slot,
+    // and merges run in split order, so results do not depend on the order). Rounds of the
+    // grid alternate direction, so a workgroup that takes a larger item in one round
+    // takes a smaller one in the next.
+    auto item_at = [&](const int i) {
+      if (i < n_full) {
+        const int b = __builtin_amdgcn_readfirstlane(__popcll(__ballot(lane < B && v_fstart + v_full <= i)));
+        const int sp = (__builtin_amdgcn_readlane(w_tiles, b) + T - 1) / T;
+        const int local = i - __builtin_amdgcn_readlane(v_fstart, b);
+        return __builtin_amdgcn_readlane(w_start, b) + (local / (sp - 1)) * sp + local % (sp - 1);
+      }
+      const int j = i - n_full;
+      const int b = __builtin_amdgcn_readfirstlane(int(__builtin_ctzll(__ballot(lane < B && v_rank == j / Hkv))));
+      const int sp = (__builtin_amdgcn_readlane(w_tiles, b) + T - 1) / T;
+      return __builtin_amdgcn_readlane(w_start, b) + (j % Hkv) * sp + sp - 1;
+    };
+    const int grid = int(gridDim.x);
+    for (int r = 0; r * grid < total_items; ++r) {
+      const int i = r * grid + ((r & 1) ? grid - 1 - item_first : item_first);
+      if (i < total_items) item_body(item_at(i));
+    }
   } else {
     for (int item = item_first; item < total_items; item += gridDim.x) item_body(item);
   }
