@@ -47,6 +47,9 @@ constexpr int kMergeBatch = 48;                     // split accumulators loaded
 // rounds +1.8 %, 6 rounds +2.8 % (more items than the workspace holds at group 16), 8
 // rounds +0.2 % (longer split merges).
 constexpr int kViewRounds = 4;
+// Largest batch that the workgroup-planned path runs in the balanced item order (ranking
+// the requests' last splits takes about B^2 / 512 steps per thread).
+constexpr int kOrderMaxBatch = 256;
 constexpr float kLog2e = 1.4426950408889634f;
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -543,7 +546,7 @@ __device__ inline void load_tile(const uint8_t* kpool, const uint8_t* vpool, int
 // request alone in a batch on the same grid), computed on the uniform length alone: no
 // cross-lane reductions, scans or request search, which shortens the chain of
 // instructions before the first tile is requested.
-template <int MODE, bool HAS_SEL, bool SINGLE, bool QK = false>
+template <int MODE, bool HAS_SEL, bool SINGLE, bool QK = false, bool BAL = false>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
   constexpr int W = kWavesPerWG;
   extern __shared__ float smem[];
@@ -566,6 +569,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
   int* s_len = s_start + B + 1;  // [B] sequence lengths (large batches)
   int* s_misc = s_len + B;  // [0] tile sum, [1] T, [2] active requests, [3] last flag, [4] max tiles
   int* s_view = s_misc + 8;  // [B] views of the requests (MODE kViews, large batches)
+  // large batches in the balanced order: [B + 1] first position of each request's items
+  // before its last splits, [B] its last split's tiles, [B] the request at each rank
+  int* s_fstart = s_view + (MODE == kViews ? B : 0);
+  int* s_rem = s_fstart + B + 1;
+  int* s_byrank = s_rem + B;
 
   if (tid == 0) {
     s_misc[0] = 0;
@@ -625,8 +633,12 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
   int T, total_items;
   int w_tiles = 0, w_start = 0, w_len = 0;  // small batches: lane b holds request b's tiles,
                                              // first item and sequence length
-  // views launch, small batches: lane b holds request b's items before its last splits
-  // (v_full, from v_fstart in the execution order) and the rank of its last split's size
+  // Balanced item order (the loop at the end; instances with BAL, which the host picks for
+  // the views launch and for batches above 64), used for the views and ragged batches:
+  // small batches keep, in lane b, request b's items before its last splits (v_full, from
+  // v_fstart in the execution order) and the rank of its last split's size; large batches
+  // the same in LDS. n_full: the items before all last splits.
+  bool balanced = false;
   int v_full = 0, v_fstart = 0, v_rank = 0, n_full = 0;
   if (SINGLE) {
     // the small-batch plan below for one request: the rounding reserve, then, when the
@@ -711,7 +723,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
     w_len = (lane < B) ? l_len : 0;
     w_start = (x - splits) * Hkv;
     total_items = __builtin_amdgcn_readlane(x, 63) * Hkv;
-    if (MODE == kViews) {
+    balanced = BAL && (MODE == kViews || mx * act > 2 * sum);
+    if (BAL && balanced) {
       // Execution order of the items (the loop at the end): every request's splits but
       // its last first, then the last splits, largest first (ties by request), so that
       // the short items fill in at the end instead of lengthening some workgroups' share.
@@ -766,6 +779,37 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
     }
     __syncthreads();
     total_items = s_start[B];
+    balanced = BAL && B <= kOrderMaxBatch && (MODE == kViews || s_misc[4] * s_misc[2] > 2 * s_misc[0]);
+    if (BAL && balanced) {  // the same order as for small batches, ranked in LDS
+      if (wave == 0) {
+        int carry = 0;
+        for (int base = 0; base < B; base += 64) {
+          const int b = base + lane;
+          const int sp = (b < B) ? (s_tiles[b] + T - 1) / T : 0;
+          const int full = (sp > 0) ? (sp - 1) * Hkv : 0;
+          const int x = wave_inclusive_scan(full);
+          if (b < B) {
+            s_fstart[b] = carry + x - full;
+            s_rem[b] = (sp > 0) ? s_tiles[b] - (sp - 1) * T : -1;
+          }
+          carry += __builtin_amdgcn_readlane(x, 63);
+        }
+        if (lane == 0) s_fstart[B] = carry;
+      }
+      __syncthreads();
+      for (int b = tid; b < B; b += blockDim.x) {
+        const int rem = s_rem[b];
+        if (rem < 0) continue;
+        int rank = 0;
+        for (int o = 0; o < B; ++o) {
+          const int ro = s_rem[o];
+          rank += (ro > rem || (ro == rem && o < b)) ? 1 : 0;
+        }
+        s_byrank[rank] = b;
+      }
+      __syncthreads();
+      n_full = s_fstart[B];
+    }
   }
 
   // Items in workgroup order. The dispatcher deals workgroups round-robin over the 8
@@ -1121,30 +1165,46 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
   };
   if constexpr (SINGLE) {
     if (item_first < total_items) item_body(item_first);
-  } else if (MODE == kViews && B <= 64) {
+  } else if constexpr (!BAL) {
+    for (int item = item_first; item < total_items; item += gridDim.x) item_body(item);
+  } else {
     // Position i of the execution order -> the item (its partials keep the item's slot,
     // and merges run in split order, so results do not depend on the order). Rounds of the
     // grid alternate direction, so a workgroup that takes a larger item in one round
     // takes a smaller one in the next.
     auto item_at = [&](const int i) {
-      if (i < n_full) {
-        const int b = __builtin_amdgcn_readfirstlane(__popcll(__ballot(lane < B && v_fstart + v_full <= i)));
-        const int sp = (__builtin_amdgcn_readlane(w_tiles, b) + T - 1) / T;
-        const int local = i - __builtin_amdgcn_readlane(v_fstart, b);
-        return __builtin_amdgcn_readlane(w_start, b) + (local / (sp - 1)) * sp + local % (sp - 1);
+      int b, sp;
+      if (B <= 64) {  // per-request values in lane b
+        if (i < n_full) {
+          b = __builtin_amdgcn_readfirstlane(__popcll(__ballot(lane < B && v_fstart + v_full <= i)));
+          sp = (__builtin_amdgcn_readlane(w_tiles, b) + T - 1) / T;
+          const int local = i - __builtin_amdgcn_readlane(v_fstart, b);
+          return __builtin_amdgcn_readlane(w_start, b) + (local / (sp - 1)) * sp + local % (sp - 1);
+        }
+        b = __builtin_amdgcn_readfirstlane(int(__builtin_ctzll(__ballot(lane < B && v_rank == (i - n_full) / Hkv))));
+        sp = (__builtin_amdgcn_readlane(w_tiles, b) + T - 1) / T;
+        return __builtin_amdgcn_readlane(w_start, b) + ((i - n_full) % Hkv) * sp + sp - 1;
       }
-      const int j = i - n_full;
-      const int b = __builtin_amdgcn_readfirstlane(int(__builtin_ctzll(__ballot(lane < B && v_rank == j / Hkv))));
-      const int sp = (__builtin_amdgcn_readlane(w_tiles, b) + T - 1) / T;
-      return __builtin_amdgcn_readlane(w_start, b) + (j % Hkv) * sp + sp - 1;
+      if (i < n_full) {  // the request whose items before its last splits hold position i
+        int lo_b = 0, hi_b = B - 1;
+        while (lo_b < hi_b) {
+          const int mid = (lo_b + hi_b + 1) >> 1;
+          if (s_fstart[mid] <= i) lo_b = mid; else hi_b = mid - 1;
+        }
+        sp = (s_tiles[lo_b] + T - 1) / T;
+        const int local = i - s_fstart[lo_b];
+        return s_start[lo_b] + (local / (sp - 1)) * sp + local % (sp - 1);
+      }
+      b = s_byrank[(i - n_full) / Hkv];
+      sp = (s_tiles[b] + T - 1) / T;
+      return s_start[b] + ((i - n_full) % Hkv) * sp + sp - 1;
     };
+    // one loop for both orders, so that the item body is compiled once
     const int grid = int(gridDim.x);
     for (int r = 0; r * grid < total_items; ++r) {
-      const int i = r * grid + ((r & 1) ? grid - 1 - item_first : item_first);
-      if (i < total_items) item_body(item_at(i));
+      const int i = r * grid + ((balanced && (r & 1)) ? grid - 1 - item_first : item_first);
+      if (i < total_items) item_body(balanced ? item_at(i) : i);
     }
-  } else {
-    for (int item = item_first; item < total_items; item += gridDim.x) item_body(item);
   }
 }
 
@@ -1226,6 +1286,19 @@ void launch_instance(bool single, int64_t grid, size_t lds, hipStream_t stream, 
                        P);
 }
 
+// Batch launches: the balanced item order for ragged requests is a variant of its own
+// (BAL), taken for batches above 64 requests; up to 64, the lengths are rarely ragged
+// enough to pay for it (the variant's extra code measured 2-4 % slower on equal lengths).
+template <int MODE, bool HAS_SEL>
+void launch_batch(int64_t grid, size_t lds, hipStream_t stream, const DecodeParams& P) {
+  if (P.kv.batch > 64)
+    hipLaunchKernelGGL((decode_kernel<MODE, HAS_SEL, false, false, true>), dim3(unsigned(grid)), dim3(kThreads), lds,
+                       stream, P);
+  else
+    hipLaunchKernelGGL((decode_kernel<MODE, HAS_SEL, false, false, false>), dim3(unsigned(grid)), dim3(kThreads), lds,
+                       stream, P);
+}
+
 template <int MODE>
 int enqueue_decode(const float* q, sk_paged_kv kv, const void* k_new, const void* v_new, int sinks, int window,
                    float scale, const int32_t* sel, int sel_value, const int32_t* lp, const int32_t* lc,
@@ -1266,7 +1339,8 @@ int enqueue_decode(const float* q, sk_paged_kv kv, const void* k_new, const void
   grid = (grid + 7) / 8 * 8;
   const int acc_region = std::max(kWavesPerWG * G * kHeadDim, 2 * kMaxSplits * G + 4 * kThreads);
   size_t lds = size_t(kThreads) * 16 + 128 * 4 + size_t(acc_region) * 4 + size_t(kWavesPerWG) * 16 * 4 * 2 +
-               size_t(3 * kv.batch + 1 + 8 + (MODE == kViews ? kv.batch : 0)) * 4;
+               size_t(3 * kv.batch + 1 + 8 + (MODE == kViews ? kv.batch : 0)) * 4 +
+               (kv.batch <= kOrderMaxBatch ? size_t(3 * kv.batch + 1) * 4 : 0);
   const bool single = kv.batch == 1 && grid >= 2 * int64_t(kv.num_kv_heads);
   if constexpr (MODE == kFull || MODE == kLocal) {
     if (qk) {
@@ -1278,8 +1352,9 @@ int enqueue_decode(const float* q, sk_paged_kv kv, const void* k_new, const void
     }
   }
   if (qk) return SK_E_RANGE;  // the q/k finish exists for the Full and Local views
-  if constexpr (MODE == kViews) {  // the views are the selector: always present
-    hipLaunchKernelGGL((decode_kernel<MODE, true, false>), dim3(unsigned(grid)), dim3(kThreads), lds, stream, P);
+  if constexpr (MODE == kViews) {  // the views are the selector: always present; balanced order
+    hipLaunchKernelGGL((decode_kernel<MODE, true, false, false, true>), dim3(unsigned(grid)), dim3(kThreads), lds,
+                       stream, P);
   } else if (single) {
     if (sel)
       hipLaunchKernelGGL((decode_kernel<MODE, true, true>), dim3(unsigned(grid)), dim3(kThreads), lds, stream, P);
@@ -1287,9 +1362,9 @@ int enqueue_decode(const float* q, sk_paged_kv kv, const void* k_new, const void
       hipLaunchKernelGGL((decode_kernel<MODE, false, true>), dim3(unsigned(grid)), dim3(kThreads), lds, stream, P);
   } else {
     if (sel)
-      hipLaunchKernelGGL((decode_kernel<MODE, true, false>), dim3(unsigned(grid)), dim3(kThreads), lds, stream, P);
+      launch_batch<MODE, true>(grid, lds, stream, P);
     else
-      hipLaunchKernelGGL((decode_kernel<MODE, false, false>), dim3(unsigned(grid)), dim3(kThreads), lds, stream, P);
+      launch_batch<MODE, false>(grid, lds, stream, P);
   }
   return launch_status(hipGetLastError());
 }
