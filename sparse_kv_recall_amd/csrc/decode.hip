@@ -763,7 +763,20 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
     if (my_active) atomicAdd(&s_misc[2], my_active);
     if (my_max) atomicMax(&s_misc[4], my_max);
     __syncthreads();
-    if (tid == 0) s_misc[1] = split_size(s_misc[0], s_misc[2], s_misc[4]);
+    if (tid == 0) {
+      int t = split_size(s_misc[0], s_misc[2], s_misc[4]);
+      if (BAL && B <= kOrderMaxBatch && s_misc[4] * s_misc[2] > 2 * s_misc[0]) {
+        // ragged lengths in the balanced order: split the long requests too, within the
+        // items a workspace holds (kTargetItems beyond one item per request and KV head)
+        const int per_head = max(1, kTargetItems / Hkv);
+        int t2 = (s_misc[0] + per_head - 1) / per_head;
+        const int t_cap = (s_misc[4] + kMaxSplits - 1) / kMaxSplits;
+        if (t2 < t_cap) t2 = t_cap;
+        if (t2 < kMinTilesPerSplit) t2 = kMinTilesPerSplit;
+        if (t2 < t) t = t2;
+      }
+      s_misc[1] = t;
+    }
     __syncthreads();
     T = s_misc[1];
     if (wave == 0) {

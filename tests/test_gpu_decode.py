@@ -313,6 +313,33 @@ def test_large_batch_all_views_with_selector():
         assert np.array_equal(bf16_tensor_to_bits(kr)[0], kn[b]) and np.array_equal(bf16_tensor_to_bits(vr)[0], vn[b])
 
 
+def test_large_ragged_batch_balanced_order():
+    # above 64 requests with ragged lengths (log-uniform 16..20000): the workgroup plan splits
+    # the long requests too and runs the items in the balanced order (full-size splits, then
+    # last splits largest first, grid rounds alternating direction); every request's output
+    # and commit against the oracle, so a split run twice or not at all would show
+    from sparse_kv_recall_amd import ops
+    Hq, Hkv = 8, 2
+    g = np.random.default_rng(67)
+    B = 80
+    ns = [int(x) for x in np.floor(np.exp(g.uniform(np.log(16), np.log(20000), size=B)))]
+    ns[:3] = [20000, 1, 17]
+    hc = HostCache(Hq, Hkv, ns, seed=68)
+    q = _q(Hq, B, seed=69)
+    kn = rand_bits(rng.mix_key(906, 1), B, Hkv)
+    vn = rand_bits(rng.mix_key(906, 2), B, Hkv)
+    out = ops.oda_decode_full(torch.as_tensor(q, device="cuda"), hc.kv, bits_to_bf16_tensor(kn),
+                              bits_to_bf16_tensor(vn)).cpu().numpy()
+    for b, n in enumerate(ns):
+        k, v = hc.k[b].copy(), hc.v[b].copy()
+        oracle.oda.commit(k, v, n, kn[b], vn[b])
+        keys = keysets.full_keys(n)
+        ref = attention.attend(q[b], k, v, keys, SCALE)
+        check_tight(out[b], ref, q[b], k, v, keys, SCALE, what="b=%d n=%d" % (b, n))
+        kr, vr = ops.kv_read(hc.kv, b, n - 1, 1)
+        assert np.array_equal(bf16_tensor_to_bits(kr)[0], kn[b]) and np.array_equal(bf16_tensor_to_bits(vr)[0], vn[b])
+
+
 def test_maximum_batch():
     # 1024 requests (the library's maximum batch), short ragged histories
     from sparse_kv_recall_amd import ops
