@@ -176,3 +176,74 @@ def test_decode_from_projection_batch(view):
         keys = keysets.local_keys(n) if view == "local" else keysets.full_keys(n)
         ref = attention.attend(q, hk, hv, keys, SCALE)
         check_tight(got[b], ref, q, hk, hv, keys, SCALE, what="%s from projection b=%d n=%d" % (view, b, n))
+
+
+def test_host_routed_model_equals_one_graph():
+    """The weight-bearing step with the recall pass routed on the host (two graphs split at
+    the recall head's gate, the select in both branches) against the one-graph step: the
+    same launches in the same order, so every step's selected and Local final hidden
+    states and every committed slot are bit-identical, and the recall graph runs exactly
+    on the steps whose gate is set."""
+    import numpy as np
+    import torch
+    from sparse_kv_recall_amd import ops
+    from sparse_kv_recall_amd.model import DecoderShape, ODADecoder
+    from sparse_kv_recall_amd.stack import HostRoutedStep, capture_graph
+    wl = decoder_small(steps=12)
+    runs = []
+    for host in (False, True):
+        mb = wl.max_blocks
+        bt = torch.arange(mb, dtype=torch.int32, device="cuda")[None]
+        seq = torch.full((1,), wl.H0, dtype=torch.int32, device="cuda")
+        caches = [ops.PagedKVCache(mb, 1, wl.q_heads, wl.kv_heads, mb, block_tables=bt, seq_lens=seq)
+                  for _ in range(wl.layers)]
+        for l, c in enumerate(caches):
+            k = wl.hist_bits("k", l, 0, wl.H0)
+            v = wl.hist_bits("v", l, 0, wl.H0)
+            ops.kv_write(c, 0, 0, torch.as_tensor(k.view(np.int16), device="cuda").view(torch.bfloat16),
+                         torch.as_tensor(v.view(np.int16), device="cuda").view(torch.bfloat16))
+        shape = DecoderShape(wl.layers, wl.hidden, wl.q_heads, wl.kv_heads, wl.intermediate, wl.vocab,
+                             wl.recall_hidden, wl.eps, wl.rope_base)
+        m = ODADecoder(shape, wl.device_weights(), caches, wl.sinks, wl.window)
+        tokens = torch.as_tensor(wl.tokens.astype(np.int64), device="cuda")
+        t_idx = torch.zeros(1, dtype=torch.int64, device="cuda")
+
+        def feed():
+            m.token.copy_(torch.index_select(tokens, 0, t_idx))
+            seq.add_(1)
+            t_idx.add_(1)
+
+        def first():
+            feed()
+            m.local_pass()
+            m.recall_gate(wl.theta)
+
+        def select():
+            ops.select(m.gate, m.final_full, m.h_local_final, m.h_prev)
+
+        def recall():
+            m.recall_pass(gated=True)
+            select()
+
+        def one_graph():
+            first()
+            recall()
+
+        step = HostRoutedStep(first, recall, m.gate, skip=select) if host else capture_graph(one_graph)
+        states, ran = [], []
+        for _ in range(wl.steps):
+            r = step.replay()
+            torch.cuda.synchronize()
+            states.append((m.h_prev.clone(), m.h_local_final.clone(), int(m.gate[0].item())))
+            ran.append(r)
+        slots = [ops.kv_read(c, 0, wl.H0, wl.steps) for c in caches]
+        runs.append((states, ran, slots))
+    (s0, _, k0), (s1, ran1, k1) = runs
+    gates = [g for _, _, g in s0]
+    assert 0 < sum(gates) < wl.steps
+    for t in range(wl.steps):
+        assert torch.equal(s0[t][0], s1[t][0]) and torch.equal(s0[t][1], s1[t][1]), t
+        assert s0[t][2] == s1[t][2] and ran1[t] == bool(s1[t][2]), t
+    for (ka, va), (kb, vb) in zip(k0, k1):
+        assert torch.equal(ka.view(torch.int16), kb.view(torch.int16))
+        assert torch.equal(va.view(torch.int16), vb.view(torch.int16))
