@@ -25,6 +25,12 @@
 //    four 16-lane rows with permlane swaps; waves combine through LDS; splits are merged by
 //    the last workgroup to finish (atomic ticket per (request, KV head)) in registers,
 //    in a fixed split order, so results are deterministic.
+//  * Instances (decode_kernel<view, gated, single request, q/k finish, balanced order>):
+//    one request runs straight-line code; the q/k-finish instances take a layer's raw
+//    q/k/v projection and apply the per-head RMSNorm and rotary positions while staging
+//    (Qwen3-family layer, for the weight-bearing decode step); the balanced-order
+//    instances (the views launch, batches above 64) run ragged batches' work items
+//    longest first, which changes which workgroup runs what, never the results.
 #include <math.h>
 
 #include <algorithm>

@@ -18,7 +18,10 @@
 // (deterministic). Residual add and the SwiGLU product (gate and up rows paired in one
 // wave) are fused into the store. The q/k/v projection is one such GEMV followed by a
 // per-head kernel for the q/k RMS norm and the rotary pairs (i, i + 64), with rotary
-// angles computed in fp64.
+// angles computed in fp64 (sk_qkv_rope); the decode launches can instead apply that
+// per-head finish themselves to the GEMV's raw output (oda_decode_*_qkv, decode.hip).
+// Each thread requests its share of the input vector before the weights: loads complete
+// in issue order, so the wait for the input then leaves the weight loads in flight.
 #include <math.h>
 
 #include "sk_internal.h"
