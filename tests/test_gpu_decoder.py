@@ -70,7 +70,8 @@ def test_qkv_rope_two_positions():
             assert np.all(np.abs(gt - ref) <= np.abs(ref) * 2.0 ** -7 + 1e-6), call
 
 
-@pytest.mark.parametrize("view,G,n", [("local", 2, 131072), ("full", 4, 2999), ("local", 8, 6), ("full", 1, 40)])
+@pytest.mark.parametrize("view,G,n", [("local", 2, 131072), ("full", 4, 2999), ("local", 8, 6), ("full", 1, 40),
+                                      ("full", 2, 1), ("local", 4, 17)])
 def test_decode_from_projection(view, G, n):
     """The Local / Full views from a raw q/k/v projection (per-head q/k RMSNorm and the
     rotation at n - 1 applied inside the decode launch) against the fp64 layer pieces of
