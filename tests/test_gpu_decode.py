@@ -313,17 +313,18 @@ def test_large_batch_all_views_with_selector():
         assert np.array_equal(bf16_tensor_to_bits(kr)[0], kn[b]) and np.array_equal(bf16_tensor_to_bits(vr)[0], vn[b])
 
 
-def test_large_ragged_batch_balanced_order():
-    # above 64 requests with ragged lengths (log-uniform 16..20000): the workgroup plan splits
+@pytest.mark.parametrize("B,n_max", [(80, 20000), (256, 1500), (257, 1500)])
+def test_large_ragged_batch_balanced_order(B, n_max):
+    # above 64 requests with ragged lengths (log-uniform 16..n_max): the workgroup plan splits
     # the long requests too and runs the items in the balanced order (full-size splits, then
     # last splits largest first, grid rounds alternating direction); every request's output
-    # and commit against the oracle, so a split run twice or not at all would show
+    # and commit against the oracle, so a split run twice or not at all would show. 256
+    # requests is the largest batch ranked in LDS for that order; 257 run in workgroup order.
     from sparse_kv_recall_amd import ops
     Hq, Hkv = 8, 2
     g = np.random.default_rng(67)
-    B = 80
-    ns = [int(x) for x in np.floor(np.exp(g.uniform(np.log(16), np.log(20000), size=B)))]
-    ns[:3] = [20000, 1, 17]
+    ns = [int(x) for x in np.floor(np.exp(g.uniform(np.log(16), np.log(n_max), size=B)))]
+    ns[:3] = [n_max, 1, 17]
     hc = HostCache(Hq, Hkv, ns, seed=68)
     q = _q(Hq, B, seed=69)
     kn = rand_bits(rng.mix_key(906, 1), B, Hkv)

@@ -1,8 +1,8 @@
 """GPU parity of oda_decode_views, the per-request views of a batch in one launch: each
 running request against the fp64 oracle for its view (Full, Local, or its gathered block
 list), with fused commits; requests whose view value names no view keep their output rows
-and their slot n-1. Batches of 12 and 64 (per-wave planning) and 65 and 100 (workgroup
-planning). With equal lengths and one view for every request the plan and the tile order
+and their slot n-1. Batches of 12 and 64 (per-wave planning), 65 and 100 (workgroup
+planning), 256 (the largest batch ranked for the balanced order) and 257 (workgroup order). With equal lengths and one view for every request the plan and the tile order
 are those of the single-view launch, so the outputs are bit-identical to it."""
 
 import numpy as np
@@ -30,10 +30,24 @@ def _mask_words(kept_per_req, max_blocks):
                                                    (100, 3, 40, 16, 4), (12, 4, 2048, 32, 2), (70, 4, 500, 32, 2)])
 def test_views_one_launch(B, sinks, window, Hq, Hkv):
     # query groups of 4 and of 16 (the merge then works on four output elements per thread)
-    from sparse_kv_recall_amd import ops
     g = np.random.default_rng(90 + B + Hkv)
     ns = [int(x) for x in g.integers(1, 6000, size=B)]
     ns[:5] = [1, 16, 17, 2052, 5999]
+    _views_case(g, B, ns, sinks, window, Hq, Hkv)
+
+
+@pytest.mark.parametrize("B", [256, 257])
+def test_views_balanced_order_batch_bound(B):
+    # 256 requests: the largest batch ranked in LDS for the balanced order; 257: the plain
+    # workgroup order. Log-uniform lengths 1..1500, so the long requests take several splits.
+    g = np.random.default_rng(80 + B)
+    ns = [int(x) for x in np.floor(np.exp(g.uniform(0.0, np.log(1500), size=B)))]
+    ns[:5] = [1, 16, 17, 1500, 1499]
+    _views_case(g, B, ns, 4, 300, 8, 2)
+
+
+def _views_case(g, B, ns, sinks, window, Hq, Hkv):
+    from sparse_kv_recall_amd import ops
     hc = HostCache(Hq, Hkv, ns, seed=91)
     # views: 0 Local, 1 Full, 2 blocks, 5 none (the request does not run)
     view = g.choice([0, 1, 2, 5], size=B, p=[0.3, 0.3, 0.3, 0.1]).astype(np.int32)
