@@ -46,6 +46,8 @@ constexpr int kThreads = 64 * kWavesPerWG;
 constexpr int kMinTilesPerSplit = 8;                   // small launches: many short splits
 constexpr int kMaxSplits = 256;                     // splits per (request, KV head)
 constexpr int kGridCap = 256;                       // decode workgroups per launch (one per CU)
+constexpr int kBufferFlags = 0x00020000;  // raw buffer access, 32-bit data format (gfx9 word 3)
+constexpr int kNonTemporal = 2;           // buffer load cache policy: non-temporal
 constexpr int kMergeBatch = 48;                     // split accumulators loaded together in the merge
 // Per-request views in one launch: work items fill at most this many rounds of the grid
 // (4 x 256 workgroups = the items a workspace holds at the largest query group). Measured
@@ -544,6 +546,24 @@ __device__ inline void load_tile(const uint8_t* kpool, const uint8_t* vpool, int
   }
 }
 
+// The tile at phys, or zeros without a memory access when ok is false: the loads go
+// through buffer ranges that are empty then, so the number of loads in flight (which the
+// waits count) does not depend on a branch.
+__device__ inline void load_tile_if(const uint8_t* kpool, const uint8_t* vpool, int phys, int g, int Hkv, int lane,
+                                    bool ok, u32x4 (&k)[4], u32x4 (&v)[4]) {
+  const size_t base = (size_t(phys) * Hkv + g) * kTileBytes;
+  const int bytes = __builtin_amdgcn_readfirstlane(ok ? int(kTileBytes) : 0);
+  const __amdgpu_buffer_rsrc_t rk =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(kpool + base), 0, bytes, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t rv =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(vpool + base), 0, bytes, kBufferFlags);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    k[c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, 16 * lane + 1024 * c, 0, kNonTemporal));
+    v[c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, 16 * lane + 1024 * c, 0, kNonTemporal));
+  }
+}
+
 // HAS_SEL: requests are filtered by sel[b] == sel_value (gated / per-request views).
 // Without a selector a separate instance runs, so a profile tells gated launches
 // (which exit at once on non-recall steps) apart from unconditional ones.
@@ -987,6 +1007,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
       s_q[qc * 128 + lane] = (qcol < G) ? __builtin_bit_cast(u32x4, oh) : z;
       s_q[qc * 128 + 64 + lane] = (qcol < G) ? __builtin_bit_cast(u32x4, ol) : z;
     }
+    if constexpr (MODE == kLocal) {
+      // the wave's second tile too, before the barrier (its waves hold one or two tiles)
+      load_tile_if(kpool, vpool, __builtin_amdgcn_readlane(dphys, 1), g, Hkv, lane, loop_tiles >= 2, k1, v1);
+    }
     __syncthreads();
 
     float m_run = -INFINITY, l_run = 0.f;
@@ -1046,8 +1070,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
     // chunk is therefore peeled, so that no fetch follows it. (Clamping that fetch to the
     // chunk's last tile instead re-requests a tile whose first request is still in flight,
     // and both go to HBM: 15 % more traffic for splits of 34 tiles, i.e. 4 or 5 per wave.)
-    // The Local view keeps the clamped form: its waves hold one tile at batch 1, and the
-    // peeled pair's larger code cost it 0.13 us per launch.
+    // The Local view's waves hold one or two tiles at batch 1: it requests a wave's second
+    // tile before the staging barrier, together with the first (the wave holding two
+    // tiles was the last to finish: its second request waited for the barrier), and
+    // fetches past the chunk's end through empty buffer ranges instead of peeling the
+    // last pair (whose larger code cost it 0.13 us per launch).
     for (int c0 = 0; c0 < loop_tiles; c0 += 64) {
       const int nt = min(64, loop_tiles - c0);
       const int last = nt - 1;
@@ -1059,13 +1086,17 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
       }
       int j = 0;
       if constexpr (MODE == kLocal) {
+#define SK_FETCH_IF(K, V, J) \
+  load_tile_if(kpool, vpool, __builtin_amdgcn_readlane(dphys, min((J), last)), g, Hkv, lane, (J) <= last, K, V)
+        if (c0 > 0) SK_FETCH_IF(k1, v1, 1);  // the first chunk's was requested before the staging barrier
         for (; j + 2 <= nt; j += 2) {
-          SK_FETCH(k1, v1, j + 1);
           process(k0, v0, SK_LOHI(j));
-          SK_FETCH(k0, v0, j + 2);
+          SK_FETCH_IF(k0, v0, j + 2);
           process(k1, v1, SK_LOHI(j + 1));
+          SK_FETCH_IF(k1, v1, j + 3);
         }
         if (j < nt) process(k0, v0, SK_LOHI(j));
+#undef SK_FETCH_IF
       } else {
         for (; j + 2 < nt; j += 2) {
           SK_FETCH(k1, v1, j + 1);
