@@ -914,6 +914,15 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
       dphys = tt.phys;
       dlohi = tt.lo | (tt.hi << 8);
     };
+    // List views: the current token's block and the list's last entry, requested with the
+    // descriptors (whose wait then covers them) rather than after them.
+    int lk_token = 0, lk_last = 0;
+    if ((MODE == kList || MODE == kViews) && (QK || P.k_new)) {
+      if (MODE == kList || view == kList) {
+        lk_token = P.kv.block_tables[int64_t(b) * maxb + (n - 1) / kBlock];
+        lk_last = P.list_phys[int64_t(b) * maxb + tiles_b - 1];
+      }
+    }
     load_desc(0);
 
     // q rows of the G heads of KV head g for the operand staging below. Waves 0-3 load
@@ -949,8 +958,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
         if (last_blk == (n - 1) / kBlock) commit_tile = tiles_b - 1;
         else if (split == 0 && wave == 0) commit_token_lanes(P, b, g, n, lane);
       } else {
-        int last_phys = P.kv.block_tables[int64_t(b) * maxb + (n - 1) / kBlock];
-        if (P.list_phys[int64_t(b) * maxb + tiles_b - 1] == last_phys) commit_tile = tiles_b - 1;
+        if (lk_last == lk_token) commit_tile = tiles_b - 1;
         else if (split == 0 && wave == 0) commit_token_lanes(P, b, g, n, lane);
       }
     }
