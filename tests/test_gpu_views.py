@@ -43,19 +43,24 @@ def test_views_balanced_order_batch_bound(B):
     g = np.random.default_rng(80 + B)
     ns = [int(x) for x in np.floor(np.exp(g.uniform(0.0, np.log(1500), size=B)))]
     ns[:5] = [1, 16, 17, 1500, 1499]
-    _views_case(g, B, ns, 4, 300, 8, 2)
+    _views_case(g, B, ns, 4, 300, 8, 2, drop_last_every=3)
 
 
-def _views_case(g, B, ns, sinks, window, Hq, Hkv):
+def _views_case(g, B, ns, sinks, window, Hq, Hkv, drop_last_every=0):
+    # drop_last_every = k: every k-th request's kept blocks leave out the block of position
+    # n-1, so its list view does not attend the current token but still commits it
     from sparse_kv_recall_amd import ops
     hc = HostCache(Hq, Hkv, ns, seed=91)
     # views: 0 Local, 1 Full, 2 blocks, 5 none (the request does not run)
     view = g.choice([0, 1, 2, 5], size=B, p=[0.3, 0.3, 0.3, 0.1]).astype(np.int32)
     view[:4] = [0, 1, 2, 5]
     kept = []
-    for n in ns:
+    for b, n in enumerate(ns):
         nb = (n + 15) // 16
-        kept.append(sorted(set(g.choice(nb, size=max(1, nb // 4), replace=False).tolist()) | {nb - 1}))
+        ks = set(g.choice(nb, size=max(1, nb // 4), replace=False).tolist()) | {nb - 1}
+        if drop_last_every and b % drop_last_every == 1 and nb > 1:
+            ks = (ks - {nb - 1}) or {0}
+        kept.append(sorted(ks))
     mask = torch.as_tensor(_mask_words(kept, hc.max_blocks).view(np.int32), device="cuda")
     q = rand_f32(rng.mix_key(992, B), (B, Hq, 128), 1.0)
     kn = rand_bits(rng.mix_key(993, B, 1), B, Hkv)
