@@ -48,6 +48,7 @@ constexpr int kMaxSplits = 256;                     // splits per (request, KV h
 constexpr int kGridCap = 256;                       // decode workgroups per launch (one per CU)
 constexpr int kBufferFlags = 0x00020000;  // raw buffer access, 32-bit data format (gfx9 word 3)
 constexpr int kNonTemporal = 2;           // buffer load cache policy: non-temporal
+constexpr int kTicketStride = 16;                   // words between ticket counters (small launches)
 constexpr int kMergeBatch = 48;                     // split accumulators loaded together in the merge
 // Per-request views in one launch: work items fill at most this many rounds of the grid
 // (4 x 256 workgroups = the items a workspace holds at the largest query group). Measured
@@ -857,6 +858,12 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
   // merges a (request, KV head) does not need to be the one that wrote its partials.
   const int item_first = int(blockIdx.x);
 
+  // Ticket counters kTicketStride words apart (a 64-byte line each) when the launch's
+  // (request, KV head) pairs fit the ticket region that way: the ticket atomics of all
+  // splits arrive together at the end of a launch, and counters sharing a line are updated
+  // one after another (measured: Local view 9.43 -> 9.20 us, 12.5 % block list 17.6 ->
+  // 16.8 us per launch).
+  const int ticket_stride = (int64_t(B) * Hkv * kTicketStride <= kMaxTickets) ? kTicketStride : 1;
   const int ncol = lane & 15, grp = lane >> 4;
   const uint8_t* kpool = reinterpret_cast<const uint8_t*>(P.kv.k_pool);
   const uint8_t* vpool = reinterpret_cast<const uint8_t*>(P.kv.v_pool);
@@ -1186,7 +1193,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
       wait_stores();
       __syncthreads();
       if (tid == 0) {
-        unsigned prev = atomicAdd(&P.tickets[b * Hkv + g], 1u);
+        unsigned prev = atomicAdd(&P.tickets[(b * Hkv + g) * ticket_stride], 1u);
         s_misc[3] = (prev == unsigned(splits - 1));
       }
       __syncthreads();
@@ -1216,7 +1223,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
           }
           P.out[(int64_t(b) * Hq + g * G + h) * kHeadDim + (idx & (kHeadDim - 1))] = (L > 0.f) ? A / L : 0.f;
         }
-        if (tid == 0) P.tickets[b * Hkv + g] = 0u;
+        if (tid == 0) P.tickets[(b * Hkv + g) * ticket_stride] = 0u;
       }
     }
     __syncthreads();
