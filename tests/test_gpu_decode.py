@@ -341,6 +341,39 @@ def test_large_ragged_batch_balanced_order(B, n_max):
         assert np.array_equal(bf16_tensor_to_bits(kr)[0], kn[b]) and np.array_equal(bf16_tensor_to_bits(vr)[0], vn[b])
 
 
+@pytest.mark.parametrize("B", [128, 129])
+def test_ticket_stride_boundary(B):
+    # Split tickets sit 16 words apart while the launch's (request, KV head) pairs fit the
+    # ticket region that way (up to 1024 pairs), one word apart beyond. 128 requests at 8 KV
+    # heads are exactly 1024 pairs, 129 are past it. The last requests are the longest, so
+    # they take several splits and the highest ticket counters; every output and commit is
+    # checked against the oracle, and a second launch on the same workspace checks that the
+    # counters were left at zero.
+    from sparse_kv_recall_amd import ops
+    Hq, Hkv = 32, 8
+    g = np.random.default_rng(300 + B)
+    ns = [int(x) for x in np.floor(np.exp(g.uniform(np.log(16), np.log(1200), size=B)))]
+    ns[-3:] = [5000, 3001, 2100]
+    hc = HostCache(Hq, Hkv, ns, seed=301)
+    q = _q(Hq, B, seed=302)
+    kn = rand_bits(rng.mix_key(907, 1), B, Hkv)
+    vn = rand_bits(rng.mix_key(907, 2), B, Hkv)
+    ws = ops.workspace(B, Hq)
+    qt = torch.as_tensor(q, device="cuda")
+    outs = [ops.oda_decode_full(qt, hc.kv, bits_to_bf16_tensor(kn), bits_to_bf16_tensor(vn), ws=ws).cpu().numpy()
+            for _ in range(2)]
+    assert np.array_equal(outs[0], outs[1])
+    for b, n in enumerate(ns):
+        k, v = hc.k[b].copy(), hc.v[b].copy()
+        oracle.oda.commit(k, v, n, kn[b], vn[b])
+        keys = keysets.full_keys(n)
+        ref = attention.attend(q[b], k, v, keys, SCALE)
+        check_tight(outs[0][b], ref, q[b], k, v, keys, SCALE, what="b=%d n=%d" % (b, n))
+        kr, vr = ops.kv_read(hc.kv, b, n - 1, 1)
+        assert np.array_equal(bf16_tensor_to_bits(kr)[0], kn[b]) and np.array_equal(bf16_tensor_to_bits(vr)[0], vn[b])
+    assert ops.workspace_error(ws) == 0
+
+
 def test_maximum_batch():
     # 1024 requests (the library's maximum batch), short ragged histories
     from sparse_kv_recall_amd import ops
