@@ -116,11 +116,13 @@ class OdaStackRun:
         self._first()
         self._recall()
 
-    def run(self, full_check_steps=None, check_feed_steps=(0,), commit_all_layers=False):
+    def run(self, full_check_steps=None, check_feed_steps=(0,), commit_all_layers=False, full_sample=None):
         """full_check_steps: recall steps whose Full outputs are checked (None: all);
         commit_all_layers: also check the committed slots of every layer (not only the
         mirrored ones) against the selected pass's candidates regenerated from the
-        seeded streams."""
+        seeded streams; full_sample: a seeded numpy Generator, with which every other
+        recall step checks the query heads of one KV head of one mirrored layer (drawn
+        from it), the oracle computing that head group alone."""
         wl, rep = self.wl, Report()
         H0 = int(wl.H0[0])
         gates = []
@@ -157,6 +159,10 @@ class OdaStackRun:
             gates.append(bool(gate))
             out_l = self.stack.out.cpu().numpy() if self.check_layers else None
             out_f = self.stack.out_full.cpu().numpy() if (gate and self.check_layers) else None
+            sampled = None  # (layer, KV head) whose Full rows this recall step checks
+            if gate and full_sample is not None and full_check_steps is not None and t not in full_check_steps:
+                sampled = (self.check_layers[int(full_sample.integers(len(self.check_layers)))],
+                           int(full_sample.integers(wl.Hkv)))
             for l in self.check_layers:
                 hk, hv = self.mirror[l]
                 qL = wl.cand_q(t, l, 0, 0)
@@ -172,6 +178,12 @@ class OdaStackRun:
                         rep.add(out_f[l, 0], oF, "recall t=%d layer=%d" % (t, l))
                     else:
                         oracle.oda.commit(hk, hv, n, kF, vF)
+                        if sampled is not None and l == sampled[0]:
+                            G, g = wl.Hq // wl.Hkv, sampled[1]
+                            keys = (keysets.local_keys(n, wl.sinks, wl.window) if l in self.local_only
+                                    else keysets.full_keys(n))
+                            oF = attention.attend(qF[g * G:(g + 1) * G], hk[:, g:g + 1], hv[:, g:g + 1], keys, SCALE)
+                            rep.add(out_f[l, 0, g * G:(g + 1) * G], oF, "recall t=%d layer=%d kv head %d" % (t, l, g))
                     if self.rpass == 0 and l in self.local_only:
                         # the same kernel on the same inputs: the recall result is the Local one
                         assert np.array_equal(out_f[l, 0], out_l[l, 0]), (t, l)

@@ -161,6 +161,22 @@ def test_gqa_grouping_is_contiguous():
             assert np.allclose(o[h], (h * Hkv) // Hq + 1, rtol=0, atol=1e-13)
 
 
+def test_head_group_alone_equals_its_rows():
+    # the query heads of KV head g read KV head g only: attending that group alone (its G
+    # query rows against KV head g's keys and values) gives the same rows as all heads
+    # together. The 128K parity run checks sampled head groups this way; a mapping that
+    # mixed KV heads (a transposed or strided grouping) would differ here.
+    for Hq, Hkv in ((32, 8), (8, 2), (16, 16)):
+        n = 300
+        q, k, v = rand_case(n, Hq, Hkv, seed=7 * Hq + Hkv)
+        keys = keysets.full_keys(n)
+        full = attention.attend(q, k, v, keys, SCALE)
+        G = Hq // Hkv
+        for g in range(Hkv):
+            alone = attention.attend(q[g * G:(g + 1) * G], k[:, g:g + 1], v[:, g:g + 1], keys, SCALE)
+            assert np.allclose(alone, full[g * G:(g + 1) * G], rtol=0, atol=1e-14)
+
+
 def brute_force(q, k, v, keys, scale):
     """Scalar loops with math.exp; no numpy arithmetic."""
     Hq, D = q.shape
