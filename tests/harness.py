@@ -355,7 +355,11 @@ class RaggedRun:
         f.step()
         self.rb.step(f.q[0, 0], f.k[0, 0], f.v[0, 0], f.scores, self.wl.theta)
 
-    def run(self, check_steps=None):
+    def run(self, check_steps=None, commit_all_requests=False):
+        """check_steps: steps whose outputs of the mirrored requests are checked (None:
+        all); commit_all_requests: also check every request's committed slots (each view
+        commits the request's candidate) against the candidates regenerated from the
+        seeded streams."""
         wl, rep = self.wl, Report()
         for t in range(self.steps):
             self.graph.replay() if self.graph is not None else self._step()
@@ -401,6 +405,14 @@ class RaggedRun:
             k, v = ops.kv_read(self.cache, r, H0, self.steps)
             assert np.array_equal(bf16_tensor_to_bits(k), hk[H0:H0 + self.steps]), r
             assert np.array_equal(bf16_tensor_to_bits(v), hv[H0:H0 + self.steps]), r
+        if commit_all_requests:
+            for r in range(wl.batch):
+                k, v = ops.kv_read(self.cache, r, int(wl.H0[r]), self.steps)
+                kb, vb = bf16_tensor_to_bits(k), bf16_tensor_to_bits(v)
+                for t in range(self.steps):
+                    ke, ve = wl.cand_kv(t, 0, 0, r)
+                    assert np.array_equal(kb[t], ke) and np.array_equal(vb[t], ve), (r, t)
+            rep.commit_layers = wl.batch
         return rep
 
 

@@ -68,15 +68,17 @@ def test_da_32k_every_step(in_kernel_rewrite):
 @pytest.mark.slow
 @pytest.mark.parametrize("one_launch", [True, False])
 def test_ragged32_sampled_requests(one_launch):
-    # the three views in one launch (oda_decode_views), and one selector launch per view
+    # the three views in one launch (oda_decode_views), and one selector launch per view;
+    # every request's view decision on every step, the outputs of six requests on every
+    # eighth step, and every request's committed slots on every step
     from tests.harness import RaggedRun
     wl = workloads.ragged32()
     order = np.argsort(wl.H0)
     check = sorted(set([int(order[0]), int(order[-1]), int(order[len(order) // 2])] +
                        [int(x) for x in np.random.default_rng(4).choice(wl.batch, size=3, replace=False)]))
     rep = RaggedRun(wl, check_requests=check, one_launch=one_launch).run(
-        check_steps=set(range(0, wl.steps, 8)) | {wl.steps - 1})
-    assert rep.decisions == wl.batch * wl.steps
+        check_steps=set(range(0, wl.steps, 8)) | {wl.steps - 1}, commit_all_requests=True)
+    assert rep.decisions == wl.batch * wl.steps and rep.commit_layers == wl.batch
     print("ragged32 (one launch: %s): requests %s, full views %d of %d, max-abs %.2e, row-rel %.2e"
           % (one_launch, check, rep.recalls, rep.decisions, rep.max_abs, rep.max_row_rel))
 
