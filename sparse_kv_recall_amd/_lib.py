@@ -44,6 +44,11 @@ _SIGNATURES = {
                                    c_void_p, c_int32, c_void_p, c_void_p, c_size_t, c_void_p]),
     "oda_decode_full": (c_int32, [c_void_p, PagedKVStruct, c_void_p, c_void_p, c_float, c_void_p, c_int32,
                                   c_void_p, c_void_p, c_size_t, c_void_p]),
+    "oda_local_tiles_bytes": (c_size_t, [c_int32, c_int32, c_int32, c_int32]),
+    "oda_local_tiles": (c_int32, [PagedKVStruct, c_int32, c_int32, c_void_p, c_size_t, c_void_p]),
+    "oda_decode_local_tiles": (c_int32, [c_void_p, PagedKVStruct, c_void_p, c_size_t, c_void_p, c_void_p, c_int32,
+                                         c_int32, c_float, c_void_p, c_int32, c_void_p, c_void_p, c_size_t,
+                                         c_void_p]),
     "oda_decode_local_qkv": (c_int32, [c_void_p, c_void_p, c_void_p, c_float, c_float, PagedKVStruct, c_int32, c_int32,
                                        c_float, c_void_p, c_int32, c_void_p, c_void_p, c_size_t, c_void_p]),
     "oda_decode_full_qkv": (c_int32, [c_void_p, c_void_p, c_void_p, c_float, c_float, PagedKVStruct, c_float,

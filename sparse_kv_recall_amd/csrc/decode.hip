@@ -91,6 +91,11 @@ struct DecodeParams {
   const uint16_t* g_k;
   float qk_eps;
   float rope_base;
+  // Local view from a step's tile table (oda_local_tiles): per request, the length the
+  // table was built for, then the physical block of each Local tile; tab_tiles = the
+  // largest Local tile count (its rows hold 1 + tab_tiles words). Null: no table.
+  const int32_t* tab;
+  int tab_tiles;
 };
 
 struct Tile {
@@ -178,6 +183,24 @@ __device__ inline int request_tiles(const DecodeParams& P, int b, int n, int lis
   return min(max(listed, 0), P.kv.max_blocks);
 }
 
+// Local view tile i at length n: returns its logical block and sets [lo, hi), the valid
+// positions in it (the sinks' blocks first, then the window's, cut at both ends).
+__device__ inline int local_tile(const DecodeParams& P, int n, int i, int& lo, int& hi) {
+  const int s_end = min(P.sinks, n);
+  const int st = (s_end + kBlock - 1) / kBlock;
+  if (i < st) {
+    lo = 0;
+    hi = min(kBlock, s_end - kBlock * i);
+    return i;
+  }
+  const int a = max(s_end, n - P.window);
+  const int j = i - st;
+  const int lb = a / kBlock + j;
+  lo = (j == 0) ? (a % kBlock) : 0;
+  hi = min(kBlock, n - kBlock * lb);
+  return lb;
+}
+
 template <int MODE>
 __device__ inline Tile tile_at(const DecodeParams& P, int b, int n, int i, int view = MODE) {
   Tile t;
@@ -188,21 +211,7 @@ __device__ inline Tile tile_at(const DecodeParams& P, int b, int n, int i, int v
     t.hi = min(kBlock, n - kBlock * i);
     t.phys = bt[i];
   } else if (m == kLocal) {
-    int s_end = min(P.sinks, n);
-    int st = (s_end + kBlock - 1) / kBlock;
-    int lb;
-    if (i < st) {
-      lb = i;
-      t.lo = 0;
-      t.hi = min(kBlock, s_end - kBlock * i);
-    } else {
-      int a = max(s_end, n - P.window);
-      int j = i - st;
-      lb = a / kBlock + j;
-      t.lo = (j == 0) ? (a % kBlock) : 0;
-      t.hi = min(kBlock, n - kBlock * lb);
-    }
-    t.phys = bt[lb];
+    t.phys = bt[local_tile(P, n, i, t.lo, t.hi)];
   } else if (MODE == kDecl) {
     const Runs r = declared_runs(P, b, n);
     const int lb = (i < r.l0) ? r.s0 + i : r.s1 + (i - r.l0);
@@ -221,6 +230,30 @@ __device__ inline Tile tile_at(const DecodeParams& P, int b, int n, int i, int v
     t.lo = t.hi = 0;
   }
   return t;
+}
+
+// The single-request plan for `tiles` tiles on `slots` split slots per KV head: tiles per
+// split T (enough that the splits fit the slots after a reserve of one for rounding, at
+// least kMinTilesPerSplit, at most kMaxSplits splits) and the splits; when those splits
+// would leave more than a quarter of the slots idle, the smallest split size from
+// tiles / slots up (its splits always fit the slots). The small-batch plan for one request.
+__device__ inline void single_plan(int tiles, int slots, int& T, int& splits) {
+  int budget = slots - (tiles > 0 ? 1 : 0);
+  if (budget < 1) budget = 1;
+  T = (tiles + budget - 1) / budget;
+  const int T_cap = (tiles + kMaxSplits - 1) / kMaxSplits;
+  if (T < T_cap) T = T_cap;
+  if (T < kMinTilesPerSplit) T = kMinTilesPerSplit;
+  splits = (tiles + T - 1) / T;
+  if (4 * splits < 3 * slots) {
+    int t = (tiles + slots - 1) / slots;
+    if (t < T_cap) t = T_cap;
+    if (t < kMinTilesPerSplit) t = kMinTilesPerSplit;
+    if (t < T) {
+      T = t;
+      splits = (tiles + T - 1) / T;
+    }
+  }
 }
 
 __device__ inline bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
@@ -573,7 +606,7 @@ __device__ inline void load_tile_if(const uint8_t* kpool, const uint8_t* vpool, 
 // request alone in a batch on the same grid), computed on the uniform length alone: no
 // cross-lane reductions, scans or request search, which shortens the chain of
 // instructions before the first tile is requested.
-template <int MODE, bool HAS_SEL, bool SINGLE, bool QK = false, bool BAL = false>
+template <int MODE, bool HAS_SEL, bool SINGLE, bool QK = false, bool BAL = false, bool TAB = false>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
   constexpr int W = kWavesPerWG;
   extern __shared__ float smem[];
@@ -614,6 +647,22 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
   // round of loads (lanes past the batch read request 0 and ignore it).
   int l_len = 0, l_listed = 0, l_view = MODE;
   bool l_sel = true;
+  // Local view from a tile table (TAB, single request): the table's length and this
+  // wave's tile descriptors under the plan of the largest Local tile count (the plan of
+  // every length from sinks + window on, unless the window's alignment changes it),
+  // requested with the length, so that the first tiles can be requested once it arrives.
+  // The item body takes them when the length and the plan match, else it reads the block
+  // table as without a table.
+  int tab_phys = 0, tab_n = -1, tab_T = 0, tab_splits = 0;
+  if constexpr (TAB) {
+    single_plan(P.tab_tiles, int(gridDim.x) / Hkv, tab_T, tab_splits);
+    const int item = int(blockIdx.x);
+    if (item < tab_splits * Hkv) {
+      const int ti = (item % tab_splits) * tab_T + wave + lane * W;
+      tab_phys = P.tab[1 + min(ti, P.tab_tiles - 1)];
+    }
+    tab_n = __builtin_amdgcn_readfirstlane(P.tab[0]);
+  }
   if (SINGLE) {  // uniform values, one round of loads
     const int n0 = P.kv.seq_lens[0];
     const int listed0 = (MODE == kList) ? P.list_num[0] : 0;
@@ -675,19 +724,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
     const bool valid = n >= 1 && n <= maxb * kBlock;
     const int tiles = valid ? request_tiles<MODE>(P, 0, n, l_listed) : 0;
     if (blockIdx.x == 0 && wave == 0 && lane == 0 && (!valid || tiles == 0)) bad_request(0, n, valid);
-    T = split_size(tiles, tiles > 0 ? 1 : 0, tiles);
-    const int slots = int(gridDim.x) / Hkv;
-    int splits = (tiles + T - 1) / T;
-    if (4 * splits < 3 * slots) {
-      int t = (tiles + slots - 1) / slots;
-      const int t_cap = (tiles + kMaxSplits - 1) / kMaxSplits;
-      if (t < t_cap) t = t_cap;
-      if (t < kMinTilesPerSplit) t = kMinTilesPerSplit;
-      if (t < T) {
-        T = t;
-        splits = (tiles + T - 1) / T;
-      }
-    }
+    int splits;
+    single_plan(tiles, int(gridDim.x) / Hkv, T, splits);
     w_tiles = tiles;
     w_len = n;
     total_items = splits * Hkv;
@@ -930,7 +968,24 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
         lk_last = P.list_phys[int64_t(b) * maxb + tiles_b - 1];
       }
     }
-    load_desc(0);
+    bool from_tab = false;
+    if constexpr (TAB) from_tab = tab_n == n && T == tab_T && splits == tab_splits;
+    if (from_tab) {  // the table's blocks, checked as tile_at checks the block table's
+      int lo = 0, hi = 0, phys = 0;
+      if (lane < my_tiles) {
+        phys = tab_phys;
+        local_tile(P, n, t_begin + wave + lane * W, lo, hi);
+        if (phys < 0 || phys >= P.kv.num_phys_blocks) {
+          set_error(P.err, SK_DEVERR_BLOCK_ID);
+          phys = 0;
+          lo = hi = 0;
+        }
+      }
+      dphys = phys;
+      dlohi = lo | (hi << 8);
+    } else {
+      load_desc(0);
+    }
 
     // q rows of the G heads of KV head g for the operand staging below. Waves 0-3 load
     // them (wave c the dims of chunk c) and stage both bf16 parts; waves 4-7 request
@@ -1322,6 +1377,32 @@ __global__ __launch_bounds__(256) void gather_kernel(sk_paged_kv kv, const uint3
     num_kept[b] = s_prefix + s_wave[0] + s_wave[1] + s_wave[2] + s_wave[3];
 }
 
+// The largest Local tile count: the sinks' blocks, the window's (one more when it is not
+// block aligned), at most the block table's columns. A tile table row holds 1 + this words.
+int local_tiles_max(int sinks, int window, int max_blocks) {
+  const int64_t t = int64_t((sinks + kBlock - 1) / kBlock) + (int64_t(window) + kBlock - 1) / kBlock + 1;
+  return int(t < max_blocks ? t : max_blocks);
+}
+
+// One thread per (request, Local tile): the physical block of tile i of request b's Local
+// view at its current length (word 1 + i of its row; word 0: that length). Requests with an
+// invalid length get the length only (the decode launch reports them).
+__global__ __launch_bounds__(256) void local_tiles_kernel(sk_paged_kv kv, int sinks, int window, int row,
+                                                          int32_t* __restrict__ tab) {
+  const int b = blockIdx.y;
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  const int n = kv.seq_lens[b];
+  int32_t* t = tab + int64_t(b) * row;
+  if (i == 0) t[0] = n;
+  if (n < 1 || n > kv.max_blocks * kBlock) return;
+  DecodeParams P{};
+  P.sinks = sinks;
+  P.window = window;
+  if (i >= request_tiles<kLocal>(P, b, n, 0)) return;
+  int lo, hi;
+  t[1 + i] = kv.block_tables[int64_t(b) * kv.max_blocks + local_tile(P, n, i, lo, hi)];
+}
+
 // Argument checks of every decode launch; the workspace is checked by the caller.
 int check_decode(const float* q, const sk_paged_kv& kv, const void* k_new, const void* v_new, const float* out) {
   int st = check_kv(kv);
@@ -1368,7 +1449,8 @@ template <int MODE>
 int enqueue_decode(const float* q, sk_paged_kv kv, const void* k_new, const void* v_new, int sinks, int window,
                    float scale, const int32_t* sel, int sel_value, const int32_t* lp, const int32_t* lc,
                    const int32_t* ln, float* out, uint8_t* scratch, int32_t* err, hipStream_t stream,
-                   const int32_t* decl, int local_tokens, const QKFinish* qk = nullptr) {
+                   const int32_t* decl, int local_tokens, const QKFinish* qk = nullptr,
+                   const int32_t* tab = nullptr) {
   DecodeParams P;
   P.q = q;
   P.kv = kv;
@@ -1392,6 +1474,8 @@ int enqueue_decode(const float* q, sk_paged_kv kv, const void* k_new, const void
   P.g_k = qk ? qk->g_k : nullptr;
   P.qk_eps = qk ? qk->eps : 0.f;
   P.rope_base = qk ? qk->rope_base : 0.f;
+  P.tab = tab;
+  P.tab_tiles = local_tiles_max(sinks, window, kv.max_blocks);
   const int G = kv.num_q_heads / kv.num_kv_heads;
   // Grid: one workgroup per CU at most, fewer for small launches (an upper bound of the
   // work items from max_blocks), rounded to a multiple of the 8 XCDs.
@@ -1421,6 +1505,17 @@ int enqueue_decode(const float* q, sk_paged_kv kv, const void* k_new, const void
     hipLaunchKernelGGL((decode_kernel<MODE, true, false, false, true>), dim3(unsigned(grid)), dim3(kThreads), lds,
                        stream, P);
   } else if (single) {
+    if constexpr (MODE == kLocal) {
+      if (tab) {  // descriptors from the step's tile table
+        if (sel)
+          hipLaunchKernelGGL((decode_kernel<MODE, true, true, false, false, true>), dim3(unsigned(grid)),
+                             dim3(kThreads), lds, stream, P);
+        else
+          hipLaunchKernelGGL((decode_kernel<MODE, false, true, false, false, true>), dim3(unsigned(grid)),
+                             dim3(kThreads), lds, stream, P);
+        return launch_status(hipGetLastError());
+      }
+    }
     if (sel)
       hipLaunchKernelGGL((decode_kernel<MODE, true, true>), dim3(unsigned(grid)), dim3(kThreads), lds, stream, P);
     else
@@ -1438,14 +1533,15 @@ template <int MODE>
 int launch_decode(const float* q, sk_paged_kv kv, const void* k_new, const void* v_new, int sinks, int window,
                   float scale, const int32_t* sel, int sel_value, const int32_t* lp, const int32_t* lc,
                   const int32_t* ln, float* out, void* ws, size_t ws_bytes, hipStream_t stream,
-                  const int32_t* decl = nullptr, int local_tokens = 0, const QKFinish* qk = nullptr) {
+                  const int32_t* decl = nullptr, int local_tokens = 0, const QKFinish* qk = nullptr,
+                  const int32_t* tab = nullptr) {
   int st = check_decode(q, kv, k_new, v_new, out);
   if (st) return st;
   if (!ws) return SK_E_NULL;
   if (ws_bytes < sk_workspace_bytes(kv.batch, kv.num_q_heads)) return SK_E_WORKSPACE;
   uint8_t* base = reinterpret_cast<uint8_t*>(ws);
   return enqueue_decode<MODE>(q, kv, k_new, v_new, sinks, window, scale, sel, sel_value, lp, lc, ln, out, base,
-                              reinterpret_cast<int32_t*>(base), stream, decl, local_tokens, qk);
+                              reinterpret_cast<int32_t*>(base), stream, decl, local_tokens, qk, tab);
 }
 
 int check_qk(const float* qkv, const uint16_t* g_q, const uint16_t* g_k, float eps, float rope_base) {
@@ -1507,6 +1603,36 @@ int oda_decode_local(const float* q, sk_paged_kv kv, const void* k_new, const vo
   if (sinks < 0 || window < 1) return SK_E_RANGE;
   return launch_decode<kLocal>(q, kv, k_new, v_new, sinks, window, scale, sel, sel_value, nullptr, nullptr,
                                nullptr, out, ws, ws_bytes, stream);
+}
+
+size_t oda_local_tiles_bytes(int32_t batch, int32_t sinks, int32_t window, int32_t max_blocks) {
+  if (batch < 1 || sinks < 0 || window < 1 || max_blocks < 1) return 0;
+  return size_t(batch) * size_t(1 + local_tiles_max(sinks, window, max_blocks)) * 4;
+}
+
+int oda_local_tiles(sk_paged_kv kv, int32_t sinks, int32_t window, int32_t* tab, size_t tab_bytes,
+                    hipStream_t stream) {
+  int st = check_kv(kv);
+  if (st) return st;
+  if (!tab) return SK_E_NULL;
+  if (sinks < 0 || window < 1) return SK_E_RANGE;
+  if (tab_bytes < oda_local_tiles_bytes(kv.batch, sinks, window, kv.max_blocks)) return SK_E_WORKSPACE;
+  const int row = 1 + local_tiles_max(sinks, window, kv.max_blocks);
+  hipLaunchKernelGGL(local_tiles_kernel, dim3(unsigned((row - 1 + 255) / 256), unsigned(kv.batch)), dim3(256), 0,
+                     stream, kv, sinks, window, row, tab);
+  return launch_status(hipGetLastError());
+}
+
+int oda_decode_local_tiles(const float* q, sk_paged_kv kv, const int32_t* tab, size_t tab_bytes, const void* k_new,
+                           const void* v_new, int32_t sinks, int32_t window, float scale, const int32_t* sel,
+                           int32_t sel_value, float* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!tab) return SK_E_NULL;
+  if (sinks < 0 || window < 1) return SK_E_RANGE;
+  if (kv.batch >= 1 && kv.max_blocks >= 1 &&
+      tab_bytes < oda_local_tiles_bytes(kv.batch, sinks, window, kv.max_blocks))
+    return SK_E_WORKSPACE;
+  return launch_decode<kLocal>(q, kv, k_new, v_new, sinks, window, scale, sel, sel_value, nullptr, nullptr,
+                               nullptr, out, ws, ws_bytes, stream, nullptr, 0, nullptr, tab);
 }
 
 int oda_decode_full(const float* q, sk_paged_kv kv, const void* k_new, const void* v_new, float scale,

@@ -144,6 +144,40 @@ def oda_decode_local(q, kv, k_new=None, v_new=None, sinks=4, window=2048, scale=
     return out
 
 
+def local_tiles_bytes(batch, sinks, window, max_blocks):
+    return int(_lib.load().oda_local_tiles_bytes(int(batch), int(sinks), int(window), int(max_blocks)))
+
+
+def local_tiles(kv, sinks=4, window=2048, tab=None):
+    """The Local view's tile table of the current step (oda_local_tiles): one int32 row per
+    request, shared by every layer with the same block tables and lengths."""
+    n = local_tiles_bytes(kv.batch, sinks, window, kv.max_blocks)
+    if n == 0:
+        raise ValueError("invalid sinks / window / shape for a Local tile table")
+    if tab is None:
+        tab = torch.zeros(n // 4, dtype=torch.int32, device=kv.block_tables.device)
+    _check(tab, torch.int32, "tab")
+    if tab.numel() * 4 < n:
+        raise ValueError("tile table too small: %d bytes needed" % n)
+    _lib.call("oda_local_tiles", kv.abi(), int(sinks), int(window), tab.data_ptr(), tab.numel() * 4,
+              _stream(tab.device))
+    return tab
+
+
+def oda_decode_local_tiles(q, kv, tab, k_new=None, v_new=None, sinks=4, window=2048, scale=None, sel=None,
+                           sel_value=MODE_LOCAL, out=None, ws=None):
+    """oda_decode_local with the step's tile table (local_tiles): the same results."""
+    if tab is None:
+        raise ValueError("tab is required (ops.local_tiles)")
+    out, ws = _decode_common(q, kv, k_new, v_new, sel, out, ws)
+    _check(tab, torch.int32, "tab")
+    scale = 1.0 / math.sqrt(HEAD_DIM) if scale is None else float(scale)
+    _lib.call("oda_decode_local_tiles", q.data_ptr(), kv.abi(), tab.data_ptr(), tab.numel() * 4, _ptr(k_new),
+              _ptr(v_new), int(sinks), int(window), scale, _ptr(sel), int(sel_value), out.data_ptr(),
+              ws.data_ptr(), ws.numel(), _stream(q.device))
+    return out
+
+
 def oda_decode_full(q, kv, k_new=None, v_new=None, scale=None, sel=None, sel_value=1, out=None, ws=None):
     out, ws = _decode_common(q, kv, k_new, v_new, sel, out, ws)
     scale = 1.0 / math.sqrt(HEAD_DIM) if scale is None else float(scale)

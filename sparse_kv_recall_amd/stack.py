@@ -40,7 +40,8 @@ class ODAStack:
     """Paged caches of an L-layer attention stack that share block tables and lengths."""
 
     def __init__(self, layers, batch, Hq, Hkv, num_phys_blocks, max_blocks, block_tables, seq_lens,
-                 sinks=4, window=2048, scale=None, device="cuda", separate_outputs=False, local_only=()):
+                 sinks=4, window=2048, scale=None, device="cuda", separate_outputs=False, local_only=(),
+                 local_tiles=True):
         self.layers, self.batch, self.Hq, self.Hkv = layers, batch, Hq, Hkv
         self.local_only = frozenset(int(l) for l in local_only)
         if any(l < 0 or l >= layers for l in self.local_only):
@@ -57,12 +58,26 @@ class ODAStack:
         self.out_full = torch.zeros(shape, dtype=torch.float32, device=device) if separate_outputs else self.out
         self.gate = torch.zeros(batch, dtype=torch.int32, device=device)
         self.qscore = torch.zeros(batch, dtype=torch.float32, device=device)
+        # the Local view's tile table, built once per step for every layer (the layers share
+        # block tables and lengths); None: every Local launch reads the block table itself
+        self.tab = (torch.zeros(ops.local_tiles_bytes(batch, sinks, window, max_blocks) // 4, dtype=torch.int32,
+                                device=device) if local_tiles else None)
+
+    def _local(self, l, q, k, v, out, sel=None, sel_value=ops.MODE_LOCAL):
+        if self.tab is None:
+            ops.oda_decode_local(q, self.caches[l], k, v, self.sinks, self.window, self.scale, sel=sel,
+                                 sel_value=sel_value, out=out, ws=self.ws)
+        else:
+            ops.oda_decode_local_tiles(q, self.caches[l], self.tab, k, v, self.sinks, self.window, self.scale,
+                                       sel=sel, sel_value=sel_value, out=out, ws=self.ws)
 
     def local_pass(self, q, k, v):
-        """q: [L][B][Hq][128] fp32, k, v: [L][B][Hkv][128] bf16 (Local candidates)."""
+        """q: [L][B][Hq][128] fp32, k, v: [L][B][Hkv][128] bf16 (Local candidates). With a
+        tile table, the step's Local tiles are listed once, then every layer attends them."""
+        if self.tab is not None:
+            ops.local_tiles(self.caches[0], self.sinks, self.window, tab=self.tab)
         for l in range(self.layers):
-            ops.oda_decode_local(q[l], self.caches[l], k[l], v[l], self.sinks, self.window, self.scale,
-                                 out=self.out[l], ws=self.ws)
+            self._local(l, q[l], k[l], v[l], self.out[l])
 
     def gate_from_scores(self, scores, theta=0.0):
         ops.oda_gate_scores(scores, theta, out=self.gate)
@@ -74,9 +89,8 @@ class ODAStack:
         """The recall pass: Full view per layer, Local view for local-only layers."""
         sel = self.gate if gated else None
         for l in range(self.layers):
-            if l in self.local_only:
-                ops.oda_decode_local(q[l], self.caches[l], k[l], v[l], self.sinks, self.window, self.scale,
-                                     sel=sel, sel_value=1, out=self.out_full[l], ws=self.ws)
+            if l in self.local_only:  # the table of this step's Local pass, if any, still holds
+                self._local(l, q[l], k[l], v[l], self.out_full[l], sel=sel, sel_value=1)
             else:
                 ops.oda_decode_full(q[l], self.caches[l], k[l], v[l], self.scale, sel=sel, sel_value=1,
                                     out=self.out_full[l], ws=self.ws)

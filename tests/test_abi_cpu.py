@@ -63,6 +63,32 @@ def test_decode_argument_validation():
     assert views(k=kv(num_q_heads=12)) == SK_E_HEADS
 
 
+def test_local_tiles_validation_and_size():
+    # the Local view's tile table: one row of 1 + (sink blocks + window blocks + 1) words per
+    # request, capped at max_blocks tiles; its builder and the decode that reads it check
+    # their arguments before any HIP call
+    L = lib()
+    assert L.oda_local_tiles_bytes(1, 4, 2048, 8194) == (1 + 1 + 128 + 1) * 4
+    assert L.oda_local_tiles_bytes(3, 0, 20, 8194) == 3 * (1 + 0 + 2 + 1) * 4
+    assert L.oda_local_tiles_bytes(1, 4, 2048, 10) == (1 + 10) * 4
+    assert L.oda_local_tiles_bytes(0, 4, 2048, 100) == 0 and L.oda_local_tiles_bytes(1, -1, 2048, 100) == 0
+    assert L.oda_local_tiles_bytes(1, 4, 0, 100) == 0
+    need = L.oda_local_tiles_bytes(1, 4, 2048, 100)
+    assert L.oda_local_tiles(kv(), 4, 2048, None, need, None) == SK_E_NULL
+    assert L.oda_local_tiles(kv(k_pool=None), 4, 2048, FAKE, need, None) == SK_E_NULL
+    assert L.oda_local_tiles(kv(), -1, 2048, FAKE, need, None) == SK_E_RANGE
+    assert L.oda_local_tiles(kv(), 4, 0, FAKE, need, None) == SK_E_RANGE
+    assert L.oda_local_tiles(kv(), 4, 2048, FAKE, need - 4, None) == SK_E_WORKSPACE
+    dec = lambda tab=FAKE, tab_bytes=need, sinks=4, window=2048, k=kv(), q=FAKE: L.oda_decode_local_tiles(
+        q, k, tab, tab_bytes, None, None, sinks, window, 0.1, None, 0, FAKE, FAKE, 1 << 30, None)
+    assert dec(tab=None) == SK_E_NULL
+    assert dec(q=None) == SK_E_NULL
+    assert dec(sinks=-1) == SK_E_RANGE
+    assert dec(window=0) == SK_E_RANGE
+    assert dec(tab_bytes=need - 4) == SK_E_WORKSPACE
+    assert dec(k=kv(head_dim=64)) == SK_E_SHAPE
+
+
 def test_decode_full_noalloc_validation():
     # the allocation-free Full view checks its arguments, and the size its device array
     # holds (16 MiB: batch * num_q_heads up to about 15700), before any HIP call
