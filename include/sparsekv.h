@@ -174,22 +174,23 @@ int oda_decode_local(const float* q, sk_paged_kv kv, const void* k_new, const vo
  * attends the same sinks and window of its own cache, so the physical blocks of
  * that view are the same in every layer that shares the block tables and
  * lengths). oda_local_tiles writes, per request b, a row of
- * oda_local_tiles_bytes(...) / (4 * batch) int32 words: word 0 the length
- * seq_lens[b] it was built for, word 1 + i the physical block of tile i of
- * request b's Local view (the sinks' blocks, then the window's, in ascending
- * order); words past the view's tiles are left as they were. A request with
- * an invalid length gets word 0 only.
+ * oda_local_tiles_bytes(...) / (4 * batch) int32 words: words 0-2 the length
+ * seq_lens[b], the sinks and the window it was built for, word 3 + i the
+ * physical block of tile i of request b's Local view (the sinks' blocks, then
+ * the window's, in ascending order); words past the view's tiles are left as
+ * they were. A request with an invalid length gets words 0-2 only.
  *  tab : int32 device memory of at least
  *        oda_local_tiles_bytes(batch, sinks, window, max_blocks) bytes
  *        (0 for an invalid argument)
  * oda_decode_local_tiles is oda_decode_local (same arguments, outputs, commits
  * and error bits, bit for bit) with such a table built on the same lengths
  * and block tables: a single-request launch requests its first tiles' blocks
- * from the table together with the length instead of after it. When word 0
- * differs from the request's current length, or the launch's split plan is not
- * the one of the largest Local tile count, it reads the block table as
- * oda_decode_local does (a table from another step gives the same results,
- * only without the saving). Build the table again after a block table changes.
+ * from the table together with the length instead of after it. When words 0-2
+ * differ from the request's current length and the call's sinks and window, or
+ * the launch's split plan is not the one of the largest Local tile count, it
+ * reads the block table as oda_decode_local does (a table from another step
+ * gives the same results, only without the saving). Build the table again after
+ * a block table changes.
  * Host-checked: tab non-NULL, sinks >= 0, window >= 1, tab_bytes large enough. */
 size_t oda_local_tiles_bytes(int32_t batch, int32_t sinks, int32_t window, int32_t max_blocks);
 int oda_local_tiles(sk_paged_kv kv, int32_t sinks, int32_t window, int32_t* tab, size_t tab_bytes,

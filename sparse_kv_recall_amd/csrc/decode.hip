@@ -49,6 +49,7 @@ constexpr int kGridCap = 256;                       // decode workgroups per lau
 constexpr int kBufferFlags = 0x00020000;  // raw buffer access, 32-bit data format (gfx9 word 3)
 constexpr int kNonTemporal = 2;           // buffer load cache policy: non-temporal
 constexpr int kTicketStride = 16;                   // words between ticket counters (small launches)
+constexpr int kTabHeader = 3;                       // tile table row: length, sinks, window, then the tiles
 constexpr int kMergeBatch = 48;                     // split accumulators loaded together in the merge
 // Per-request views in one launch: work items fill at most this many rounds of the grid
 // (4 x 256 workgroups = the items a workspace holds at the largest query group). Measured
@@ -91,9 +92,10 @@ struct DecodeParams {
   const uint16_t* g_k;
   float qk_eps;
   float rope_base;
-  // Local view from a step's tile table (oda_local_tiles): per request, the length the
-  // table was built for, then the physical block of each Local tile; tab_tiles = the
-  // largest Local tile count (its rows hold 1 + tab_tiles words). Null: no table.
+  // Local view from a step's tile table (oda_local_tiles): per request, the length, sinks
+  // and window the table was built for, then the physical block of each Local tile;
+  // tab_tiles = the largest Local tile count (its rows hold kTabHeader + tab_tiles words).
+  // Null: no table.
   const int32_t* tab;
   int tab_tiles;
 };
@@ -653,20 +655,21 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
   // requested with the length, so that the first tiles can be requested once it arrives.
   // The item body takes them when the length and the plan match, else it reads the block
   // table as without a table.
-  int tab_phys = 0, tab_n = -1, tab_T = 0, tab_splits = 0;
-  if constexpr (TAB) {
-    single_plan(P.tab_tiles, int(gridDim.x) / Hkv, tab_T, tab_splits);
-    const int item = int(blockIdx.x);
-    if (item < tab_splits * Hkv) {
-      const int ti = (item % tab_splits) * tab_T + wave + lane * W;
-      tab_phys = P.tab[1 + min(ti, P.tab_tiles - 1)];
-    }
-    tab_n = __builtin_amdgcn_readfirstlane(P.tab[0]);
-  }
+  // Every load here is unconditional (an index past the wave's tiles is clamped into the row
+  // and its value not used), so that all of them are requested before the first wait.
+  int tab_phys = 0, tab_n = -1, tab_T = 0, tab_splits = 0, tab_s = -1, tab_w = -1;
   if (SINGLE) {  // uniform values, one round of loads
     const int n0 = P.kv.seq_lens[0];
     const int listed0 = (MODE == kList) ? P.list_num[0] : 0;
     const int sel0 = HAS_SEL ? P.sel[0] : 0;
+    if constexpr (TAB) {
+      tab_n = P.tab[0];
+      tab_s = P.tab[1];
+      tab_w = P.tab[2];
+      single_plan(P.tab_tiles, int(gridDim.x) / Hkv, tab_T, tab_splits);
+      const int ti = (int(blockIdx.x) % tab_splits) * tab_T + wave + lane * W;
+      tab_phys = P.tab[kTabHeader + min(ti, P.tab_tiles - 1)];
+    }
     l_len = __builtin_amdgcn_readfirstlane(n0);
     l_listed = __builtin_amdgcn_readfirstlane(listed0);
     if (HAS_SEL && __builtin_amdgcn_readfirstlane(sel0) != P.sel_value) return;
@@ -969,7 +972,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
       }
     }
     bool from_tab = false;
-    if constexpr (TAB) from_tab = tab_n == n && T == tab_T && splits == tab_splits;
+    if constexpr (TAB)  // the table was built for this length, sinks and window, and this plan
+      from_tab = (tab_n == n) & (tab_s == P.sinks) & (tab_w == P.window) & (T == tab_T) & (splits == tab_splits);
     if (from_tab) {  // the table's blocks, checked as tile_at checks the block table's
       int lo = 0, hi = 0, phys = 0;
       if (lane < my_tiles) {
@@ -1378,29 +1382,35 @@ __global__ __launch_bounds__(256) void gather_kernel(sk_paged_kv kv, const uint3
 }
 
 // The largest Local tile count: the sinks' blocks, the window's (one more when it is not
-// block aligned), at most the block table's columns. A tile table row holds 1 + this words.
+// block aligned), at most the block table's columns. A tile table row holds kTabHeader +
+// this words.
 int local_tiles_max(int sinks, int window, int max_blocks) {
   const int64_t t = int64_t((sinks + kBlock - 1) / kBlock) + (int64_t(window) + kBlock - 1) / kBlock + 1;
   return int(t < max_blocks ? t : max_blocks);
 }
 
 // One thread per (request, Local tile): the physical block of tile i of request b's Local
-// view at its current length (word 1 + i of its row; word 0: that length). Requests with an
-// invalid length get the length only (the decode launch reports them).
+// view at its current length (word kTabHeader + i of its row; words 0-2: that length, the
+// sinks and the window). Requests with an invalid length get the header only (the decode
+// launch reports them).
 __global__ __launch_bounds__(256) void local_tiles_kernel(sk_paged_kv kv, int sinks, int window, int row,
                                                           int32_t* __restrict__ tab) {
   const int b = blockIdx.y;
   const int i = blockIdx.x * 256 + threadIdx.x;
   const int n = kv.seq_lens[b];
   int32_t* t = tab + int64_t(b) * row;
-  if (i == 0) t[0] = n;
+  if (i == 0) {
+    t[0] = n;
+    t[1] = sinks;
+    t[2] = window;
+  }
   if (n < 1 || n > kv.max_blocks * kBlock) return;
   DecodeParams P{};
   P.sinks = sinks;
   P.window = window;
   if (i >= request_tiles<kLocal>(P, b, n, 0)) return;
   int lo, hi;
-  t[1 + i] = kv.block_tables[int64_t(b) * kv.max_blocks + local_tile(P, n, i, lo, hi)];
+  t[kTabHeader + i] = kv.block_tables[int64_t(b) * kv.max_blocks + local_tile(P, n, i, lo, hi)];
 }
 
 // Argument checks of every decode launch; the workspace is checked by the caller.
@@ -1607,7 +1617,7 @@ int oda_decode_local(const float* q, sk_paged_kv kv, const void* k_new, const vo
 
 size_t oda_local_tiles_bytes(int32_t batch, int32_t sinks, int32_t window, int32_t max_blocks) {
   if (batch < 1 || sinks < 0 || window < 1 || max_blocks < 1) return 0;
-  return size_t(batch) * size_t(1 + local_tiles_max(sinks, window, max_blocks)) * 4;
+  return size_t(batch) * size_t(kTabHeader + local_tiles_max(sinks, window, max_blocks)) * 4;
 }
 
 int oda_local_tiles(sk_paged_kv kv, int32_t sinks, int32_t window, int32_t* tab, size_t tab_bytes,
@@ -1617,8 +1627,8 @@ int oda_local_tiles(sk_paged_kv kv, int32_t sinks, int32_t window, int32_t* tab,
   if (!tab) return SK_E_NULL;
   if (sinks < 0 || window < 1) return SK_E_RANGE;
   if (tab_bytes < oda_local_tiles_bytes(kv.batch, sinks, window, kv.max_blocks)) return SK_E_WORKSPACE;
-  const int row = 1 + local_tiles_max(sinks, window, kv.max_blocks);
-  hipLaunchKernelGGL(local_tiles_kernel, dim3(unsigned((row - 1 + 255) / 256), unsigned(kv.batch)), dim3(256), 0,
+  const int row = kTabHeader + local_tiles_max(sinks, window, kv.max_blocks);
+  hipLaunchKernelGGL(local_tiles_kernel, dim3(unsigned((row - kTabHeader + 255) / 256), unsigned(kv.batch)), dim3(256), 0,
                      stream, kv, sinks, window, row, tab);
   return launch_status(hipGetLastError());
 }

@@ -64,13 +64,13 @@ def test_decode_argument_validation():
 
 
 def test_local_tiles_validation_and_size():
-    # the Local view's tile table: one row of 1 + (sink blocks + window blocks + 1) words per
+    # the Local view's tile table: one row of 3 + (sink blocks + window blocks + 1) words per
     # request, capped at max_blocks tiles; its builder and the decode that reads it check
     # their arguments before any HIP call
     L = lib()
-    assert L.oda_local_tiles_bytes(1, 4, 2048, 8194) == (1 + 1 + 128 + 1) * 4
-    assert L.oda_local_tiles_bytes(3, 0, 20, 8194) == 3 * (1 + 0 + 2 + 1) * 4
-    assert L.oda_local_tiles_bytes(1, 4, 2048, 10) == (1 + 10) * 4
+    assert L.oda_local_tiles_bytes(1, 4, 2048, 8194) == (3 + 1 + 128 + 1) * 4
+    assert L.oda_local_tiles_bytes(3, 0, 20, 8194) == 3 * (3 + 0 + 2 + 1) * 4
+    assert L.oda_local_tiles_bytes(1, 4, 2048, 10) == (3 + 10) * 4
     assert L.oda_local_tiles_bytes(0, 4, 2048, 100) == 0 and L.oda_local_tiles_bytes(1, -1, 2048, 100) == 0
     assert L.oda_local_tiles_bytes(1, 4, 0, 100) == 0
     need = L.oda_local_tiles_bytes(1, 4, 2048, 100)

@@ -43,9 +43,9 @@ def test_table_lists_the_local_blocks(sinks, window):
     t = tab.cpu().numpy().reshape(len(ns), row)
     for b, n in enumerate(ns):
         exp = _expected_tiles(hc.bt[b], n, sinks, window)
-        assert t[b, 0] == n
-        assert len(exp) <= row - 1
-        assert np.array_equal(t[b, 1:1 + len(exp)], exp), (b, n)
+        assert list(t[b, :3]) == [n, sinks, window]
+        assert len(exp) <= row - 3
+        assert np.array_equal(t[b, 3:3 + len(exp)], exp), (b, n)
 
 
 def _run_pair(hc, b, q, kn, vn, sinks, window, tab=None, sel=None, sel_value=0):
@@ -98,8 +98,8 @@ def test_decode_with_table_equals_without(sinks, window):
 
 def test_table_of_another_step_falls_back():
     # a table built at n, used at n + 1 (the window moved by one position, and at n = 2064
-    # into a new block), and a table never built: the launch reads the block table and
-    # gives the same bits as without a table
+    # into a new block), a table built for another window, and a table never built: the
+    # launch reads the block table and gives the same bits as without a table
     from sparse_kv_recall_amd import ops
     Hq, Hkv = 32, 8
     ns = [2064, 3000, 40]
@@ -111,9 +111,10 @@ def test_table_of_another_step_falls_back():
         stale = ops.local_tiles(one, 4, 2048)
         one.seq_lens.fill_(n + 1)
         hc.ns[b] = n + 1
-        for tab in (stale, torch.zeros_like(stale)):
+        other_window = ops.local_tiles(one, 4, 2032, tab=torch.zeros_like(stale))
+        for tab in (stale, other_window, torch.zeros_like(stale)):
             o0, o1 = _run_pair(hc, b, q, None, None, 4, 2048, tab=tab)
-            assert np.array_equal(o0.view(np.uint32), o1.view(np.uint32)), (n, int(tab[0].item()))
+            assert np.array_equal(o0.view(np.uint32), o1.view(np.uint32)), (n, tab[:3].tolist())
 
 
 def test_table_with_selector_and_batches():
@@ -143,7 +144,7 @@ def test_table_entry_outside_the_pool_sets_the_block_error():
     hc = HostCache(Hq, Hkv, [3000], seed=970)
     one = _single(hc, 0)
     tab = ops.local_tiles(one, 4, 2048)
-    tab[5] = hc.kv.num_phys_blocks + 9
+    tab[7] = hc.kv.num_phys_blocks + 9
     ws = ops.workspace(1, Hq)
     q = torch.as_tensor(rand_f32(rng.mix_key(971), (1, Hq, 128)), device="cuda")
     ops.oda_decode_local_tiles(q, one, tab, ws=ws)
