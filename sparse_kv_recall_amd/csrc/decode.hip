@@ -649,14 +649,14 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
   // round of loads (lanes past the batch read request 0 and ignore it).
   int l_len = 0, l_listed = 0, l_view = MODE;
   bool l_sel = true;
-  // Local view from a tile table (TAB, single request): the table's length and this
-  // wave's tile descriptors under the plan of the largest Local tile count (the plan of
-  // every length from sinks + window on, unless the window's alignment changes it),
-  // requested with the length, so that the first tiles can be requested once it arrives.
-  // The item body takes them when the length and the plan match, else it reads the block
-  // table as without a table.
-  // Every load here is unconditional (an index past the wave's tiles is clamped into the row
-  // and its value not used), so that all of them are requested before the first wait.
+  // Local view from a tile table (TAB, single request): the row's header (the length, sinks
+  // and window it was built for) and this wave's tile descriptors under the plan of the
+  // largest Local tile count (the plan of every length from sinks + window on, unless the
+  // window's alignment changes it), requested with the length, so that the first tiles can
+  // be requested once it arrives. The item body takes them when the header and the plan
+  // match, else it reads the block table as without a table. Every load here is
+  // unconditional (an index past the wave's tiles is clamped into the row and its value not
+  // used), so that all of them are requested before the first wait.
   int tab_phys = 0, tab_n = -1, tab_T = 0, tab_splits = 0, tab_s = -1, tab_w = -1;
   if (SINGLE) {  // uniform values, one round of loads
     const int n0 = P.kv.seq_lens[0];
@@ -1628,8 +1628,8 @@ int oda_local_tiles(sk_paged_kv kv, int32_t sinks, int32_t window, int32_t* tab,
   if (sinks < 0 || window < 1) return SK_E_RANGE;
   if (tab_bytes < oda_local_tiles_bytes(kv.batch, sinks, window, kv.max_blocks)) return SK_E_WORKSPACE;
   const int row = kTabHeader + local_tiles_max(sinks, window, kv.max_blocks);
-  hipLaunchKernelGGL(local_tiles_kernel, dim3(unsigned((row - kTabHeader + 255) / 256), unsigned(kv.batch)), dim3(256), 0,
-                     stream, kv, sinks, window, row, tab);
+  hipLaunchKernelGGL(local_tiles_kernel, dim3(unsigned((row - kTabHeader + 255) / 256), unsigned(kv.batch)),
+                     dim3(256), 0, stream, kv, sinks, window, row, tab);
   return launch_status(hipGetLastError());
 }
 
