@@ -399,6 +399,43 @@ def test_commit_holds_selected_candidate():
         assert out is (o_f if g else o_l)
 
 
+def test_oda_steps_golden():
+    # the four decode steps worked by hand in golden/oda_steps.txt (ODA summary page,
+    # "Approach": Local every step, recall recomputes the step with Full, the selected pass's
+    # KV is kept; "Developer perspective": a Local-only layer's recall pass): with q = 0 every
+    # output is the mean of the values over the key set, so each pass's key set and the
+    # candidate kept at n-1 (and read by the next step) show in the numbers
+    D, s, w = 128, 1, 2
+    rows = read_golden("oda_steps.txt")
+    history = [float(x) for x in rows[-1][1:]]
+    assert rows[-1][0] == "HISTORY"
+    val = lambda x: to_bf16_bits(np.full((1, D), float(x), np.float32))  # [Hkv = 1][D]
+    hk = np.zeros((len(history), 1, D), np.uint16)
+    for j, x in enumerate([1, 2, 4, 8]):
+        hk[j] = val(x)
+    hv = hk.copy()
+    hk_lo, hv_lo = hk.copy(), hv.copy()  # a Local-only layer fed the same candidates
+    q = np.zeros((1, D))
+    mean = lambda o: float(o.mean())
+    for r in rows[:-1]:
+        t, n, gate, vl, vf = int(r[0]), int(r[1]), int(r[2]), float(r[3]), float(r[4])
+        o_l = oda.local_pass(q, val(vl), val(vl), hk, hv, n, SCALE, sinks=s, window=w)
+        oda.local_pass(q, val(vl), val(vl), hk_lo, hv_lo, n, SCALE, sinks=s, window=w)
+        assert np.allclose(o_l, float(r[5]), rtol=0, atol=1e-12), t
+        o_f = None
+        if gate:
+            o_f = oda.recall_pass(q, val(vf), val(vf), hk, hv, n, SCALE, False, sinks=s, window=w)
+            o_lo = oda.recall_pass(q, val(vf), val(vf), hk_lo, hv_lo, n, SCALE, True, sinks=s, window=w)
+            assert np.allclose(o_f, float(r[6]), rtol=0, atol=1e-12), t
+            assert np.allclose(o_lo, float(r[7]), rtol=0, atol=1e-12), t
+        else:
+            assert r[6] == r[7] == "-"
+        assert abs(mean(oda.select(gate, o_l, o_f)) - float(r[8])) < 1e-12, t
+        assert np.array_equal(hv[n - 1], val(r[9])) and np.array_equal(hk[n - 1], val(r[9])), t
+    assert all(np.array_equal(hv[j], val(x)) for j, x in enumerate(history))
+    assert np.array_equal(hv_lo, hv)  # the Local-only layer keeps the same candidates
+
+
 def test_recall_pass_access_control():
     # Per-layer access control: a local-only layer's recall pass reads the
     # sinks and the window only -- perturbing any other position leaves its output
