@@ -1009,7 +1009,8 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the decode path here is built and measured on a single "
-              "MI355X (see DESIGN.md for how it would shard); run with --gpus 1", file=sys.stderr)
+              "MI355X (requests would shard across GPUs with no exchange, one long sequence by KV head); "
+              "run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
