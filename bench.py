@@ -297,6 +297,27 @@ def stream_floor(device, sizes, launches=36, reps=3):
     return out
 
 
+def local_view_rate(stack, feeder, reps):
+    """Per-launch time of the Local view over all layers at the current n: the step's Local
+    pass (the tile-table launch and one Local launch per layer, each committing its
+    candidate at n - 1) captured in one graph and timed with HIP events around the replays;
+    the table launch's share is spread over the layers."""
+    import torch
+    from sparse_kv_recall_amd.stack import capture_graph
+    q, k, v = feeder.q, feeder.k, feeder.v
+    g = capture_graph(lambda: stack.local_pass(q[:, 0, :], k[:, 0, :], v[:, 0, :]))
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    e1.synchronize()
+    del g
+    return e0.elapsed_time(e1) / (reps * stack.layers)
+
+
 def gated_off_launch(stack, feeder, reps=20):
     """Per-launch time of the recall pass's Full launches when the gate is 0, so that every
     workgroup leaves at once: the per-node cost that the step graph pays 36 times on
@@ -1073,6 +1094,11 @@ def main():
     bytes_full = n_now * wl.Hkv * 128 * 2 * 2 + 2 * wl.Hq * 128 * 4 + 2 * wl.Hkv * 128 * 2
     achieved = bytes_full / (full_ms * 1e-3) / 1e9
     log("Full-view kernel at n=%d: %.1f us per launch, %.0f GB/s" % (n_now, full_ms * 1e3, achieved))
+    local_ms = local_view_rate(stack, feeder, 10)
+    local_pos = min(n_now, wl.sinks + wl.window)
+    bytes_local = local_pos * wl.Hkv * 128 * 2 * 2 + 2 * wl.Hq * 128 * 4 + 2 * wl.Hkv * 128 * 2
+    log("Local-view kernel (%d positions, tile table): %.2f us per launch, %.0f GB/s"
+        % (local_pos, local_ms * 1e3, bytes_local / (local_ms * 1e-3) / 1e9))
     gated_off_ms = gated_off_launch(stack, feeder)
     log("gated-off Full launch: %.2f us" % (gated_off_ms * 1e3))
     blocks = roofline_blocks(stack, feeder, args.roofline_reps)
@@ -1141,6 +1167,13 @@ def main():
                      "us_per_launch": round(full_ms * 1e3, 2), "algorithmic_bytes_per_launch": int(bytes_full),
                      "traffic_source": "profiles/decode_128k_hbm_counters.md (rocprofv3 FETCH_SIZE x2.0 + "
                                        "WRITE_SIZE x1.0, rescaled to this n); null if the kernel changed"},
+        "local_view": {"us_per_launch": round(local_ms * 1e3, 2), "positions": local_pos,
+                       "algorithmic_bytes_per_launch": int(bytes_local),
+                       "achieved_GBs": round(bytes_local / (local_ms * 1e-3) / 1e9, 1),
+                       "frac": round(bytes_local / (local_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                       "stream_floor_us": floor["local_2052_positions"]["us_per_launch"],
+                       "kernel": "decode_kernel<local, tile table> (oda_decode_local_tiles) in the step's Local "
+                                 "pass graph (one table launch and 36 Local launches), n=%d" % n_now},
         "roofline_block_sparse": dict(blocks, kernel="decode_kernel<list> over a permuted block table (36-layer "
                                       "rotation, n=%d); also per layer with the rewrite (gather) in every call and "
                                       "once per step" % n_now),
