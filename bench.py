@@ -1067,6 +1067,8 @@ def main():
         print("--steps must be in %d..%d: the timed window starts at step 0 and needs a whole run of %d steps "
               "(one recall step and seven others)" % (RECALL_PERIOD, wl.steps, RECALL_PERIOD), file=sys.stderr)
         sys.exit(2)
+    if args.ramp_ms > 0:  # the reference below is short too: measured at working clocks
+        clock_ramp(device, args.ramp_ms)
     stream_gbs = stream_peak(device)  # before the stack is staged: a fresh allocation
     log("streaming-read reference: %.0f GB/s" % stream_gbs)
     log("staging %d layers x %d positions of bf16 KV" % (wl.layers, int(wl.H0[0])))
