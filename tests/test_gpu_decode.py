@@ -623,3 +623,61 @@ def test_single_request_invalid_length_and_empty_list():
     assert not out.cpu().numpy().any()
     kr, vr = ops.kv_read(hc.kv, 0, 299, 1)
     assert np.array_equal(bf16_tensor_to_bits(kr)[0], kn[0]) and np.array_equal(bf16_tensor_to_bits(vr)[0], vn[0])
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(12, 3), (10, 5), (16, 16), (48, 3)])
+def test_odd_and_wide_kv_head_counts(Hq, Hkv):
+    # The split plan gives each KV head grid / Hkv slots; with 3, 5 or 16 KV heads the grid
+    # (a multiple of 8 workgroups) does not divide evenly. Batch instance (four ragged
+    # requests): Full, Local and a block list; single-request instance: Full with the
+    # current token committed, Local with and without the step's tile table, a block list.
+    from sparse_kv_recall_amd import ops
+    g = np.random.default_rng(Hq * 100 + Hkv)
+    ns = [37, 4500, 2100, 9000]
+    hc = HostCache(Hq, Hkv, ns, seed=Hq * 10 + Hkv)
+    q = _q(Hq, len(ns), seed=Hq + 7 * Hkv)
+    qt = torch.as_tensor(q, device="cuda")
+    kept = []
+    for n in ns:
+        nb = (n + 15) // 16
+        kept.append(sorted(set(g.choice(nb, size=max(1, nb // 8), replace=False).tolist()) | {nb - 1}))
+    mask = torch.as_tensor(_mask_words(kept, hc.max_blocks).view(np.int32), device="cuda")
+    ws = ops.workspace(len(ns), Hq)
+    outs = {"full": ops.oda_decode_full(qt, hc.kv, ws=ws).cpu().numpy(),
+            "local": ops.oda_decode_local(qt, hc.kv, ws=ws).cpu().numpy(),
+            "list": ops.da_decode_blocks(qt, hc.kv, mask, ws=ws)[0].cpu().numpy()}
+    assert ops.workspace_error(ws) == 0
+    for b, n in enumerate(ns):
+        for view, keys in (("full", keysets.full_keys(n)), ("local", keysets.local_keys(n)),
+                           ("list", keysets.block_keys(n, kept[b]))):
+            ref = attention.attend(q[b], hc.k[b], hc.v[b], keys, SCALE)
+            check_tight(outs[view][b], ref, q[b], hc.k[b], hc.v[b], keys, SCALE,
+                        what="batch %s Hq=%d Hkv=%d n=%d" % (view, Hq, Hkv, n))
+
+    n = 9000
+    one = HostCache(Hq, Hkv, [n], seed=Hq * 10 + Hkv + 1)
+    q1 = _q(Hq, 1, seed=Hq + 7 * Hkv + 1)
+    q1t = torch.as_tensor(q1, device="cuda")
+    kn = rand_bits(rng.mix_key(902, Hq, Hkv, 1), 1, Hkv)
+    vn = rand_bits(rng.mix_key(902, Hq, Hkv, 2), 1, Hkv)
+    ws1 = ops.workspace(1, Hq)
+    loc = ops.oda_decode_local(q1t, one.kv, ws=ws1).cpu().numpy()
+    tab = ops.local_tiles(one.kv)
+    loc_tab = ops.oda_decode_local_tiles(q1t, one.kv, tab, ws=ws1).cpu().numpy()
+    assert np.array_equal(loc.view(np.uint32), loc_tab.view(np.uint32)), "tile table changed the Local view"
+    nb = (n + 15) // 16
+    kept1 = sorted(set(g.choice(nb, size=nb // 8, replace=False).tolist()) | {nb - 1})
+    mask1 = torch.as_tensor(_mask_words([kept1], one.max_blocks).view(np.int32), device="cuda")
+    lst = ops.da_decode_blocks(q1t, one.kv, mask1, ws=ws1)[0].cpu().numpy()
+    full = ops.oda_decode_full(q1t, one.kv, bits_to_bf16_tensor(kn), bits_to_bf16_tensor(vn), ws=ws1).cpu().numpy()
+    k_got, v_got = ops.kv_read(one.kv, 0, n - 1, 1)
+    assert np.array_equal(bf16_tensor_to_bits(k_got)[0], kn[0]) and np.array_equal(bf16_tensor_to_bits(v_got)[0],
+                                                                                   vn[0])
+    kb, vb = one.k[0].copy(), one.v[0].copy()
+    kb[n - 1], vb[n - 1] = kn[0], vn[0]
+    for view, got, keys, kk, vv in (("local", loc, keysets.local_keys(n), one.k[0], one.v[0]),
+                                    ("list", lst, keysets.block_keys(n, kept1), one.k[0], one.v[0]),
+                                    ("full+commit", full, keysets.full_keys(n), kb, vb)):
+        ref = attention.attend(q1[0], kk, vv, keys, SCALE)
+        check_tight(got[0], ref, q1[0], kk, vv, keys, SCALE, what="single %s Hq=%d Hkv=%d" % (view, Hq, Hkv))
+    assert ops.workspace_error(ws1) == 0
