@@ -27,9 +27,12 @@ def _mask_words(kept_per_req, max_blocks):
 
 
 @pytest.mark.parametrize("B,sinks,window,Hq,Hkv", [(12, 4, 2048, 16, 4), (64, 4, 2048, 16, 4), (65, 4, 300, 16, 4),
-                                                   (100, 3, 40, 16, 4), (12, 4, 2048, 32, 2), (70, 4, 500, 32, 2)])
+                                                   (100, 3, 40, 16, 4), (12, 4, 2048, 32, 2), (70, 4, 500, 32, 2),
+                                                   (40, 4, 2048, 15, 3), (90, 4, 500, 10, 5), (20, 4, 2048, 16, 16)])
 def test_views_one_launch(B, sinks, window, Hq, Hkv):
-    # query groups of 4 and of 16 (the merge then works on four output elements per thread)
+    # query groups of 4 and of 16 (the merge then works on four output elements per thread);
+    # 3, 5 and 16 KV heads, whose split slots per KV head leave a remainder of the grid, the
+    # 90-request batch through the workgroup plan and its ranking for the balanced order
     g = np.random.default_rng(90 + B + Hkv)
     ns = [int(x) for x in g.integers(1, 6000, size=B)]
     ns[:5] = [1, 16, 17, 2052, 5999]
