@@ -53,8 +53,18 @@ def _mask_of(blocks_per_req, max_blocks):
 @pytest.mark.parametrize("local_tokens", [0, 20, 1024])
 @pytest.mark.parametrize("commit", [False, True])
 def test_declared_matches_oracle_and_list_path(local_tokens, commit):
+    _declared_case(local_tokens, commit, 32, 8)
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(15, 3), (16, 16)])
+def test_declared_odd_and_wide_kv_head_counts(Hq, Hkv):
+    # split slots per KV head that leave a remainder of the grid (3 KV heads), one q head per
+    # KV head (16)
+    _declared_case(1024, True, Hq, Hkv)
+
+
+def _declared_case(local_tokens, commit, Hq, Hkv):
     from sparse_kv_recall_amd import ops
-    Hq, Hkv = 32, 8
     ns = [n for n, _ in CASES]
     decl = np.array([d for _, d in CASES], np.int32)
     B = len(ns)
