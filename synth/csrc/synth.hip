@@ -60,7 +60,8 @@ struct FeedParams {
 
 // Element indices stay below 2^31 for every workload here (the host checks), so the
 // decomposition uses 32-bit arithmetic.
-__global__ __launch_bounds__(256) void feed_kernel(FeedParams F) {
+constexpr int kFeedThreads = 1024;  // 16 waves per block: the hash chains are latency-bound
+__global__ __launch_bounds__(kFeedThreads) void feed_kernel(FeedParams F) {
   __shared__ int s_last;
   const int t = F.state[0] % F.num_steps;
   const int rq = F.Hq * 128, rkv = F.Hkv * 128;
@@ -152,9 +153,10 @@ int synth_feed(int32_t* state, int32_t* seq_lens, const int32_t* H0, int B, int 
   if (total >= (int64_t(1) << 31) || B < 1 || num_steps < 1) return -4;
   FeedParams F{state, seq_lens, H0, B, L, P, Hq, Hkv, num_steps, key_q, key_k, key_v, key_x, key_score, scale,
                q_out, k_out, v_out, x_dim, x_out, sched, score_out, decl_table, decl_out, token_table, token_out};
-  int64_t blocks = (total + 255) / 256;
+  // at most 256 blocks (one per CU), so the last-block ticket that advances the step stays cheap
+  int64_t blocks = (total + kFeedThreads - 1) / kFeedThreads;
   if (blocks > 256) blocks = 256;
-  hipLaunchKernelGGL(feed_kernel, dim3(unsigned(blocks)), dim3(256), 0, s, F);
+  hipLaunchKernelGGL(feed_kernel, dim3(unsigned(blocks)), dim3(kFeedThreads), 0, s, F);
   return status(hipGetLastError());
 }
 
