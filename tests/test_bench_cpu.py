@@ -19,5 +19,6 @@ def test_bench_help_lists_the_options():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--help"], capture_output=True, text=True,
                        timeout=120)
     assert r.returncode == 0
-    for opt in ("--gpus", "--steps", "--warmup", "--no-cpu-baseline", "--no-model", "--no-other", "--sweep"):
+    for opt in ("--gpus", "--steps", "--warmup", "--no-cpu-baseline", "--no-model", "--no-other", "--sweep",
+                "--ramp-ms"):
         assert opt in r.stdout, opt
