@@ -70,9 +70,10 @@ def test_qkv_rope_two_positions():
             assert np.all(np.abs(gt - ref) <= np.abs(ref) * 2.0 ** -7 + 1e-6), call
 
 
-@pytest.mark.parametrize("view,G,n", [("local", 2, 131072), ("full", 4, 2999), ("local", 8, 6), ("full", 1, 40),
-                                      ("full", 2, 1), ("local", 4, 17)])
-def test_decode_from_projection(view, G, n):
+@pytest.mark.parametrize("view,G,n,Hkv", [("local", 2, 131072, 2), ("full", 4, 2999, 2), ("local", 8, 6, 2),
+                                          ("full", 1, 40, 2), ("full", 2, 1, 2), ("local", 4, 17, 2),
+                                          ("full", 4, 3001, 3), ("local", 1, 2100, 16)])
+def test_decode_from_projection(view, G, n, Hkv):
     """The Local / Full views from a raw q/k/v projection (per-head q/k RMSNorm and the
     rotation at n - 1 applied inside the decode launch) against the fp64 layer pieces of
     the decoder oracle: the committed v bit for bit, the committed k within one bf16 unit
@@ -86,12 +87,12 @@ def test_decode_from_projection(view, G, n):
     from sparse_kv_recall_amd import ops
     from synth import rng
     from tests.helpers import SCALE, bf16_tensor_to_bits, bits_to_bf16_tensor, check_tight, rand_bits
-    Hkv, eps, base = 2, 1e-6, 1.0e6
+    eps, base = 1e-6, 1.0e6
     Hq = G * Hkv
     g = np.random.default_rng(100 * G + n % 997)
     mb = -(-n // 16)
-    hk = rand_bits(rng.mix_key(911, G, 1), n, Hkv)
-    hv = rand_bits(rng.mix_key(911, G, 2), n, Hkv)
+    hk = rand_bits(rng.mix_key(911, G, Hkv, 1), n, Hkv)
+    hv = rand_bits(rng.mix_key(911, G, Hkv, 2), n, Hkv)
     seq = torch.tensor([n], dtype=torch.int32, device="cuda")
     bt = torch.arange(mb, dtype=torch.int32, device="cuda")[None]
     cache = ops.PagedKVCache(mb, 1, Hq, Hkv, mb, block_tables=bt, seq_lens=seq)
@@ -116,7 +117,7 @@ def test_decode_from_projection(view, G, n):
     hk[n - 1], hv[n - 1] = kb, vb
     keys = keysets.local_keys(n) if view == "local" else keysets.full_keys(n)
     ref = attention.attend(q, hk, hv, keys, SCALE)
-    check_tight(out[0].cpu().numpy(), ref, q, hk, hv, keys, SCALE, what="%s from projection G=%d n=%d" % (view, G, n))
+    check_tight(out[0].cpu().numpy(), ref, q, hk, hv, keys, SCALE, what="%s from projection G=%d Hkv=%d n=%d" % (view, G, Hkv, n))
 
 
 @pytest.mark.parametrize("view", ["local", "full"])
